@@ -1,0 +1,57 @@
+"""Altered copies of the oracle must fail at least one pin (CPU only).
+
+Each mutant changes one plausible detail of s2r_oracle.cpp -- a dropped sign, a wrong
+shift, a lost term, a wrong median index -- is compiled with g++ into a temporary
+library, and the pin suite is run against it.  A mutant that passes every pin would mean
+the pins cannot tell that mistake from the real thing.
+"""
+import os
+
+import pytest
+
+import oracle
+import pins
+
+MUTANTS = {
+    "drop_sign_in_insert": ("S[cell] += (double)orc_sign(p, j, i) * (double)g;",
+                            "S[cell] += (double)g;"),
+    "abs_mass_signed": ("A[cell] += std::fabs((double)g);", "A[cell] += (double)g;"),
+    "shift_by_one": ("return low64 >> (64 - bits);", "return (low64 << 1) >> (64 - bits);"),
+    "drop_add_term": ("(unsigned __int128)a * (unsigned __int128)x + c;",
+                      "(unsigned __int128)a * (unsigned __int128)x;"),
+    "add_after_shift": ("uint64_t low64 = (uint64_t)full;  // mod 2^64\n  return low64 >> (64 - bits);",
+                        "uint64_t low64 = (uint64_t)full - c;\n  return (low64 >> (64 - bits)) + (c >> (64 - bits)) & ((1ull << bits) - 1);"),
+    "partition_not_shifted": ("return (uint32_t)((part << K) | low);", "return (uint32_t)(part | low);"),
+    "sign_uses_bucket_constant": ("mas_top(p->sA[j], p->sB[j], i, 1)", "mas_top(p->hA[j], p->sB[j], i, 1)"),
+    "bitmap_bit_off_by_one": ("bitmap[i / 64] |= 1ull << (i % 64);\n    if (count < cap)",
+                              "bitmap[i / 64] |= 1ull << ((i + 1) % 64);\n    if (count < cap)"),
+    "negative_zero_counts": ("return (u & 0x7FFFFFFFu) != 0;", "return u != 0;"),
+    "median_odd_takes_max": ("(d % 2) ? est[(d - 1) / 2]", "(d % 2) ? est[d - 1]"),
+    "median_even_takes_lower": ("0.5 * (est[d / 2 - 1] + est[d / 2])", "est[d / 2 - 1]"),
+    "query_ignores_sign": ("est[j] = (double)orc_sign(p, j, (uint32_t)i) * S[cell];",
+                           "est[j] = S[cell];"),
+    "reduce_drops_last_worker": ("for (uint32_t k = 0; k < W; ++k) {\n      s += S",
+                                 "for (uint32_t k = 0; k + 1 < W; ++k) {\n      s += S"),
+    "merge_by_xor": ("m |= bitmaps[(uint64_t)k * words + q];", "m ^= bitmaps[(uint64_t)k * words + q];"),
+    "draw_order_swapped": ("out->hA[j] = orc_splitmix64_next(&st);\n    out->hB[j] = orc_splitmix64_next(&st);",
+                           "out->hB[j] = orc_splitmix64_next(&st);\n    out->hA[j] = orc_splitmix64_next(&st);"),
+    "splitmix_wrong_gamma": ("*state += 0x9E3779B97F4A7C15ull;", "*state += 0x9E3779B97F4A7C17ull;"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(name, tmp_path):
+    old, new = MUTANTS[name]
+    src = open(oracle.source_path()).read()
+    assert src.count(old) == 1, f"mutation site for {name} not unique/found"
+    mpath = tmp_path / f"{name}.cpp"
+    mpath.write_text(src.replace(old, new))
+    lib = oracle.compile_source(str(mpath), str(tmp_path / f"lib{name}.so"))
+    failed = []
+    with oracle.using(lib):
+        for pin in pins.ALL_PINS:
+            try:
+                pin()
+            except AssertionError:
+                failed.append(pin.__name__)
+    assert failed, f"mutant {name} passes every pin"
