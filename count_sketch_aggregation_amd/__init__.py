@@ -1,0 +1,202 @@
+"""Python binding of libs2r: sparse-sketch gradient aggregation on MI355X (gfx950).
+
+Thin ctypes marshalling over the C ABI in include/s2r.h -- the functions below carry the
+same names as the C entry points, take torch tensors (device memory) and the current torch
+stream, and do no arithmetic of their own.  Every step of the path runs in the HIP kernels
+of libs2r.so; there is no CPU or PyTorch fallback: if the library is not built, importing
+the binding's entry points raises.
+
+The method is the data-parallel hot path of S2 Reducer (arXiv 2110.02140, Section 3.1 and
+Algorithm 1): encode (bitmap + count-sketch per worker), reduce (sum of sketches, OR of
+bitmaps) and decode (median over rows at every set bit).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libs2r.so")
+MAX_ROWS = 16
+
+S2R_OK, S2R_ERR_NULL, S2R_ERR_DIM, S2R_ERR_ALIGN, S2R_ERR_WORKSPACE, S2R_ERR_HIP = range(6)
+
+
+class S2RError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {status_string(status)} (status {status})")
+
+
+class s2r_params(ctypes.Structure):
+    """Mirror of ``s2r_params`` in include/s2r.h."""
+
+    _fields_ = [
+        ("d", ctypes.c_uint32),
+        ("log2_w", ctypes.c_uint32),
+        ("log2_part", ctypes.c_uint32),
+        ("reserved", ctypes.c_uint32),
+        ("pA", ctypes.c_uint64),
+        ("pB", ctypes.c_uint64),
+        ("hA", ctypes.c_uint64 * MAX_ROWS),
+        ("hB", ctypes.c_uint64 * MAX_ROWS),
+        ("sA", ctypes.c_uint64 * MAX_ROWS),
+        ("sB", ctypes.c_uint64 * MAX_ROWS),
+    ]
+
+    @property
+    def w(self) -> int:
+        return 1 << self.log2_w
+
+    def as_dict(self) -> dict:
+        d = self.d
+        return {
+            "d": d, "log2_w": self.log2_w, "log2_part": self.log2_part,
+            "pA": self.pA, "pB": self.pB,
+            "hA": list(self.hA)[:d], "hB": list(self.hB)[:d],
+            "sA": list(self.sA)[:d], "sB": list(self.sB)[:d],
+        }
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libs2r.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(
+                f"libs2r.so not found at {LIB_PATH}: build it with "
+                "`python -c 'import __graft_entry__ as g; g.build()'` (hipcc, gfx950)")
+        L = ctypes.CDLL(LIB_PATH)
+        P = ctypes.POINTER
+        vp, u64, u32, sz = ctypes.c_void_p, ctypes.c_uint64, ctypes.c_uint32, ctypes.c_size_t
+        st = ctypes.c_int
+        L.s2r_params_from_seed.argtypes = [u64, u32, u32, u32, P(s2r_params)]
+        L.s2r_params_from_seed.restype = st
+        L.s2r_default_log2_part.argtypes = [u32, u32]
+        L.s2r_default_log2_part.restype = u32
+        L.s2r_bitmap_words.argtypes = [u64]
+        L.s2r_bitmap_words.restype = u64
+        L.s2r_encode_workspace_bytes.argtypes = [P(s2r_params), u32, u64, u64]
+        L.s2r_encode_workspace_bytes.restype = sz
+        L.s2r_encode.argtypes = [P(s2r_params), u32, vp, u64, u64, vp, vp, vp, vp, u64, vp, vp, sz,
+                                 vp]
+        L.s2r_encode.restype = st
+        L.s2r_reduce.argtypes = [P(s2r_params), u32, u64, vp, vp, vp, vp, vp]
+        L.s2r_reduce.restype = st
+        L.s2r_decode.argtypes = [P(s2r_params), u64, vp, vp, vp, vp]
+        L.s2r_decode.restype = st
+        L.s2r_hash.argtypes = [P(s2r_params), vp, u64, vp, vp, vp]
+        L.s2r_hash.restype = st
+        L.s2r_status_string.argtypes = [st]
+        L.s2r_status_string.restype = ctypes.c_char_p
+        _lib = L
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return lib().s2r_status_string(status).decode()
+
+
+def _check(status: int, where: str) -> None:
+    if status != S2R_OK:
+        raise S2RError(status, where)
+
+
+def _ptr(t) -> int | None:
+    """Device pointer of a tensor (None for None), or an int passed through."""
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _stream(stream) -> int | None:
+    if stream is not None:
+        return stream if isinstance(stream, int) else stream.cuda_stream
+    import torch
+    return torch.cuda.current_stream().cuda_stream
+
+
+# ---------------------------------------------------------------------------------------
+# entry points (same names as the C ABI)
+
+
+def s2r_params_from_seed(seed: int, d: int, log2_w: int, log2_part: int | None = None) -> s2r_params:
+    """Hash constants from a seed (SplitMix64).  log2_part defaults to the largest partition
+    that fits the LDS accumulator (s2r_default_log2_part); log2_part == log2_w gives
+    independent rows."""
+    if log2_part is None:
+        log2_part = s2r_default_log2_part(d, log2_w)
+    p = s2r_params()
+    _check(lib().s2r_params_from_seed(seed, d, log2_w, log2_part, ctypes.byref(p)),
+           "s2r_params_from_seed")
+    return p
+
+
+def s2r_default_log2_part(d: int, log2_w: int) -> int:
+    return int(lib().s2r_default_log2_part(d, log2_w))
+
+
+def s2r_bitmap_words(n: int) -> int:
+    return int(lib().s2r_bitmap_words(n))
+
+
+def s2r_encode_workspace_bytes(p: s2r_params, W: int, n: int, cap: int) -> int:
+    return int(lib().s2r_encode_workspace_bytes(ctypes.byref(p), W, n, cap))
+
+
+def s2r_encode(p: s2r_params, W: int, grad, n: int, ld: int, bitmaps, sketches, idx, val, cap: int,
+               nnz, workspace, ws_bytes: int | None = None, stream=None) -> None:
+    if ws_bytes is None:
+        ws_bytes = workspace.numel() * workspace.element_size()
+    _check(lib().s2r_encode(ctypes.byref(p), W, _ptr(grad), n, ld, _ptr(bitmaps), _ptr(sketches),
+                            _ptr(idx), _ptr(val), cap, _ptr(nnz), _ptr(workspace), ws_bytes,
+                            _stream(stream)), "s2r_encode")
+
+
+def s2r_reduce(p: s2r_params, W: int, n: int, bitmaps, sketches, bitmap_out, sketch_out,
+               stream=None) -> None:
+    _check(lib().s2r_reduce(ctypes.byref(p), W, n, _ptr(bitmaps), _ptr(sketches), _ptr(bitmap_out),
+                            _ptr(sketch_out), _stream(stream)), "s2r_reduce")
+
+
+def s2r_decode(p: s2r_params, n: int, bitmap, sketch, out, stream=None) -> None:
+    _check(lib().s2r_decode(ctypes.byref(p), n, _ptr(bitmap), _ptr(sketch), _ptr(out),
+                            _stream(stream)), "s2r_decode")
+
+
+def s2r_hash(p: s2r_params, keys, m: int, buckets, signs, stream=None) -> None:
+    _check(lib().s2r_hash(ctypes.byref(p), _ptr(keys), m, _ptr(buckets), _ptr(signs),
+                          _stream(stream)), "s2r_hash")
+
+
+# ---------------------------------------------------------------------------------------
+# allocation helper (torch supplies device memory; no arithmetic here)
+
+
+def alloc_encode_buffers(p: s2r_params, W: int, n: int, cap: int, device="cuda") -> dict:
+    """torch tensors for every s2r_encode output plus its workspace."""
+    import torch
+    words = s2r_bitmap_words(n)
+    ws = s2r_encode_workspace_bytes(p, W, n, cap)
+    if ws == 0:
+        raise S2RError(S2R_ERR_DIM, "s2r_encode_workspace_bytes")
+    return {
+        "bitmaps": torch.empty((W, max(words, 1)), dtype=torch.int64, device=device),
+        "sketches": torch.empty((W, p.d, p.w), dtype=torch.float32, device=device),
+        "idx": torch.empty((W, max(cap, 1)), dtype=torch.int32, device=device),
+        "val": torch.empty((W, max(cap, 1)), dtype=torch.float32, device=device),
+        "nnz": torch.empty((W,), dtype=torch.int64, device=device),
+        "workspace": torch.empty((ws,), dtype=torch.uint8, device=device),
+    }
+
+
+__all__ = [
+    "s2r_params", "S2RError", "s2r_params_from_seed", "s2r_default_log2_part", "s2r_bitmap_words",
+    "s2r_encode_workspace_bytes", "s2r_encode", "s2r_reduce", "s2r_decode", "s2r_hash",
+    "alloc_encode_buffers", "status_string", "lib",
+]

@@ -1,0 +1,220 @@
+// api.hip -- the C ABI of libs2r (declared in include/s2r.h): host-side validation,
+// SplitMix64 derivation of the hash constants, workspace layout and kernel launches.
+// Every check runs before the first enqueue, so a call that returns an error has enqueued
+// nothing.
+#include <string.h>
+
+#include "s2r_launch.hpp"
+
+namespace s2r {
+
+static inline uint64_t splitmix64_step(uint64_t& state) {
+  // SplitMix64 (Steele, Lea & Flood, OOPSLA 2014): gamma increment, then mix
+  state += 0x9E3779B97F4A7C15ull;
+  uint64_t z = state;
+  z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+  z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+  return z ^ (z >> 31);
+}
+
+static bool params_ok(const s2r_params* p) {
+  return p && p->d >= 1 && p->d <= S2R_MAX_ROWS && p->log2_w <= 31 && p->log2_part <= p->log2_w &&
+         p->reserved == 0;
+}
+
+HashArgs make_hash_args(const s2r_params& p) {
+  HashArgs h;
+  memset(&h, 0, sizeof(h));
+  h.d = p.d;
+  h.K = p.log2_part;
+  h.shift_part = 32u - (p.log2_w - p.log2_part);
+  h.shift_row = 32u - p.log2_part;
+  h.pA = p.pA;
+  h.pB = p.pB;
+  for (uint32_t j = 0; j < p.d; ++j) {
+    h.hA[j] = p.hA[j];
+    h.hB[j] = p.hB[j];
+    h.sA[j] = p.sA[j];
+    h.sB[j] = p.sB[j];
+  }
+  return h;
+}
+
+bool use_partitioned(const s2r_params& p) {
+  const uint64_t tile_bytes = ((uint64_t)p.d << p.log2_part) * sizeof(float);
+  const uint64_t parts = 1ull << (p.log2_w - p.log2_part);
+  return tile_bytes <= kAccLdsBytes && parts <= (uint64_t)kMaxPartitions;
+}
+
+static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+EncodeLayout encode_layout(const s2r_params& p, uint32_t W, uint64_t n, uint64_t cap) {
+  EncodeLayout L;
+  L.tiles = (n + kTile - 1) / kTile;
+  const uint64_t listable = cap < n ? cap : n;
+  L.chunks = (listable + kChunk - 1) / kChunk;
+  L.partitioned = use_partitioned(p);
+  L.partitions = L.partitioned ? (1ull << (p.log2_w - p.log2_part)) : 0;
+  size_t off = 0;
+  L.off_counts = off;
+  off = align256(off + (size_t)W * L.tiles * 4);
+  L.off_offsets = off;
+  off = align256(off + (size_t)W * (L.tiles + 1) * 4);
+  L.off_chunk_tile = off;
+  off = align256(off + (size_t)W * L.chunks * 4);
+  L.off_bidx = L.off_bval = L.off_prefix = off;
+  if (L.partitioned) {
+    const size_t slots = (size_t)W * L.chunks * kChunk;
+    L.off_bidx = off;
+    off = align256(off + slots * 4);
+    L.off_bval = off;
+    off = align256(off + slots * 4);
+    L.off_prefix = off;
+    off = align256(off + (size_t)W * (L.partitions + 1) * L.chunks * 4);
+  }
+  L.total = off > 0 ? off : 256;
+  return L;
+}
+
+}  // namespace s2r
+
+using namespace s2r;
+
+extern "C" {
+
+s2r_status s2r_params_from_seed(uint64_t seed, uint32_t d, uint32_t log2_w, uint32_t log2_part,
+                                s2r_params* out) {
+  if (!out) return S2R_ERR_NULL;
+  if (d < 1 || d > S2R_MAX_ROWS || log2_w > 31 || log2_part > log2_w) return S2R_ERR_DIM;
+  memset(out, 0, sizeof(*out));
+  out->d = d;
+  out->log2_w = log2_w;
+  out->log2_part = log2_part;
+  uint64_t st = seed;
+  out->pA = splitmix64_step(st);
+  out->pB = splitmix64_step(st);
+  for (uint32_t j = 0; j < d; ++j) {
+    out->hA[j] = splitmix64_step(st);
+    out->hB[j] = splitmix64_step(st);
+    out->sA[j] = splitmix64_step(st);
+    out->sB[j] = splitmix64_step(st);
+  }
+  return S2R_OK;
+}
+
+uint32_t s2r_default_log2_part(uint32_t d, uint32_t log2_w) {
+  if (d < 1 || d > S2R_MAX_ROWS || log2_w > 31) return 0;
+  uint32_t K = log2_w;
+  while (K > 0 && ((uint64_t)d << K) * sizeof(float) > kAccLdsBytes) --K;
+  return K;
+}
+
+uint64_t s2r_bitmap_words(uint64_t n) { return (n + 63) / 64; }
+
+size_t s2r_encode_workspace_bytes(const s2r_params* p, uint32_t W, uint64_t n, uint64_t cap) {
+  if (!params_ok(p) || W == 0 || n >= (1ull << 32)) return 0;
+  return encode_layout(*p, W, n, cap).total;
+}
+
+static inline bool aligned(const void* ptr, size_t a) {
+  return (reinterpret_cast<uintptr_t>(ptr) % a) == 0;
+}
+
+#define S2R_TRY(expr)                          \
+  do {                                         \
+    if ((expr) != hipSuccess) return S2R_ERR_HIP; \
+  } while (0)
+
+s2r_status s2r_encode(const s2r_params* p, uint32_t W, const float* grad, uint64_t n,
+                      uint64_t ld, uint64_t* bitmaps, float* sketches, uint32_t* idx,
+                      float* val, uint64_t cap, uint64_t* nnz, void* workspace,
+                      size_t ws_bytes, void* stream) {
+  if (!p || (!bitmaps && n > 0) || !sketches || !nnz || !workspace) return S2R_ERR_NULL;
+  if (n > 0 && !grad) return S2R_ERR_NULL;
+  if (cap > 0 && (!idx || !val)) return S2R_ERR_NULL;
+  if (!params_ok(p) || W == 0 || W > 65535 || n >= (1ull << 32) || ld < n) return S2R_ERR_DIM;
+  if (ld % 4 != 0 || !aligned(grad, 16) || !aligned(bitmaps, 8) || !aligned(sketches, 4) ||
+      !aligned(nnz, 8) || !aligned(workspace, 16) || (cap > 0 && (!aligned(idx, 4) || !aligned(val, 4))))
+    return S2R_ERR_ALIGN;
+  const EncodeLayout L = encode_layout(*p, W, n, cap);
+  if (ws_bytes < L.total) return S2R_ERR_WORKSPACE;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  uint32_t* counts = reinterpret_cast<uint32_t*>(ws + L.off_counts);
+  uint32_t* offsets = reinterpret_cast<uint32_t*>(ws + L.off_offsets);
+  uint32_t* chunk_tile = reinterpret_cast<uint32_t*>(ws + L.off_chunk_tile);
+  const uint64_t w = 1ull << p->log2_w;
+  const uint64_t dw = (uint64_t)p->d * w;
+  const uint64_t words = s2r_bitmap_words(n);
+  const HashArgs h = make_hash_args(*p);
+
+  S2R_TRY(launch_stream(W, grad, n, ld, L.tiles, bitmaps, counts, s));
+  S2R_TRY(launch_scan(W, L.tiles, counts, offsets, nnz, chunk_tile, L.chunks, cap, s));
+  if (L.partitioned) {
+    uint32_t* bidx = reinterpret_cast<uint32_t*>(ws + L.off_bidx);
+    float* bval = reinterpret_cast<float*>(ws + L.off_bval);
+    uint32_t* prefix = reinterpret_cast<uint32_t*>(ws + L.off_prefix);
+    S2R_TRY(launch_list_bin(h, W, grad, ld, L.tiles, bitmaps, words, offsets, chunk_tile, idx, val,
+                            cap, L.chunks, L.partitions, bidx, bval, prefix, s));
+    S2R_TRY(launch_accumulate(h, W, L.tiles, offsets, cap, L.chunks, L.partitions, bidx, bval,
+                              prefix, sketches, w, s));
+  } else {
+    S2R_TRY(launch_fill_zero(sketches, (uint64_t)W * dw, s));
+    S2R_TRY(launch_list_atomic(h, W, grad, ld, L.tiles, bitmaps, words, offsets, chunk_tile, idx,
+                               val, cap, L.chunks, sketches, dw, s));
+  }
+  return S2R_OK;
+}
+
+s2r_status s2r_reduce(const s2r_params* p, uint32_t W, uint64_t n, const uint64_t* bitmaps,
+                      const float* sketches, uint64_t* bitmap_out, float* sketch_out,
+                      void* stream) {
+  if (!p || !sketches || !sketch_out) return S2R_ERR_NULL;
+  if (n > 0 && (!bitmaps || !bitmap_out)) return S2R_ERR_NULL;
+  if (!params_ok(p) || W == 0 || n >= (1ull << 32)) return S2R_ERR_DIM;
+  if (!aligned(sketches, 4) || !aligned(sketch_out, 4) || !aligned(bitmaps, 8) ||
+      !aligned(bitmap_out, 8))
+    return S2R_ERR_ALIGN;
+  const uint64_t cells = (uint64_t)p->d << p->log2_w;
+  S2R_TRY(launch_reduce(W, cells, s2r_bitmap_words(n), bitmaps, sketches, bitmap_out, sketch_out,
+                        static_cast<hipStream_t>(stream)));
+  return S2R_OK;
+}
+
+s2r_status s2r_decode(const s2r_params* p, uint64_t n, const uint64_t* bitmap,
+                      const float* sketch, float* out, void* stream) {
+  if (!p || !sketch) return S2R_ERR_NULL;
+  if (n > 0 && (!bitmap || !out)) return S2R_ERR_NULL;
+  if (!params_ok(p) || n >= (1ull << 32)) return S2R_ERR_DIM;
+  if (!aligned(bitmap, 8) || !aligned(sketch, 4) || !aligned(out, 16)) return S2R_ERR_ALIGN;
+  const HashArgs h = make_hash_args(*p);
+  S2R_TRY(launch_decode_direct(h, n, bitmap, sketch, 1ull << p->log2_w, out,
+                               static_cast<hipStream_t>(stream)));
+  return S2R_OK;
+}
+
+s2r_status s2r_hash(const s2r_params* p, const uint32_t* keys, uint64_t m, uint32_t* buckets,
+                    int8_t* signs, void* stream) {
+  if (!p) return S2R_ERR_NULL;
+  if (m > 0 && (!keys || !buckets || !signs)) return S2R_ERR_NULL;
+  if (!params_ok(p)) return S2R_ERR_DIM;
+  if (!aligned(keys, 4) || !aligned(buckets, 4)) return S2R_ERR_ALIGN;
+  S2R_TRY(launch_hash(make_hash_args(*p), keys, m, buckets, signs,
+                      static_cast<hipStream_t>(stream)));
+  return S2R_OK;
+}
+
+const char* s2r_status_string(s2r_status s) {
+  switch (s) {
+    case S2R_OK: return "ok";
+    case S2R_ERR_NULL: return "null pointer argument";
+    case S2R_ERR_DIM: return "size or parameter out of range";
+    case S2R_ERR_ALIGN: return "misaligned pointer or leading dimension";
+    case S2R_ERR_WORKSPACE: return "workspace too small";
+    case S2R_ERR_HIP: return "HIP launch failed";
+  }
+  return "unknown status";
+}
+
+}  // extern "C"

@@ -1,0 +1,64 @@
+// reduce.hip -- aggregation of W workers' sketches and bitmaps on one GPU.
+//
+// S2 Reducer (arXiv 2110.02140) Section 3.1 "Collecting Sparse-Sketch with AllReduce": the
+// sketch is the linear map A^T g, so the sketches of W workers add element-wise to the
+// sketch of the summed gradient; the merged bitmap marks the union of non-zero positions.
+// With the W workers resident as W buffers of one GPU, the AllReduce becomes this
+// streaming pass: sum in worker order k = 0..W-1 (fixed, so the fp32 result is
+// reproducible) and OR of the bitmap words.  HBM-bound: W reads + 1 write per cell.
+#include "s2r_launch.hpp"
+
+namespace s2r {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+template <bool VEC>
+__global__ __launch_bounds__(256) void k_reduce(uint32_t W, uint64_t cells, uint64_t words,
+                                                const uint64_t* __restrict__ bitmaps,
+                                                const float* sketches, uint64_t* bitmap_out,
+                                                float* sketch_out) {
+  // no __restrict__ on sketches / sketch_out: they may alias (in place into slot 0)
+  const uint64_t stride = (uint64_t)gridDim.x * blockDim.x;
+  const uint64_t gid = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if constexpr (VEC) {
+    const uint64_t c4 = cells / 4;
+    const f32x4* in = reinterpret_cast<const f32x4*>(sketches);
+    f32x4* out = reinterpret_cast<f32x4*>(sketch_out);
+    for (uint64_t c = gid; c < c4; c += stride) {
+      f32x4 acc = __builtin_nontemporal_load(in + c);
+      for (uint32_t k = 1; k < W; ++k) acc += __builtin_nontemporal_load(in + (uint64_t)k * c4 + c);
+      out[c] = acc;
+    }
+  } else {
+    for (uint64_t c = gid; c < cells; c += stride) {
+      float acc = sketches[c];
+      for (uint32_t k = 1; k < W; ++k) acc += sketches[(uint64_t)k * cells + c];
+      sketch_out[c] = acc;
+    }
+  }
+  for (uint64_t q = gid; q < words; q += stride) {
+    uint64_t m = 0;
+    for (uint32_t k = 0; k < W; ++k) m |= bitmaps[(uint64_t)k * words + q];
+    bitmap_out[q] = m;
+  }
+}
+
+hipError_t launch_reduce(uint32_t W, uint64_t cells, uint64_t words, const uint64_t* bitmaps,
+                         const float* sketches, uint64_t* bitmap_out, float* sketch_out,
+                         hipStream_t s) {
+  const bool vec = (cells % 4 == 0) && (reinterpret_cast<uintptr_t>(sketches) % 16 == 0) &&
+                   (reinterpret_cast<uintptr_t>(sketch_out) % 16 == 0);
+  const uint64_t units = (vec ? cells / 4 : cells) > words ? (vec ? cells / 4 : cells) : words;
+  uint64_t blocks = (units + 255) / 256;
+  if (blocks > 16384) blocks = 16384;
+  if (blocks == 0) return hipSuccess;
+  if (vec)
+    hipLaunchKernelGGL(k_reduce<true>, dim3((uint32_t)blocks), dim3(256), 0, s, W, cells, words,
+                       bitmaps, sketches, bitmap_out, sketch_out);
+  else
+    hipLaunchKernelGGL(k_reduce<false>, dim3((uint32_t)blocks), dim3(256), 0, s, W, cells, words,
+                       bitmaps, sketches, bitmap_out, sketch_out);
+  return hipGetLastError();
+}
+
+}  // namespace s2r

@@ -1,0 +1,152 @@
+// s2r_device.hpp -- device helpers shared by the gfx950 kernels of libs2r.
+//
+// Hash: multiply-add-shift (Dietzfelbinger 1996) on the 32-bit element index with 64-bit
+// constants, as the public header defines: the top b bits of (a*x + c) mod 2^64.  For
+// b <= 32 those bits lie in the high word, which costs one v_mad_u64_u32 (low word of a
+// times x plus c, a 64-bit result that wraps mod 2^64) and one 32-bit multiply-add for
+// the high word of a -- no 64x64 product is needed.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "s2r.h"
+
+namespace s2r {
+
+constexpr int kWave = 64;
+
+// Kernel-argument copy of the hash constants.  Shifts are precomputed on the host so
+// kernels need no branches on K or L: top b bits of a 32-bit word = (uint64)hi >> (32-b),
+// which is 0 for b = 0.
+struct HashArgs {
+  uint32_t d;
+  uint32_t shift_part;  // 32 - (L - K)
+  uint32_t shift_row;   // 32 - K
+  uint32_t K;
+  uint64_t pA, pB;
+  uint64_t hA[S2R_MAX_ROWS], hB[S2R_MAX_ROWS];
+  uint64_t sA[S2R_MAX_ROWS], sB[S2R_MAX_ROWS];
+};
+
+// High 32 bits of (a*x + c) mod 2^64.
+__device__ __forceinline__ uint32_t mas_hi32(uint64_t a, uint64_t c, uint32_t x) {
+  uint64_t t = (uint64_t)(uint32_t)a * (uint64_t)x + c;
+  return (uint32_t)(t >> 32) + (uint32_t)(a >> 32) * x;
+}
+
+__device__ __forceinline__ uint32_t top_bits(uint32_t hi, uint32_t shift) {
+  return (uint32_t)((uint64_t)hi >> shift);
+}
+
+// P(i): the partition of index i (shared by all rows).
+__device__ __forceinline__ uint32_t partition_of(const HashArgs& h, uint32_t i) {
+  return top_bits(mas_hi32(h.pA, h.pB, i), h.shift_part);
+}
+
+// Q_j(i): bucket of index i within its partition, row j.
+__device__ __forceinline__ uint32_t row_bucket(const HashArgs& h, int j, uint32_t i) {
+  return top_bits(mas_hi32(h.hA[j], h.hB[j], i), h.shift_row);
+}
+
+// h_j(i) = P(i) * 2^K + Q_j(i)
+__device__ __forceinline__ uint32_t bucket_of(const HashArgs& h, uint32_t part, int j,
+                                              uint32_t i) {
+  return (part << h.K) | row_bucket(h, j, i);
+}
+
+// 0x80000000 when s_j(i) = -1, else 0: xor-ing it into an fp32 pattern multiplies by s_j(i)
+// exactly.
+__device__ __forceinline__ uint32_t sign_mask(const HashArgs& h, int j, uint32_t i) {
+  return mas_hi32(h.sA[j], h.sB[j], i) & 0x80000000u;
+}
+
+__device__ __forceinline__ float apply_sign(float v, uint32_t mask) {
+  return __uint_as_float(__float_as_uint(v) ^ mask);
+}
+
+__device__ __forceinline__ bool nonzero_bits(float x) {
+  return (__float_as_uint(x) & 0x7FFFFFFFu) != 0u;
+}
+
+// Place bit m of a 16-bit value at bit 4m of a 64-bit word.
+__device__ __forceinline__ uint64_t spread4(uint64_t x) {
+  x &= 0xFFFFull;
+  x = (x | (x << 24)) & 0x000000FF000000FFull;
+  x = (x | (x << 12)) & 0x000F000F000F000Full;
+  x = (x | (x << 6)) & 0x0303030303030303ull;
+  x = (x | (x << 3)) & 0x1111111111111111ull;
+  return x;
+}
+
+// Median of D values (D <= 16), exact selection for odd D; even D gives the mean of the
+// two middle values rounded once (halving is exact away from the subnormal range).
+template <int D>
+__device__ __forceinline__ float median_of(float* v) {
+  if constexpr (D == 1) {
+    return v[0];
+  } else if constexpr (D == 2) {
+    return 0.5f * v[0] + 0.5f * v[1];
+  } else if constexpr (D == 3) {
+    return __builtin_amdgcn_fmed3f(v[0], v[1], v[2]);
+  } else if constexpr (D == 5) {
+    // the median of five is the median of e and the two inner values of the sorted pairs
+    float lo = fmaxf(fminf(v[0], v[1]), fminf(v[2], v[3]));
+    float hi = fminf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3]));
+    return __builtin_amdgcn_fmed3f(v[4], lo, hi);
+  } else {
+    // odd-even transposition sort: D rounds of compare-exchange sort D values
+#pragma unroll
+    for (int r = 0; r < D; ++r) {
+#pragma unroll
+      for (int a = (r & 1); a + 1 < D; a += 2) {
+        float x = v[a], y = v[a + 1];
+        v[a] = fminf(x, y);
+        v[a + 1] = fmaxf(x, y);
+      }
+    }
+    if constexpr (D % 2) return v[(D - 1) / 2];
+    else return 0.5f * v[D / 2 - 1] + 0.5f * v[D / 2];
+  }
+}
+
+// Wave-wide inclusive prefix sum (64 lanes).
+__device__ __forceinline__ uint32_t wave_inclusive_sum(uint32_t x) {
+  const int lane = threadIdx.x & (kWave - 1);
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+    uint32_t y = __shfl_up(x, off, kWave);
+    if (lane >= off) x += y;
+  }
+  return x;
+}
+
+__device__ __forceinline__ uint32_t wave_sum(uint32_t x) {
+#pragma unroll
+  for (int off = kWave / 2; off > 0; off >>= 1) x += __shfl_xor(x, off, kWave);
+  return x;
+}
+
+}  // namespace s2r
+
+// Expand a template call over D = 1..16 (every row count the header allows).
+#define S2R_DISPATCH_D(d, CALL)                        \
+  switch (d) {                                         \
+    case 1: { constexpr int D = 1; CALL; } break;      \
+    case 2: { constexpr int D = 2; CALL; } break;      \
+    case 3: { constexpr int D = 3; CALL; } break;      \
+    case 4: { constexpr int D = 4; CALL; } break;      \
+    case 5: { constexpr int D = 5; CALL; } break;      \
+    case 6: { constexpr int D = 6; CALL; } break;      \
+    case 7: { constexpr int D = 7; CALL; } break;      \
+    case 8: { constexpr int D = 8; CALL; } break;      \
+    case 9: { constexpr int D = 9; CALL; } break;      \
+    case 10: { constexpr int D = 10; CALL; } break;    \
+    case 11: { constexpr int D = 11; CALL; } break;    \
+    case 12: { constexpr int D = 12; CALL; } break;    \
+    case 13: { constexpr int D = 13; CALL; } break;    \
+    case 14: { constexpr int D = 14; CALL; } break;    \
+    case 15: { constexpr int D = 15; CALL; } break;    \
+    case 16: { constexpr int D = 16; CALL; } break;    \
+    default: break;                                    \
+  }

@@ -1,0 +1,70 @@
+// s2r_launch.hpp -- host-side launchers of the gfx950 kernels (internal to libs2r).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "s2r_device.hpp"
+
+namespace s2r {
+
+// ---- encode geometry -------------------------------------------------------------------
+constexpr int kStreamThreads = 256;                 // 4 waves
+constexpr int kStreamVec = 8;                       // float4 loads per thread
+constexpr int kTile = kStreamThreads * kStreamVec * 4;  // 8192 elements per tile
+constexpr int kTileWords = kTile / 64;              // 128 bitmap words per tile
+
+constexpr int kListThreads = 256;
+constexpr int kChunk = 8192;                        // list entries per chunk
+constexpr int kMaxPartitions = 8192;                // LDS histogram limit of the binning pass
+constexpr int kAccThreads = 512;
+constexpr size_t kAccLdsBytes = 128 * 1024;         // LDS of one partition tile
+
+constexpr int kScanThreads = 1024;
+
+// Workspace layout of s2r_encode (every section 256-byte aligned).
+struct EncodeLayout {
+  uint64_t tiles;        // tiles per worker
+  uint64_t chunks;       // list chunks per worker (bounded by min(cap, n))
+  uint64_t partitions;   // 2^(L-K) on the partitioned path, 0 otherwise
+  bool partitioned;
+  size_t off_counts, off_offsets, off_chunk_tile, off_bidx, off_bval, off_prefix, total;
+};
+EncodeLayout encode_layout(const s2r_params& p, uint32_t W, uint64_t n, uint64_t cap);
+bool use_partitioned(const s2r_params& p);
+
+HashArgs make_hash_args(const s2r_params& p);
+
+hipError_t launch_stream(uint32_t W, const float* grad, uint64_t n, uint64_t ld,
+                         uint64_t tiles, uint64_t* bitmaps, uint32_t* counts, hipStream_t s);
+hipError_t launch_scan(uint32_t W, uint64_t tiles, const uint32_t* counts, uint32_t* offsets,
+                       uint64_t* nnz, uint32_t* chunk_tile, uint64_t chunks, uint64_t cap,
+                       hipStream_t s);
+hipError_t launch_fill_zero(float* p, uint64_t count, hipStream_t s);
+hipError_t launch_list_atomic(const HashArgs& h, uint32_t W, const float* grad, uint64_t ld,
+                              uint64_t tiles, const uint64_t* bitmaps, uint64_t words,
+                              const uint32_t* offsets, const uint32_t* chunk_tile, uint32_t* idx,
+                              float* val, uint64_t cap, uint64_t chunks, float* sketches,
+                              uint64_t dw, hipStream_t s);
+hipError_t launch_list_bin(const HashArgs& h, uint32_t W, const float* grad, uint64_t ld,
+                           uint64_t tiles, const uint64_t* bitmaps, uint64_t words,
+                           const uint32_t* offsets, const uint32_t* chunk_tile, uint32_t* idx,
+                           float* val, uint64_t cap, uint64_t chunks, uint64_t partitions,
+                           uint32_t* bidx, float* bval, uint32_t* prefix, hipStream_t s);
+hipError_t launch_accumulate(const HashArgs& h, uint32_t W, uint64_t tiles,
+                             const uint32_t* offsets, uint64_t cap, uint64_t chunks,
+                             uint64_t partitions, const uint32_t* bidx, const float* bval,
+                             const uint32_t* prefix, float* sketches, uint64_t w, hipStream_t s);
+
+hipError_t launch_reduce(uint32_t W, uint64_t cells, uint64_t words, const uint64_t* bitmaps,
+                         const float* sketches, uint64_t* bitmap_out, float* sketch_out,
+                         hipStream_t s);
+
+hipError_t launch_decode_direct(const HashArgs& h, uint64_t n, const uint64_t* bitmap,
+                                const float* sketch, uint64_t w, float* out, hipStream_t s);
+
+hipError_t launch_hash(const HashArgs& h, const uint32_t* keys, uint64_t m, uint32_t* buckets,
+                       int8_t* signs, hipStream_t s);
+
+}  // namespace s2r

@@ -1,0 +1,156 @@
+/* s2r.h -- C ABI of the sparse-sketch gradient aggregation library (libs2r.so, gfx950).
+ *
+ * The operation is the data-parallel hot path of S2 Reducer ("S2 Reducer: High-Performance
+ * Sparse Communication to Accelerate Distributed Deep Learning", Ge et al., arXiv
+ * 2110.02140):
+ *
+ *   s2r_encode  -- Section 3.1 "Compressing Sparse Gradient" and the compression loop of
+ *                  Algorithm 1: every worker's gradient becomes a bitmap of its non-zero
+ *                  positions plus a d x w count-sketch in which each non-zero g(i) adds
+ *                  s_j(i) * g(i) to bucket h_j(i) of every row j.
+ *   s2r_reduce  -- Section 3.1 "Collecting Sparse-Sketch with AllReduce" (the AllReduce of
+ *                  Algorithm 1): sketches add element-wise, bitmaps merge by OR.  On one
+ *                  GPU the W workers are W buffers and the AllReduce is this local step.
+ *   s2r_decode  -- Section 3.1 "Decompressing Sparse Gradient" and the query loop of
+ *                  Algorithm 1: for every set bit i, g_hat(i) = median over rows j of
+ *                  s_j(i) * S[j, h_j(i)]; every clear bit decodes to +0.0.
+ *   s2r_hash    -- the bucket and sign hashes of Algorithm 1 on arbitrary keys (test hook).
+ *
+ * Conventions shared by every call:
+ *   - Device arrays are caller-owned device memory (hipMalloc / torch tensors).  The
+ *     library never allocates, frees or synchronises; it keeps no global state, so calls
+ *     from several host threads are safe as long as their buffers differ.
+ *   - Work is only enqueued on `stream` (a hipStream_t; NULL = the default stream).  Every
+ *     argument check happens on the host before anything is enqueued, so a call that
+ *     returns an error has enqueued nothing.  S2R_ERR_HIP means a launch failed.
+ *   - Indices are the element positions 0..n-1 of a worker's gradient, so n < 2^32.
+ *   - Bitmap layout: ceil(n/64) uint64 words per bitmap, bit i = bit (i % 64) of word
+ *     i / 64 (least significant bit first); bits >= n are 0 on output.
+ *   - Sketch layout: fp32 [d][w] row-major per worker, w = 2^log2_w.
+ *   - "Non-zero" means (bits(x) & 0x7fffffff) != 0: +0 and -0 are zero, subnormals are
+ *     not.  Non-finite gradient values are outside the contract.
+ */
+#ifndef S2R_H
+#define S2R_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define S2R_MAX_ROWS 16
+
+typedef enum {
+  S2R_OK = 0,
+  S2R_ERR_NULL = 1,      /* a required pointer is NULL                                 */
+  S2R_ERR_DIM = 2,       /* a size or parameter is out of range                        */
+  S2R_ERR_ALIGN = 3,     /* a pointer or leading dimension breaks an alignment rule     */
+  S2R_ERR_WORKSPACE = 4, /* the workspace is smaller than the *_workspace_bytes query    */
+  S2R_ERR_HIP = 5        /* a HIP launch failed                                        */
+} s2r_status;
+
+/* Hash constants shared by every worker and by encode and decode (Algorithm 1 draws its
+ * sign hashes {s_j} and bucket hashes {h_j} once, before the worker loop).  Host memory;
+ * copied at call time.
+ *
+ *   MAS_b(a, c; x) = ((a * x + c) mod 2^64) >> (64 - b)   (the top b bits; 0 when b = 0)
+ *   P(i)   = MAS_{L-K}(pA, pB; i)          partition hash, shared by all rows
+ *   Q_j(i) = MAS_K(hA[j], hB[j]; i)        row hash
+ *   h_j(i) = P(i) * 2^K + Q_j(i)           bucket in row j, 0 <= h_j(i) < 2^L
+ *   s_j(i) = +1 if MAS_1(sA[j], sB[j]; i) == 0 else -1
+ *
+ * with L = log2_w and K = log2_part.  K == L makes every row an independent
+ * multiply-add-shift hash (Dietzfelbinger 1996).  K < L keeps each row a uniform
+ * 2-independent map onto 2^L buckets but groups all rows of an item into the same
+ * partition of 2^K buckets per row; the library then accumulates and queries one
+ * partition at a time in LDS instead of through global atomics and gathers.
+ */
+typedef struct {
+  uint32_t d;         /* rows (the pages' r), 1..S2R_MAX_ROWS                         */
+  uint32_t log2_w;    /* L: w = 2^L buckets per row (the pages' c, also m), 0..31        */
+  uint32_t log2_part; /* K: 0..L, see above                                            */
+  uint32_t reserved;  /* must be 0                                                     */
+  uint64_t pA, pB;
+  uint64_t hA[S2R_MAX_ROWS], hB[S2R_MAX_ROWS];
+  uint64_t sA[S2R_MAX_ROWS], sB[S2R_MAX_ROWS];
+} s2r_params;
+
+/* Fill *out from a 64-bit seed: SplitMix64 (Steele, Lea & Flood 2014) seeded with `seed`
+ * yields pA, pB, then hA[j], hB[j], sA[j], sB[j] for j = 0..d-1.  Pure host code.
+ * Errors: S2R_ERR_NULL (out), S2R_ERR_DIM (d, log2_w or log2_part out of range). */
+s2r_status s2r_params_from_seed(uint64_t seed, uint32_t d, uint32_t log2_w, uint32_t log2_part,
+                                s2r_params* out);
+
+/* The largest K <= log2_w whose partition tile (d rows x 2^K fp32 buckets) fits the LDS
+ * budget of the partitioned path; pure host code. */
+uint32_t s2r_default_log2_part(uint32_t d, uint32_t log2_w);
+
+/* ceil(n / 64): uint64 words per bitmap. */
+uint64_t s2r_bitmap_words(uint64_t n);
+
+/* Bytes of device workspace s2r_encode needs for W workers of n elements with list
+ * capacity `cap` per worker (0 if the arguments are invalid). */
+size_t s2r_encode_workspace_bytes(const s2r_params* p, uint32_t W, uint64_t n, uint64_t cap);
+
+/* Compression of W workers' gradients in one call (Section 3.1; Algorithm 1, steps before
+ * the AllReduce).
+ *   grad      [W][ld] fp32, row k = worker k; 16-byte aligned, ld % 4 == 0, ld >= n.
+ *   bitmaps   [W][s2r_bitmap_words(n)] uint64 out.
+ *   sketches  [W][d][w] fp32 out (fully overwritten; need not be initialised).
+ *   idx, val  [W][cap] out: worker k's non-zero indices in ascending order and their
+ *             exact fp32 values (the compacted Sparse(g_k)); may be NULL only if cap == 0.
+ *   nnz       [W] uint64 out: exact non-zero count of each worker.
+ *   workspace device memory of at least s2r_encode_workspace_bytes(p, W, n, cap) bytes,
+ *             256-byte aligned; its contents on entry do not matter.
+ * Capacity: if nnz[k] > cap, the bitmap and nnz of worker k are still exact, but its
+ * list holds only the first cap entries and its sketch is unspecified; cap >= n is always
+ * safe.  Sketch cells are fp32 sums whose order is unspecified (each differs from the
+ * exact sum by at most (count-1) * 2^-24 * sum|contributions|).
+ * Aliasing: no output may overlap grad or another output.
+ * Errors (nothing enqueued): S2R_ERR_NULL, S2R_ERR_DIM (W == 0, n >= 2^32, ld < n, bad
+ * params), S2R_ERR_ALIGN, S2R_ERR_WORKSPACE; S2R_ERR_HIP on a failed launch.
+ * n == 0 writes nnz = 0 and zero sketches. */
+s2r_status s2r_encode(const s2r_params* p, uint32_t W, const float* grad, uint64_t n,
+                      uint64_t ld, uint64_t* bitmaps, float* sketches, uint32_t* idx,
+                      float* val, uint64_t cap, uint64_t* nnz, void* workspace,
+                      size_t ws_bytes, void* stream);
+
+/* Aggregation (Section 3.1; the AllReduce of Algorithm 1) of W workers on one GPU:
+ *   sketch_out[c] = sum_{k=0..W-1} sketches[k][c]   (fp32, added in order k = 0, 1, ...)
+ *   bitmap_out[q] = OR_k bitmaps[k][q]
+ * sketches [W][d][w] and bitmaps [W][s2r_bitmap_words(n)] in, sketch_out [d][w] and
+ * bitmap_out [words] out.  sketch_out may equal `sketches` and bitmap_out may equal
+ * `bitmaps` (in place into worker 0's slot); other overlaps are not allowed.
+ * Errors: S2R_ERR_NULL, S2R_ERR_DIM, S2R_ERR_ALIGN (sketch pointers not 4-byte aligned or
+ * bitmap pointers not 8-byte aligned), S2R_ERR_HIP. */
+s2r_status s2r_reduce(const s2r_params* p, uint32_t W, uint64_t n, const uint64_t* bitmaps,
+                      const float* sketches, uint64_t* bitmap_out, float* sketch_out,
+                      void* stream);
+
+/* Decompression (Section 3.1; the query loop of Algorithm 1):
+ *   out[i] = median_j s_j(i) * sketch[j][h_j(i)]  if bit i of bitmap is set,
+ *   out[i] = +0.0                                 otherwise,           for i < n.
+ * For even d the median is the mean of the two middle values, rounded once to fp32.
+ * bitmap [s2r_bitmap_words(n)] uint64 (bits >= n are ignored), sketch [d][w] fp32,
+ * out [n] fp32, 16-byte aligned.  Must use the same params as the encode that produced
+ * the sketch.  out may not overlap the inputs.
+ * Errors: S2R_ERR_NULL, S2R_ERR_DIM, S2R_ERR_ALIGN, S2R_ERR_HIP. */
+s2r_status s2r_decode(const s2r_params* p, uint64_t n, const uint64_t* bitmap,
+                      const float* sketch, float* out, void* stream);
+
+/* Test hook: the same device hash the other calls use, on arbitrary keys.
+ *   buckets[j * m + t] = h_j(keys[t]),  signs[j * m + t] = s_j(keys[t])  (int8, +1/-1)
+ * Errors: S2R_ERR_NULL, S2R_ERR_DIM, S2R_ERR_HIP. */
+s2r_status s2r_hash(const s2r_params* p, const uint32_t* keys, uint64_t m, uint32_t* buckets,
+                    int8_t* signs, void* stream);
+
+/* Static string naming a status code. */
+const char* s2r_status_string(s2r_status s);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* S2R_H */

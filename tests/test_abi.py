@@ -1,0 +1,118 @@
+"""The C ABI on the CPU: symbols, host-only calls and argument checks (no GPU needed).
+
+Every call here returns before anything is enqueued, so no device is touched.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import oracle
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "s2r.h")
+
+
+@pytest.fixture(scope="module")
+def s2r():
+    import count_sketch_aggregation_amd as m
+    if not os.path.exists(m.LIB_PATH):
+        from count_sketch_aggregation_amd import _build
+        _build.build()
+    return m
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(s2r_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_symbols_exported(s2r):
+    names = _declared()
+    assert {"s2r_encode", "s2r_reduce", "s2r_decode", "s2r_hash"} <= set(names)
+    L = ctypes.CDLL(s2r.LIB_PATH)
+    for name in names:
+        assert hasattr(L, name), f"{name} declared in s2r.h but not exported"
+
+
+def test_params_match_oracle(s2r):
+    for (seed, d, L, K) in [(0, 1, 0, 0), (1, 3, 14, 13), (2**64 - 1, 16, 31, 11), (7, 5, 20, 20)]:
+        p = s2r.s2r_params_from_seed(seed, d, L, K)
+        assert p.as_dict() == oracle.params_from_seed(seed, d, L, K).as_dict()
+
+
+def test_params_range_checks(s2r):
+    for args in [(0, 0, 10, 10), (0, 17, 10, 10), (0, 3, 32, 10), (0, 3, 10, 11)]:
+        with pytest.raises(s2r.S2RError) as e:
+            s2r.s2r_params_from_seed(*args)
+        assert e.value.status == s2r.S2R_ERR_DIM
+
+
+def test_small_helpers(s2r):
+    assert [s2r.s2r_bitmap_words(n) for n in (0, 1, 64, 65, 2**32 - 1)] == [0, 1, 1, 2, 2**26]
+    # partition tile = d x 2^K fp32 must fit 128 KiB of LDS
+    assert s2r.s2r_default_log2_part(5, 23) == 12
+    assert s2r.s2r_default_log2_part(3, 19) == 13
+    assert s2r.s2r_default_log2_part(1, 10) == 10
+    assert s2r.s2r_default_log2_part(16, 31) == 11
+    p = s2r.s2r_params_from_seed(1, 3, 14, 13)
+    assert s2r.s2r_encode_workspace_bytes(p, 4, 1 << 20, 1 << 20) > 0
+    assert s2r.s2r_encode_workspace_bytes(p, 0, 1 << 20, 1 << 20) == 0
+    assert s2r.s2r_encode_workspace_bytes(p, 1, 1 << 32, 1) == 0
+    assert s2r.status_string(s2r.S2R_ERR_WORKSPACE) == "workspace too small"
+
+
+FAKE = 1 << 20  # a 256-byte aligned non-null address; never dereferenced on these paths
+
+
+def _encode(s2r, p, **kw):
+    a = dict(W=2, grad=FAKE, n=1000, ld=1000, bitmaps=FAKE, sketches=FAKE, idx=FAKE, val=FAKE,
+             cap=1000, nnz=FAKE, workspace=FAKE, ws_bytes=1 << 40, stream=0)
+    a.update(kw)
+    return s2r.lib().s2r_encode(ctypes.byref(p), a["W"], a["grad"], a["n"], a["ld"], a["bitmaps"],
+                                a["sketches"], a["idx"], a["val"], a["cap"], a["nnz"],
+                                a["workspace"], a["ws_bytes"], a["stream"])
+
+
+def test_encode_argument_errors(s2r):
+    p = s2r.s2r_params_from_seed(3, 3, 10, 10)
+    assert _encode(s2r, p, grad=None) == s2r.S2R_ERR_NULL
+    assert _encode(s2r, p, nnz=None) == s2r.S2R_ERR_NULL
+    assert _encode(s2r, p, idx=None) == s2r.S2R_ERR_NULL          # cap > 0 needs a list
+    assert _encode(s2r, p, W=0) == s2r.S2R_ERR_DIM
+    assert _encode(s2r, p, n=2**32, ld=2**32) == s2r.S2R_ERR_DIM
+    assert _encode(s2r, p, ld=996) == s2r.S2R_ERR_DIM              # ld < n
+    assert _encode(s2r, p, ld=1002) == s2r.S2R_ERR_ALIGN           # ld % 4
+    assert _encode(s2r, p, grad=FAKE + 4) == s2r.S2R_ERR_ALIGN     # grad not 16-byte aligned
+    assert _encode(s2r, p, bitmaps=FAKE + 4) == s2r.S2R_ERR_ALIGN
+    need = s2r.s2r_encode_workspace_bytes(p, 2, 1000, 1000)
+    assert _encode(s2r, p, ws_bytes=need - 1) == s2r.S2R_ERR_WORKSPACE
+    bad = s2r.s2r_params_from_seed(3, 3, 10, 10)
+    bad.reserved = 1
+    assert _encode(s2r, bad) == s2r.S2R_ERR_DIM
+    bad = s2r.s2r_params_from_seed(3, 3, 10, 10)
+    bad.log2_part = 11
+    assert _encode(s2r, bad) == s2r.S2R_ERR_DIM
+
+
+def test_reduce_decode_hash_argument_errors(s2r):
+    L = s2r.lib()
+    p = s2r.s2r_params_from_seed(3, 3, 10, 10)
+    pr = ctypes.byref(p)
+    assert L.s2r_reduce(pr, 2, 100, FAKE, None, FAKE, FAKE, 0) == s2r.S2R_ERR_NULL
+    assert L.s2r_reduce(pr, 0, 100, FAKE, FAKE, FAKE, FAKE, 0) == s2r.S2R_ERR_DIM
+    assert L.s2r_reduce(pr, 2, 100, FAKE + 4, FAKE, FAKE, FAKE, 0) == s2r.S2R_ERR_ALIGN
+    assert L.s2r_decode(pr, 100, None, FAKE, FAKE, 0) == s2r.S2R_ERR_NULL
+    assert L.s2r_decode(pr, 2**32, FAKE, FAKE, FAKE, 0) == s2r.S2R_ERR_DIM
+    assert L.s2r_decode(pr, 100, FAKE, FAKE, FAKE + 4, 0) == s2r.S2R_ERR_ALIGN  # out 16-byte
+    assert L.s2r_hash(pr, None, 10, FAKE, FAKE, 0) == s2r.S2R_ERR_NULL
+    assert L.s2r_hash(None, FAKE, 10, FAKE, FAKE, 0) == s2r.S2R_ERR_NULL
+
+
+def test_binding_refuses_without_library(s2r, tmp_path, monkeypatch):
+    monkeypatch.setattr(s2r, "LIB_PATH", str(tmp_path / "missing.so"))
+    monkeypatch.setattr(s2r, "_lib", None)
+    with pytest.raises(ImportError):
+        s2r.lib()

@@ -1,0 +1,220 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle on seeded inputs.
+
+Sizes are ones the oracle finishes in seconds while still spanning several 8192-element
+tiles, several 8192-entry list chunks and ragged tails.  Both hash families are covered:
+log2_part == log2_w (independent rows; the global-atomic path whenever the d x w table
+exceeds the LDS accumulator) and the LDS-partitioned default.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import workloads as WL
+
+pytestmark = pytest.mark.gpu
+
+gp = pytest.importorskip("gpu_path")
+
+
+def _grads(W, n, ld, density, seed, integer=False, pad=0.0, block=None):
+    rows = []
+    for k in range(W):
+        if block:
+            idx, val = WL.blocks_sparse(n, block, density, seed + k)
+        else:
+            idx, val = WL.uniform_sparse(n, density, seed + k, integer=integer)
+        rows.append(WL.dense_from_sparse(n, idx, val, ld=ld, fill_pad=pad))
+    return np.stack(rows)
+
+
+# ---------------------------------------------------------------------------------------
+# hash
+
+
+@pytest.mark.parametrize("d,L,K", [(1, 0, 0), (3, 14, 14), (3, 14, 13), (5, 22, 12), (16, 31, 11),
+                                   (4, 31, 31), (2, 9, 0), (7, 17, 5)])
+def test_hash_bit_exact(d, L, K):
+    gp.say(f"hash d={d} L={L} K={K}")
+    p, op = gp.params_pair(1234 + L, d, L, K)
+    rng = np.random.Generator(np.random.PCG64(L))
+    keys = np.concatenate([np.arange(1 << 16), rng.integers(0, 2**32, 1 << 16),
+                           [2**32 - 1, 2**31, 2**31 - 1]]).astype(np.uint32)
+    b, s = gp.run_hash(p, keys)
+    ob, os_ = oracle.hash_keys(op, keys)
+    assert np.array_equal(b, ob)
+    assert np.array_equal(s, os_)
+
+
+# ---------------------------------------------------------------------------------------
+# encode
+
+
+ENCODE_CASES = [
+    # (name, W, n, ld, density, d, L, K or None, extra)
+    ("tiny_cfg_atomic", 4, 1 << 20, 1 << 20, 0.01, 3, 14, 14, {}),
+    ("tiny_cfg_partitioned", 4, 1 << 20, 1 << 20, 0.01, 3, 14, None, {}),
+    ("n1", 1, 1, 4, 1.0, 3, 10, None, {}),
+    ("n63", 2, 63, 64, 0.5, 3, 10, None, {}),
+    ("n64", 2, 64, 64, 0.5, 3, 10, 10, {}),
+    ("n65_pad_garbage", 3, 65, 72, 0.5, 2, 8, None, {"pad": 7.0}),
+    ("tile_edges", 2, 8193, 8196, 0.3, 5, 16, None, {}),
+    ("ragged_many_tiles", 3, 100_003, 100_008, 0.05, 3, 15, None, {"pad": float("nan")}),
+    ("dense_all", 2, 20_000, 20_000, 1.0, 3, 12, None, {}),
+    ("all_zero", 2, 30_000, 30_000, 0.0, 3, 12, None, {}),
+    ("blocks_partitioned", 4, 300_000, 300_000, 0.05, 5, 18, None, {"block": 256}),
+    ("blocks_atomic", 2, 300_000, 300_000, 0.05, 5, 18, 18, {"block": 256}),
+    ("d1", 2, 50_000, 50_000, 0.1, 1, 12, None, {}),
+    ("d16", 2, 50_000, 50_000, 0.1, 16, 12, None, {}),
+    ("d2_w1", 2, 5_000, 5_000, 0.1, 2, 0, 0, {}),
+    ("w2_K0", 2, 5_000, 5_000, 0.1, 3, 1, 0, {}),
+    ("K0_many_partitions", 2, 200_000, 200_000, 0.05, 3, 13, 0, {}),
+]
+
+
+@pytest.mark.parametrize("case", ENCODE_CASES, ids=[c[0] for c in ENCODE_CASES])
+def test_encode(case):
+    name, W, n, ld, density, d, L, K, extra = case
+    gp.say(f"encode {name}: W={W} n={n} ld={ld} d={d} L={L} K={K}")
+    p, op = gp.params_pair(WL.HASH_SEED_BASE + len(name), d, L, K)
+    grads = _grads(W, n, ld, density, 10 + len(name), pad=extra.get("pad", 0.0),
+                   block=extra.get("block"))
+    res = gp.run_encode(p, grads, n)
+    gp.assert_encode_matches(op, grads, n, res)
+
+
+@pytest.mark.parametrize("K", [None, 15])
+def test_encode_integer_values_exact(K):
+    """Integer values: every fp32 partial sum is exact, so the sketch must be bit-exact."""
+    gp.say(f"encode integer K={K}")
+    W, n, d, L = 3, 200_000, 3, 15
+    p, op = gp.params_pair(77, d, L, K)
+    grads = _grads(W, n, n, 0.2, 5, integer=True)
+    res = gp.run_encode(p, grads, n)
+    gp.assert_encode_matches(op, grads, n, res, exact_sketch=True)
+
+
+def test_encode_special_values():
+    """+0/-0 are zero; subnormals are non-zero and kept bit-exact."""
+    gp.say("encode special values")
+    n = 10_000
+    g = np.zeros((1, n), np.float32)
+    g[0, 1::7] = -0.0
+    g[0, 2::11] = np.float32(1e-45)
+    g[0, 3::13] = -np.float32(3e-39)
+    g[0, 5::17] = np.float32(1.5)
+    p, op = gp.params_pair(5, 3, 11)
+    res = gp.run_encode(p, g, n)
+    gp.assert_encode_matches(op, g, n, res)
+
+
+@pytest.mark.parametrize("cap", [0, 1, 1000, 8192, 8193])
+def test_encode_capacity(cap):
+    """nnz beyond cap: bitmap and nnz exact, the first cap list entries exact."""
+    gp.say(f"encode capacity cap={cap}")
+    W, n = 2, 300_000
+    p, op = gp.params_pair(9, 3, 14)
+    grads = _grads(W, n, n, 0.05, 3)
+    res = gp.run_encode(p, grads, n, cap=cap)
+    gp.assert_encode_matches(op, grads, n, res, cap=cap)
+
+
+def test_encode_deterministic_integer_parts():
+    """Two runs give identical bitmaps and lists (catches races in the compaction)."""
+    gp.say("encode twice")
+    W, n = 4, 400_000
+    p, _ = gp.params_pair(21, 5, 18)
+    grads = _grads(W, n, n, 0.03, 8, block=512)
+    a = gp.run_encode(p, grads, n)
+    b = gp.run_encode(p, grads, n)
+    for key in ("bitmaps", "idx", "nnz"):
+        assert np.array_equal(a[key], b[key])
+    assert np.array_equal(a["val"].view(np.uint32), b["val"].view(np.uint32))
+
+
+# ---------------------------------------------------------------------------------------
+# reduce (on tables that do not come from an encode)
+
+
+@pytest.mark.parametrize("W,d,L,n,inplace", [(1, 3, 10, 1000, False), (4, 3, 14, 1 << 20, False),
+                                             (16, 3, 12, 99_999, False), (8, 5, 16, 640, True),
+                                             (3, 3, 1, 70, False), (5, 1, 0, 1, False)])
+def test_reduce(W, d, L, n, inplace):
+    gp.say(f"reduce W={W} d={d} L={L} n={n} inplace={inplace}")
+    p, _ = gp.params_pair(3, d, L)
+    sk = np.stack([WL.random_sketch((d, 1 << L), 100 + k) for k in range(W)])
+    bms = np.stack([WL.random_bitmap(n, 0.1, 200 + k) for k in range(W)])
+    bm, S = gp.run_reduce(p, n, bms, sk, inplace=inplace)
+    obm, oS, oA = oracle.reduce(bms, sk.astype(np.float64), np.abs(sk.astype(np.float64)))
+    assert np.array_equal(bm, obm)
+    gp.assert_sketch_close(S, oS, oA, "reduced sketch")
+    # the sum runs in worker order: it equals a left-to-right fp32 replay
+    replay = sk[0].copy()
+    for k in range(1, W):
+        replay = replay + sk[k]
+    assert np.array_equal(S.view(np.uint32), replay.view(np.uint32))
+
+
+def test_reduce_integer_exact():
+    gp.say("reduce integer")
+    W, d, L, n = 8, 5, 13, 5000
+    p, _ = gp.params_pair(4, d, L)
+    sk = np.stack([WL.random_sketch((d, 1 << L), 300 + k, integer=True) for k in range(W)])
+    bms = np.stack([WL.random_bitmap(n, 0.3, 400 + k) for k in range(W)])
+    bm, S = gp.run_reduce(p, n, bms, sk)
+    obm, oS, _ = oracle.reduce(bms, sk.astype(np.float64), np.abs(sk.astype(np.float64)))
+    assert np.array_equal(bm, obm) and np.array_equal(S.astype(np.float64), oS)
+
+
+# ---------------------------------------------------------------------------------------
+# decode (on a generated bitmap and sketch)
+
+
+@pytest.mark.parametrize("d,L,K,n,density", [(3, 14, 13, 1 << 20, 0.04), (5, 16, 12, 100_003, 0.3),
+                                             (1, 10, 10, 4097, 0.5), (2, 10, 4, 5000, 0.5),
+                                             (4, 12, 12, 65, 1.0), (7, 9, 3, 9000, 0.2),
+                                             (16, 11, 11, 3000, 0.2), (5, 20, 12, 1, 1.0)])
+def test_decode(d, L, K, n, density):
+    gp.say(f"decode d={d} L={L} K={K} n={n}")
+    p, op = gp.params_pair(55 + d, d, L, K)
+    sketch = WL.random_sketch((d, 1 << L), 7 * d)
+    bm = WL.random_bitmap(n, density, 9 * d)
+    # set bits beyond n in the input: they must be ignored
+    if n % 64:
+        bm[-1] |= np.uint64(~((1 << (n % 64)) - 1) & 0xFFFFFFFFFFFFFFFF)
+    out = gp.run_decode(p, n, bm, sketch)
+    want, tol = oracle.decode_dense(op, n, bm, sketch.astype(np.float64))
+    setmask = gp.bits_of(bm, n)
+    # odd d: the median selects one of the fp32 inputs, so the result is exact
+    gp.assert_decode_matches(out, want, tol, setmask, exact=(d % 2 == 1))
+
+
+def test_decode_empty_bitmap():
+    gp.say("decode empty")
+    p, op = gp.params_pair(1, 3, 12)
+    n = 10_000
+    out = gp.run_decode(p, n, np.zeros(WL.workload(0).N // 64, np.uint64)[: (n + 63) // 64],
+                        WL.random_sketch((3, 1 << 12), 2))
+    assert np.all(out.view(np.uint32) == 0)
+
+
+# ---------------------------------------------------------------------------------------
+# end to end
+
+
+@pytest.mark.parametrize("K", [None, 14])
+def test_pipeline_tiny_config(K):
+    """The tiny workload end to end (W=4, N=2^20, 1% uniform, d=3, w=2^14)."""
+    wl = WL.workload(0)
+    gp.say(f"pipeline tiny K={K}")
+    p, op = gp.params_pair(wl.hash_seed, wl.d, wl.log2_w, K)
+    grads = np.stack([WL.dense_from_sparse(wl.N, *WL.worker_sparse(0, k)) for k in range(wl.W)])
+    res = gp.run_encode(p, grads, wl.N)
+    encs = gp.assert_encode_matches(op, grads, wl.N, res)
+    bm, S = gp.run_reduce(p, wl.N, res["bitmaps"], res["sketches"])
+    obm, oS, oA = oracle.reduce(np.stack([e["bitmap"] for e in encs]),
+                                np.stack([e["S"] for e in encs]), np.stack([e["A"] for e in encs]))
+    assert np.array_equal(bm, obm)
+    gp.assert_sketch_close(S, oS, oA, "reduced sketch")
+    out = gp.run_decode(p, wl.N, bm, S)
+    want, tol = oracle.decode_dense(op, wl.N, obm, oS, oA)
+    gp.assert_decode_matches(out, want, tol, gp.bits_of(obm, wl.N))
