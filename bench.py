@@ -1,0 +1,220 @@
+#!/usr/bin/env python3
+"""Throughput of the sparse-sketch aggregation hot path on one MI355X.
+
+One step = s2r_encode (all W workers) -> s2r_reduce -> s2r_decode over one batch of
+synthetic gradients already resident in HBM.  The metric is gradient elements per second,
+W * N / t_step, in units of 1e9, plus the fraction of the 8 TB/s HBM roofline that the
+dominant phase reaches on its algorithmic bytes:
+
+  encode  W * (4N + 8 words + 4 d w)        read gradients, write bitmaps and sketches
+  reduce  (W + 1) * (4 d w + 8 words)       read W sketches/bitmaps, write one of each
+  decode  8 words + min(4 d w, 4 d U) + 4N  read bitmap and sketch cells, write g_hat
+
+(words = ceil(N/64), U = set bits of the merged bitmap).  List writes and any extra
+traffic of the implementation are not credited.
+
+Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--workload embedding]
+Prints ONE JSON line on stdout; progress goes to stderr.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
+
+
+def log(msg: str) -> None:
+    print(msg, file=sys.stderr, flush=True)
+
+
+def build_inputs(wl, dev, hash_family: str):
+    import numpy as np
+    import torch
+
+    import count_sketch_aggregation_amd as s2r
+    import workloads as WL
+
+    K = wl.log2_w if hash_family == "independent" else s2r.s2r_default_log2_part(wl.d, wl.log2_w)
+    p = s2r.s2r_params_from_seed(wl.hash_seed, wl.d, wl.log2_w, K)
+    ld = (wl.N + 3) // 4 * 4
+    grad = torch.zeros((wl.W, ld), dtype=torch.float32, device=dev)
+    nnz_max = 0
+    sparse = []
+    for k in range(wl.W):
+        idx, val = WL.worker_sparse(wl.cid, k)
+        nnz_max = max(nnz_max, idx.size)
+        grad[k].index_copy_(0, torch.from_numpy(idx.astype(np.int64)).to(dev),
+                            torch.from_numpy(val).to(dev))
+        sparse.append((idx, val))
+        log(f"  worker {k}: nnz={idx.size}")
+    cap = nnz_max
+    return p, grad, ld, cap, sparse
+
+
+def cpu_baseline(wl, sparse, p_dict, budget_s: float = 20.0):
+    """The fp64 oracle, single-threaded, on the first workers of the same workload until
+    about `budget_s` seconds of oracle work are done (at least one worker)."""
+    import numpy as np
+
+    import oracle
+    import workloads as WL
+
+    op = oracle.params_from_constants(p_dict["d"], p_dict["log2_w"], p_dict["log2_part"],
+                                      p_dict["pA"], p_dict["pB"], p_dict["hA"], p_dict["hB"],
+                                      p_dict["sA"], p_dict["sB"])
+    elapsed = 0.0
+    encs = []
+    for k in range(wl.W):
+        g = WL.dense_from_sparse(wl.N, *sparse[k])
+        t0 = time.perf_counter()
+        encs.append(oracle.encode_dense(op, g))
+        elapsed += time.perf_counter() - t0
+        del g
+        est_total = elapsed / len(encs) * (len(encs) + 1) * 1.5
+        if est_total > budget_s:
+            break
+    Wp = len(encs)
+    t0 = time.perf_counter()
+    bm, S, A = oracle.reduce(np.stack([e["bitmap"] for e in encs]), np.stack([e["S"] for e in encs]),
+                             np.stack([e["A"] for e in encs]))
+    oracle.decode(op, wl.N, bm, S, A)
+    elapsed += time.perf_counter() - t0
+    return {
+        "value": round(Wp * wl.N / elapsed / 1e9, 6),
+        "unit": "G gradient-elements/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": f"{Wp} of {wl.W} workers of the {wl.name} workload (full N={wl.N} each): "
+                  f"fp64 encode of each, reduce and decode over them; {elapsed:.1f} s",
+    }
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="embedding",
+                    help="tiny | embedding | resnet50_blocktopk | transformer_mixed | large")
+    ap.add_argument("--hash", dest="hash_family", default="partitioned",
+                    choices=["partitioned", "independent"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the W data-parallel "
+              "workers are simulated as W buffers on that GPU.", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import count_sketch_aggregation_amd as s2r
+    import workloads as WL
+
+    names = {w.name: w for w in WL.WORKLOADS}
+    if args.workload not in names:
+        print(f"unknown workload {args.workload}; choose from {sorted(names)}", file=sys.stderr)
+        return 2
+    wl = names[args.workload]
+    dev = torch.device("cuda:0")
+    log(f"workload {wl.name}: W={wl.W} N={wl.N} d={wl.d} w=2^{wl.log2_w} hash={args.hash_family}")
+    p, grad, ld, cap, sparse = build_inputs(wl, dev, args.hash_family)
+    buf = s2r.alloc_encode_buffers(p, wl.W, wl.N, cap, dev)
+    words = s2r.s2r_bitmap_words(wl.N)
+    bm = torch.empty(max(words, 1), dtype=torch.int64, device=dev)
+    sk = torch.empty((wl.d, 1 << wl.log2_w), dtype=torch.float32, device=dev)
+    out = torch.empty(wl.N, dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        s2r.s2r_encode(p, wl.W, grad, wl.N, ld, buf["bitmaps"], buf["sketches"], buf["idx"],
+                       buf["val"], cap, buf["nnz"], buf["workspace"], stream=stream)
+        if ev is not None:
+            ev[1].record(stream)
+        s2r.s2r_reduce(p, wl.W, wl.N, buf["bitmaps"], buf["sketches"], bm, sk, stream=stream)
+        if ev is not None:
+            ev[2].record(stream)
+        s2r.s2r_decode(p, wl.N, bm, sk, out, stream=stream)
+        if ev is not None:
+            ev[3].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    nnz = buf["nnz"].cpu().numpy()
+    assert all(int(x) <= cap for x in nnz), "list capacity exceeded"
+    U = int(np.unpackbits(bm.cpu().numpy().view(np.uint8), bitorder="little")[:wl.N].sum())
+
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        step(events[s])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    phase_ms = {"encode": 0.0, "reduce": 0.0, "decode": 0.0}
+    for ev in events:
+        phase_ms["encode"] += ev[0].elapsed_time(ev[1])
+        phase_ms["reduce"] += ev[1].elapsed_time(ev[2])
+        phase_ms["decode"] += ev[2].elapsed_time(ev[3])
+    for k in phase_ms:
+        phase_ms[k] /= args.steps
+    ms_per_step = wall * 1e3 / args.steps
+    value = wl.W * wl.N / (ms_per_step * 1e-3) / 1e9
+
+    dw = wl.d * (1 << wl.log2_w)
+    b_alg = {
+        "encode": wl.W * (4 * wl.N + 8 * words + 4 * dw),
+        "reduce": (wl.W + 1) * (4 * dw + 8 * words),
+        "decode": 8 * words + min(4 * dw, 4 * wl.d * U) + 4 * wl.N,
+    }
+    phases = {k: {"ms": round(phase_ms[k], 4), "alg_bytes": b_alg[k],
+                  "alg_GBs": round(b_alg[k] / (phase_ms[k] * 1e-3) / 1e9, 1)} for k in phase_ms}
+    dom = max(phase_ms, key=phase_ms.get)
+    achieved = b_alg[dom] / (phase_ms[dom] * 1e-3) / 1e9
+    step_alg = sum(b_alg.values()) / (ms_per_step * 1e-3) / 1e9
+    log(f"ms/step {ms_per_step:.3f}  phases {phases}  step alg GB/s {step_alg:.0f}")
+
+    result = {
+        "metric": "G gradient-elements/s (encode+reduce+decode) and % of peak HBM GB/s",
+        "value": round(value, 3),
+        "unit": "G gradient-elements/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "W": wl.W, "N": wl.N, "d": wl.d, "w": 1 << wl.log2_w,
+                   "log2_part": p.log2_part, "hash": args.hash_family, "nnz_per_worker": int(nnz.max()),
+                   "set_bits_merged": U},
+        "roofline": {"bound": "hbm", "kernel": f"s2r_{dom}", "achieved": round(achieved, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": None},
+        "step_alg_GBs": round(step_alg, 1),
+        "step_hbm_frac": round(step_alg / HBM_PEAK_GBS, 4),
+        "phases": phases,
+    }
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle) ...")
+        result["cpu_baseline"] = cpu_baseline(wl, sparse, p.as_dict())
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())
