@@ -133,6 +133,9 @@ def main() -> int:
     bm = torch.empty(max(words, 1), dtype=torch.int64, device=dev)
     sk = torch.empty((wl.d, 1 << wl.log2_w), dtype=torch.float32, device=dev)
     out = torch.empty(wl.N, dtype=torch.float32, device=dev)
+    # the merged bitmap has at most sum_k nnz_k set bits
+    max_set = min(wl.N, sum(x[0].size for x in sparse))
+    dws = s2r.alloc_decode_workspace(p, wl.N, max_set, dev)
     stream = torch.cuda.current_stream()
 
     def step(ev=None):
@@ -145,7 +148,7 @@ def main() -> int:
         s2r.s2r_reduce(p, wl.W, wl.N, buf["bitmaps"], buf["sketches"], bm, sk, stream=stream)
         if ev is not None:
             ev[2].record(stream)
-        s2r.s2r_decode(p, wl.N, bm, sk, out, stream=stream)
+        s2r.s2r_decode(p, wl.N, bm, sk, out, max_set=max_set, workspace=dws, stream=stream)
         if ev is not None:
             ev[3].record(stream)
 

@@ -86,7 +86,9 @@ def lib() -> ctypes.CDLL:
         L.s2r_encode.restype = st
         L.s2r_reduce.argtypes = [P(s2r_params), u32, u64, vp, vp, vp, vp, vp]
         L.s2r_reduce.restype = st
-        L.s2r_decode.argtypes = [P(s2r_params), u64, vp, vp, vp, vp]
+        L.s2r_decode_workspace_bytes.argtypes = [P(s2r_params), u64, u64]
+        L.s2r_decode_workspace_bytes.restype = sz
+        L.s2r_decode.argtypes = [P(s2r_params), u64, vp, vp, vp, u64, vp, sz, vp]
         L.s2r_decode.restype = st
         L.s2r_hash.argtypes = [P(s2r_params), vp, u64, vp, vp, vp]
         L.s2r_hash.restype = st
@@ -164,9 +166,18 @@ def s2r_reduce(p: s2r_params, W: int, n: int, bitmaps, sketches, bitmap_out, ske
                             _ptr(sketch_out), _stream(stream)), "s2r_reduce")
 
 
-def s2r_decode(p: s2r_params, n: int, bitmap, sketch, out, stream=None) -> None:
-    _check(lib().s2r_decode(ctypes.byref(p), n, _ptr(bitmap), _ptr(sketch), _ptr(out),
-                            _stream(stream)), "s2r_decode")
+def s2r_decode_workspace_bytes(p: s2r_params, n: int, max_set: int) -> int:
+    return int(lib().s2r_decode_workspace_bytes(ctypes.byref(p), n, max_set))
+
+
+def s2r_decode(p: s2r_params, n: int, bitmap, sketch, out, max_set: int = 0, workspace=None,
+               ws_bytes: int | None = None, stream=None) -> None:
+    """workspace=None selects direct gathers; otherwise pass a buffer of
+    s2r_decode_workspace_bytes(p, n, max_set) bytes (see include/s2r.h)."""
+    if ws_bytes is None:
+        ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().s2r_decode(ctypes.byref(p), n, _ptr(bitmap), _ptr(sketch), _ptr(out), max_set,
+                            _ptr(workspace), ws_bytes, _stream(stream)), "s2r_decode")
 
 
 def s2r_hash(p: s2r_params, keys, m: int, buckets, signs, stream=None) -> None:
@@ -176,6 +187,13 @@ def s2r_hash(p: s2r_params, keys, m: int, buckets, signs, stream=None) -> None:
 
 # ---------------------------------------------------------------------------------------
 # allocation helper (torch supplies device memory; no arithmetic here)
+
+
+def alloc_decode_workspace(p: s2r_params, n: int, max_set: int, device="cuda"):
+    """A workspace tensor for the partitioned decode, or None when it does not apply."""
+    import torch
+    nb = s2r_decode_workspace_bytes(p, n, max_set)
+    return torch.empty((nb,), dtype=torch.uint8, device=device) if nb else None
 
 
 def alloc_encode_buffers(p: s2r_params, W: int, n: int, cap: int, device="cuda") -> dict:
@@ -197,6 +215,7 @@ def alloc_encode_buffers(p: s2r_params, W: int, n: int, cap: int, device="cuda")
 
 __all__ = [
     "s2r_params", "S2RError", "s2r_params_from_seed", "s2r_default_log2_part", "s2r_bitmap_words",
-    "s2r_encode_workspace_bytes", "s2r_encode", "s2r_reduce", "s2r_decode", "s2r_hash",
+    "s2r_encode_workspace_bytes", "s2r_encode", "s2r_reduce", "s2r_decode_workspace_bytes",
+    "s2r_decode", "s2r_hash",
     "alloc_encode_buffers", "status_string", "lib",
 ]

@@ -60,8 +60,6 @@ EncodeLayout encode_layout(const s2r_params& p, uint32_t W, uint64_t n, uint64_t
   off = align256(off + (size_t)W * L.tiles * 4);
   L.off_offsets = off;
   off = align256(off + (size_t)W * (L.tiles + 1) * 4);
-  L.off_chunk_tile = off;
-  off = align256(off + (size_t)W * L.chunks * 4);
   L.off_bidx = L.off_bval = L.off_prefix = off;
   if (L.partitioned) {
     const size_t slots = (size_t)W * L.chunks * kChunk;
@@ -143,26 +141,25 @@ s2r_status s2r_encode(const s2r_params* p, uint32_t W, const float* grad, uint64
   char* ws = static_cast<char*>(workspace);
   uint32_t* counts = reinterpret_cast<uint32_t*>(ws + L.off_counts);
   uint32_t* offsets = reinterpret_cast<uint32_t*>(ws + L.off_offsets);
-  uint32_t* chunk_tile = reinterpret_cast<uint32_t*>(ws + L.off_chunk_tile);
   const uint64_t w = 1ull << p->log2_w;
   const uint64_t dw = (uint64_t)p->d * w;
   const uint64_t words = s2r_bitmap_words(n);
   const HashArgs h = make_hash_args(*p);
 
+  if (!L.partitioned) S2R_TRY(launch_fill_zero(sketches, (uint64_t)W * dw, s));
   S2R_TRY(launch_stream(W, grad, n, ld, L.tiles, bitmaps, counts, s));
-  S2R_TRY(launch_scan(W, L.tiles, counts, offsets, nnz, chunk_tile, L.chunks, cap, s));
+  S2R_TRY(launch_scan(W, L.tiles, counts, offsets, nnz, nullptr, 0, cap, s));
+  S2R_TRY(launch_expand(W, grad, ld, L.tiles, bitmaps, words, offsets, idx, val, cap, s));
   if (L.partitioned) {
     uint32_t* bidx = reinterpret_cast<uint32_t*>(ws + L.off_bidx);
     float* bval = reinterpret_cast<float*>(ws + L.off_bval);
     uint32_t* prefix = reinterpret_cast<uint32_t*>(ws + L.off_prefix);
-    S2R_TRY(launch_list_bin(h, W, grad, ld, L.tiles, bitmaps, words, offsets, chunk_tile, idx, val,
-                            cap, L.chunks, L.partitions, bidx, bval, prefix, s));
+    S2R_TRY(launch_bin(h, W, L.tiles, offsets, idx, val, cap, L.chunks, L.partitions, bidx, bval,
+                       prefix, s));
     S2R_TRY(launch_accumulate(h, W, L.tiles, offsets, cap, L.chunks, L.partitions, bidx, bval,
                               prefix, sketches, w, s));
   } else {
-    S2R_TRY(launch_fill_zero(sketches, (uint64_t)W * dw, s));
-    S2R_TRY(launch_list_atomic(h, W, grad, ld, L.tiles, bitmaps, words, offsets, chunk_tile, idx,
-                               val, cap, L.chunks, sketches, dw, s));
+    S2R_TRY(launch_scatter(h, W, L.tiles, offsets, idx, val, cap, L.chunks, sketches, w, s));
   }
   return S2R_OK;
 }
@@ -182,15 +179,23 @@ s2r_status s2r_reduce(const s2r_params* p, uint32_t W, uint64_t n, const uint64_
   return S2R_OK;
 }
 
+size_t s2r_decode_workspace_bytes(const s2r_params* p, uint64_t n, uint64_t max_set) {
+  if (!params_ok(p) || n >= (1ull << 32)) return 0;
+  return decode_layout(*p, n, max_set).total;
+}
+
 s2r_status s2r_decode(const s2r_params* p, uint64_t n, const uint64_t* bitmap,
-                      const float* sketch, float* out, void* stream) {
+                      const float* sketch, float* out, uint64_t max_set, void* workspace,
+                      size_t ws_bytes, void* stream) {
   if (!p || !sketch) return S2R_ERR_NULL;
   if (n > 0 && (!bitmap || !out)) return S2R_ERR_NULL;
   if (!params_ok(p) || n >= (1ull << 32)) return S2R_ERR_DIM;
-  if (!aligned(bitmap, 8) || !aligned(sketch, 4) || !aligned(out, 16)) return S2R_ERR_ALIGN;
-  const HashArgs h = make_hash_args(*p);
-  S2R_TRY(launch_decode_direct(h, n, bitmap, sketch, 1ull << p->log2_w, out,
-                               static_cast<hipStream_t>(stream)));
+  if (!aligned(bitmap, 8) || !aligned(sketch, 4) || !aligned(out, 16) || !aligned(workspace, 16))
+    return S2R_ERR_ALIGN;
+  if (workspace && ws_bytes > 0 && ws_bytes < decode_layout(*p, n, max_set).total)
+    return S2R_ERR_WORKSPACE;
+  S2R_TRY(launch_decode(make_hash_args(*p), *p, n, bitmap, sketch, out, max_set, workspace,
+                        ws_bytes, static_cast<hipStream_t>(stream)));
   return S2R_OK;
 }
 

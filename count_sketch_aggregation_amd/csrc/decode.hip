@@ -4,11 +4,28 @@
 // loop of Algorithm 1: recover the indices from the set bits of the merged bitmap and, for
 // each, take the median over rows j of s_j(i) * S[j, h_j(i)]; clear bits decode to +0.0.
 //
-// k_decode_direct: one workgroup per 4096 output elements (64 bitmap words).  Wave 0 loads
-// the words, ranks the set bits with a wave prefix sum and lists their local offsets in LDS;
-// every thread then takes whole items (d hashed gathers from the sketch + a register
-// median) and writes the result into an LDS copy of the output tile, which is finally
-// stored with 128-bit coalesced writes (zeros included).
+// Two paths.
+//
+// Direct (no workspace, or a table that does not partition): k_dwrite lists the set bits of
+// each 8192-element tile in LDS and, per item, gathers its d sketch cells from HBM and takes
+// a register median; the tile is written with 128-bit coalesced stores, zeros included.
+// Random gathers into a table larger than L2 run at ~55-80 G/s on MI355X, so this path is
+// bound by the d*U gathers.
+//
+// Partitioned (h_j(i) = P(i) 2^K + Q_j(i), all rows of an item in one partition):
+//   k_dcount   popcount per 8192-element tile of the merged bitmap;
+//   k_scan     tile rank offsets, the number U of set bits, and the tile where every chunk
+//              of 8192 consecutive ranks starts;
+//   k_dbin     per rank chunk: expands its indices from the bitmap, counting-sorts them by
+//              partition in LDS, writes them partition-ordered with per-partition offsets,
+//              and records for every rank its slot in that order;
+//   k_dmedian  per partition: loads the partition's d x 2^K cells into LDS once and takes
+//              every item's median from LDS, writing it at the item's slot;
+//   k_dwrite   per tile: fetches each set bit's median through its slot and writes the tile.
+// If U exceeds the workspace capacity the first three steps do nothing and k_dwrite falls
+// back to the direct gathers, decided on the device.
+#include <string.h>
+
 #include "s2r_launch.hpp"
 
 namespace s2r {
@@ -16,47 +33,302 @@ namespace s2r {
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kDecThreads = 256;
-constexpr int kDecTile = 4096;
-constexpr int kDecWords = kDecTile / 64;
+constexpr int kDecTile = 8192;
+constexpr int kDecWords = kDecTile / 64;     // 128
+constexpr int kDBinThreads = 512;
+constexpr int kDBinWordsPerThread = 4;
+constexpr int kDBinBatchWords = kDBinThreads * kDBinWordsPerThread;  // 2048 words per round
 
+// bitmap word q with the bits at or beyond n cleared
+__device__ __forceinline__ uint64_t masked_word(const uint64_t* __restrict__ bitmap,
+                                                uint64_t nwords, uint64_t n, uint64_t q) {
+  if (q >= nwords) return 0ull;
+  uint64_t wv = bitmap[q];
+  const uint64_t first = q * 64;
+  if (n - first < 64) wv &= (1ull << (n - first)) - 1ull;
+  return wv;
+}
+
+// ---------------------------------------------------------------------------------------
+__global__ __launch_bounds__(kDecWords) void k_dcount(const uint64_t* __restrict__ bitmap,
+                                                      uint64_t n, uint64_t nwords,
+                                                      uint32_t* __restrict__ tcount) {
+  const uint64_t q = (uint64_t)blockIdx.x * kDecWords + threadIdx.x;
+  const uint32_t c = wave_sum((uint32_t)__popcll(masked_word(bitmap, nwords, n, q)));
+  __shared__ uint32_t part[kDecWords / kWave];
+  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = c;
+  __syncthreads();
+  if (threadIdx.x == 0) tcount[blockIdx.x] = part[0] + part[1];
+}
+
+// ---------------------------------------------------------------------------------------
+// k_dbin: grid = rank chunks, 512 threads.
+struct DecodeWs {
+  const uint32_t* toff;       // [tiles + 1] rank offset of every tile
+  const uint32_t* chunk_tile; // [chunks] tile holding rank c * kChunk
+  uint32_t* bidx;             // [chunks][kChunk] indices, partition-ordered per chunk
+  uint16_t* slot;             // [chunks][kChunk] rank -> slot in that order
+  float* gval;                // [chunks][kChunk] median of the item at each slot
+  uint32_t* prefix;           // [P + 1][chunks] partition starts per chunk
+  uint64_t chunks;            // capacity in chunks (max_set rounded up)
+  uint64_t max_set;
+};
+
+__global__ __launch_bounds__(kDBinThreads) void k_dbin(HashArgs h, uint64_t n,
+                                                       const uint64_t* __restrict__ bitmap,
+                                                       uint64_t nwords, uint64_t tiles,
+                                                       DecodeWs ws, uint32_t P) {
+  extern __shared__ uint32_t hist[];  // P + 1
+  __shared__ uint32_t litem[kChunk];  // indices in rank order
+  __shared__ uint32_t sitem[kChunk];  // indices in partition order
+  __shared__ uint32_t wtot[kDBinThreads / kWave];
+  const uint32_t c = blockIdx.x;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const uint64_t U = ws.toff[tiles];
+  if (U > ws.max_set) return;  // over capacity: k_dwrite decodes directly
+  const uint64_t start = (uint64_t)c * kChunk;
+  if (start >= U) return;
+  const uint32_t cnt = (uint32_t)(U - start < kChunk ? U - start : kChunk);
+  const uint64_t end = start + cnt;
+
+  // 1. expand ranks [start, end) into litem, 2048 bitmap words per round
+  const uint32_t t0 = ws.chunk_tile[c];
+  uint64_t q0 = (uint64_t)t0 * kDecWords;
+  uint64_t rank0 = ws.toff[t0];
+  while (rank0 < end && q0 < nwords) {
+    uint64_t wv[kDBinWordsPerThread];
+    uint32_t sum = 0;
+#pragma unroll
+    for (int u = 0; u < kDBinWordsPerThread; ++u) {
+      wv[u] = masked_word(bitmap, nwords, n, q0 + (uint64_t)tid * kDBinWordsPerThread + u);
+      sum += (uint32_t)__popcll(wv[u]);
+    }
+    const uint32_t inc = wave_inclusive_sum(sum);
+    if (lane == kWave - 1) wtot[wave] = inc;
+    __syncthreads();
+    uint32_t before = inc - sum, batch_total = 0;
+    for (int v = 0; v < kDBinThreads / kWave; ++v) {
+      if (v < wave) before += wtot[v];
+      batch_total += wtot[v];
+    }
+    uint64_t r = rank0 + before;
+#pragma unroll
+    for (int u = 0; u < kDBinWordsPerThread; ++u) {
+      uint64_t bits = wv[u];
+      const uint64_t pc = (uint64_t)__popcll(bits);
+      if (r + pc > start && r < end) {
+        const uint32_t ibase = (uint32_t)((q0 + (uint64_t)tid * kDBinWordsPerThread + u) * 64);
+        uint64_t rr = r;
+        while (bits) {
+          const int b = __builtin_ctzll(bits);
+          bits &= bits - 1;
+          if (rr >= start && rr < end) litem[rr - start] = ibase + b;
+          ++rr;
+        }
+      }
+      r += pc;
+    }
+    rank0 += batch_total;
+    q0 += kDBinBatchWords;
+    __syncthreads();  // wtot is reused next round
+  }
+  for (uint32_t p = tid; p <= P; p += kDBinThreads) hist[p] = 0;
+  __syncthreads();
+
+  // 2. counting sort by partition
+  constexpr int R = kChunk / kDBinThreads;
+  uint32_t pp[R], rk[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const uint32_t s = tid + kDBinThreads * r;
+    if (s < cnt) {
+      pp[r] = partition_of(h, litem[s]);
+      rk[r] = atomicAdd(&hist[pp[r]], 1u);
+    }
+  }
+  __syncthreads();
+  {  // exclusive scan of hist[0..P) in place
+    const uint32_t per = (P + kDBinThreads - 1) / kDBinThreads;
+    const uint32_t lo = tid * per < P ? tid * per : P;
+    const uint32_t hi = lo + per < P ? lo + per : P;
+    uint32_t sum = 0;
+    for (uint32_t p = lo; p < hi; ++p) sum += hist[p];
+    const uint32_t inc = wave_inclusive_sum(sum);
+    if (lane == kWave - 1) wtot[wave] = inc;
+    __syncthreads();
+    uint32_t run = inc - sum;
+    for (int v = 0; v < wave; ++v) run += wtot[v];
+    for (uint32_t p = lo; p < hi; ++p) {
+      const uint32_t x = hist[p];
+      hist[p] = run;
+      run += x;
+    }
+    __syncthreads();
+  }
+  uint32_t* pf = ws.prefix + c;
+  for (uint32_t p = tid; p < P; p += kDBinThreads) pf[(uint64_t)p * ws.chunks] = hist[p];
+  if (tid == 0) pf[(uint64_t)P * ws.chunks] = cnt;
+  uint16_t* sl = ws.slot + start;
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const uint32_t s = tid + kDBinThreads * r;
+    if (s < cnt) {
+      const uint32_t pos = hist[pp[r]] + rk[r];
+      sitem[pos] = litem[s];
+      sl[s] = (uint16_t)pos;
+    }
+  }
+  __syncthreads();
+  uint32_t* bo = ws.bidx + start;
+  const uint32_t cnt4 = cnt / 4;
+  for (uint32_t q = tid; q < cnt4; q += kDBinThreads)
+    *reinterpret_cast<uint4*>(bo + 4 * q) = *reinterpret_cast<const uint4*>(&sitem[4 * q]);
+  for (uint32_t s = 4 * cnt4 + tid; s < cnt; s += kDBinThreads) bo[s] = sitem[s];
+}
+
+// ---------------------------------------------------------------------------------------
+// k_dmedian: grid = partitions, 1024 threads.  LDS holds the partition's d x 2^K cells.
 template <int D>
-__global__ __launch_bounds__(kDecThreads) void k_decode_direct(
-    HashArgs h, uint64_t n, uint64_t nwords, const uint64_t* __restrict__ bitmap,
-    const float* __restrict__ sketch, uint64_t w, float* __restrict__ out) {
+__global__ __launch_bounds__(kAccThreads) void k_dmedian(HashArgs h, uint64_t tiles,
+                                                         const float* __restrict__ sketch,
+                                                         uint64_t w, DecodeWs ws, uint32_t P,
+                                                         int vec4) {
+  extern __shared__ float tile[];  // D * 2^K
+  __shared__ uint32_t seg_src[kSegBatch];
+  __shared__ uint32_t seg_off[kSegBatch + 1];
+  __shared__ uint32_t wtot[kAccThreads / kWave];
+  const uint32_t p = blockIdx.x;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const uint64_t U = ws.toff[tiles];
+  if (U > ws.max_set || U == 0) return;
+  const uint32_t pw = 1u << h.K;
+  const float* sk = sketch + (uint64_t)p * pw;
+  if (vec4) {
+    const uint32_t pw4 = pw / 4;
+    for (uint32_t c = tid; c < D * pw4; c += kAccThreads) {
+      const uint32_t j = c / pw4, q = c - j * pw4;
+      *reinterpret_cast<f32x4*>(&tile[j * pw + 4 * q]) =
+          *reinterpret_cast<const f32x4*>(sk + (uint64_t)j * w + 4 * q);
+    }
+  } else {
+    for (uint32_t c = tid; c < D * pw; c += kAccThreads) {
+      const uint32_t j = c / pw, q = c - j * pw;
+      tile[c] = sk[(uint64_t)j * w + q];
+    }
+  }
+  const uint32_t nch = (uint32_t)((U + kChunk - 1) / kChunk);
+  const uint32_t* pf = ws.prefix + (uint64_t)p * ws.chunks;
+  constexpr int PER = kSegBatch / kAccThreads;
+  for (uint32_t cb = 0; cb < nch; cb += kSegBatch) {
+    const uint32_t nb = nch - cb < (uint32_t)kSegBatch ? nch - cb : (uint32_t)kSegBatch;
+    __syncthreads();
+    uint32_t len[PER], sum = 0;
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const uint32_t c = tid * PER + u;
+      len[u] = 0;
+      if (c < nb) {
+        const uint32_t lo = pf[cb + c], hi = pf[ws.chunks + cb + c];
+        seg_src[c] = (cb + c) * (uint32_t)kChunk + lo;
+        len[u] = hi - lo;
+      }
+      sum += len[u];
+    }
+    const uint32_t inc = wave_inclusive_sum(sum);
+    if (lane == kWave - 1) wtot[wave] = inc;
+    __syncthreads();
+    uint32_t run = inc - sum;
+    for (int v = 0; v < wave; ++v) run += wtot[v];
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const uint32_t c = tid * PER + u;
+      if (c <= nb) seg_off[c] = run;
+      run += len[u];
+    }
+    if (tid == kAccThreads - 1 && nb == (uint32_t)kSegBatch) seg_off[kSegBatch] = run;
+    __syncthreads();
+    const uint32_t E = seg_off[nb];
+    for (uint32_t e0 = 0; e0 < E; e0 += 4 * kAccThreads) {
+      uint32_t ii[4];
+      uint64_t at[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const uint32_t e = e0 + u * kAccThreads + tid;
+        if (e < E) {
+          const uint32_t c = segment_of(seg_off, nb, e);
+          at[u] = (uint64_t)seg_src[c] + (e - seg_off[c]);
+          ii[u] = ws.bidx[at[u]];
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        if (e0 + u * kAccThreads + tid < E) {
+          float v[D];
+#pragma unroll
+          for (int j = 0; j < D; ++j)
+            v[j] = apply_sign(tile[j * pw + row_bucket(h, j, ii[u])], sign_mask(h, j, ii[u]));
+          ws.gval[at[u]] = median_of<D>(v);
+        }
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------------------
+// k_dwrite: grid = tiles, 256 threads.  partitioned = 0: direct gathers for every item;
+// partitioned = 1: medians from k_dmedian (direct gathers if U exceeded the capacity).
+template <int D>
+__global__ __launch_bounds__(kDecThreads) void k_dwrite(HashArgs h, uint64_t n, uint64_t nwords,
+                                                        const uint64_t* __restrict__ bitmap,
+                                                        const float* __restrict__ sketch,
+                                                        uint64_t w, float* __restrict__ out,
+                                                        DecodeWs ws, uint64_t tiles,
+                                                        int partitioned) {
   __shared__ float otile[kDecTile];
   __shared__ uint16_t items[kDecTile];
-  __shared__ uint32_t count;
-  const int tid = threadIdx.x;
+  __shared__ uint32_t wtot[2];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const uint64_t base = (uint64_t)blockIdx.x * kDecTile;
-
   for (int c = tid; c < kDecTile; c += kDecThreads) otile[c] = 0.f;
-  if (tid < kWave) {
-    const uint64_t q = (uint64_t)blockIdx.x * kDecWords + tid;
-    uint64_t wv = q < nwords ? bitmap[q] : 0ull;
-    const uint64_t first = q * 64;  // bits at or beyond n are ignored
-    if (first >= n) wv = 0;
-    else if (n - first < 64) wv &= (1ull << (n - first)) - 1ull;
-    const uint32_t pc = (uint32_t)__popcll(wv);
-    const uint32_t inc = wave_inclusive_sum(pc);
-    uint32_t slot = inc - pc;
+  uint64_t wv = 0;
+  if (tid < kDecWords) wv = masked_word(bitmap, nwords, n, (uint64_t)blockIdx.x * kDecWords + tid);
+  const uint32_t pc = (uint32_t)__popcll(wv);
+  const uint32_t inc = wave_inclusive_sum(pc);
+  if (tid < kDecWords && lane == kWave - 1) wtot[wave] = inc;
+  __syncthreads();
+  if (tid < kDecWords) {
+    uint32_t slot_i = inc - pc + (wave ? wtot[0] : 0u);
     while (wv) {
       const int b = __builtin_ctzll(wv);
       wv &= wv - 1;
-      items[slot++] = (uint16_t)(tid * 64 + b);
+      items[slot_i++] = (uint16_t)(tid * 64 + b);
     }
-    if (tid == kWave - 1) count = inc;
   }
   __syncthreads();
-  const uint32_t cnt = count;
-  for (uint32_t e = tid; e < cnt; e += kDecThreads) {
-    const uint32_t li = items[e];
-    const uint32_t i = (uint32_t)(base + li);
-    const uint32_t part = partition_of(h, i);
-    float v[D];
+  const uint32_t cnt = wtot[0] + wtot[1];
+  bool direct = !partitioned;
+  uint64_t rank0 = 0;
+  if (partitioned) {
+    direct = ws.toff[tiles] > ws.max_set;
+    rank0 = ws.toff[blockIdx.x];
+  }
+  if (direct) {
+    for (uint32_t e = tid; e < cnt; e += kDecThreads) {
+      const uint32_t li = items[e];
+      const uint32_t i = (uint32_t)(base + li);
+      const uint32_t part = partition_of(h, i);
+      float v[D];
 #pragma unroll
-    for (int j = 0; j < D; ++j)
-      v[j] = apply_sign(sketch[(uint64_t)j * w + bucket_of(h, part, j, i)], sign_mask(h, j, i));
-    otile[li] = median_of<D>(v);
+      for (int j = 0; j < D; ++j)
+        v[j] = apply_sign(sketch[(uint64_t)j * w + bucket_of(h, part, j, i)], sign_mask(h, j, i));
+      otile[li] = median_of<D>(v);
+    }
+  } else {
+    for (uint32_t e = tid; e < cnt; e += kDecThreads) {
+      const uint64_t r = rank0 + e;
+      const uint64_t chunk_base = r / kChunk * kChunk;
+      otile[items[e]] = ws.gval[chunk_base + ws.slot[r]];
+    }
   }
   __syncthreads();
   if (base + kDecTile <= n) {
@@ -69,14 +341,97 @@ __global__ __launch_bounds__(kDecThreads) void k_decode_direct(
   }
 }
 
-hipError_t launch_decode_direct(const HashArgs& h, uint64_t n, const uint64_t* bitmap,
-                                const float* sketch, uint64_t w, float* out, hipStream_t s) {
+// ---------------------------------------------------------------------------------------
+// host side
+
+static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+DecodeLayout decode_layout(const s2r_params& p, uint64_t n, uint64_t max_set) {
+  DecodeLayout L;
+  L.tiles = (n + kDecTile - 1) / kDecTile;
+  const uint64_t cap = max_set < n ? max_set : n;
+  L.chunks = (cap + kChunk - 1) / kChunk;
+  L.partitioned = use_partitioned(p) && n > 0;
+  L.partitions = 1ull << (p.log2_w - p.log2_part);
+  size_t off = 0;
+  L.off_tcount = off;
+  off = align256(off + L.tiles * 4);
+  L.off_toff = off;
+  off = align256(off + (L.tiles + 1) * 4);
+  L.off_total = off;
+  off = align256(off + 8);
+  L.off_chunk_tile = off;
+  off = align256(off + L.chunks * 4);
+  L.off_bidx = off;
+  off = align256(off + L.chunks * kChunk * 4);
+  L.off_slot = off;
+  off = align256(off + L.chunks * kChunk * 2);
+  L.off_gval = off;
+  off = align256(off + L.chunks * kChunk * 4);
+  L.off_prefix = off;
+  off = align256(off + (L.partitions + 1) * L.chunks * 4);
+  L.total = L.partitioned ? off : 0;
+  return L;
+}
+
+hipError_t launch_decode(const HashArgs& h, const s2r_params& p, uint64_t n,
+                         const uint64_t* bitmap, const float* sketch, float* out,
+                         uint64_t max_set, void* workspace, size_t ws_bytes, hipStream_t s) {
   if (n == 0) return hipSuccess;
-  const uint64_t blocks = (n + kDecTile - 1) / kDecTile;
+  const uint64_t w = 1ull << p.log2_w;
   const uint64_t nwords = (n + 63) / 64;
-  S2R_DISPATCH_D(h.d, hipLaunchKernelGGL((k_decode_direct<D>), dim3((uint32_t)blocks),
-                                         dim3(kDecThreads), 0, s, h, n, nwords, bitmap, sketch, w,
-                                         out));
+  const DecodeLayout L = decode_layout(p, n, max_set);
+  const bool part = L.partitioned && workspace != nullptr && ws_bytes >= L.total;
+  DecodeWs ws;
+  memset(&ws, 0, sizeof(ws));
+  if (part) {
+    char* b = static_cast<char*>(workspace);
+    uint32_t* tcount = reinterpret_cast<uint32_t*>(b + L.off_tcount);
+    uint32_t* toff = reinterpret_cast<uint32_t*>(b + L.off_toff);
+    uint32_t* chunk_tile = reinterpret_cast<uint32_t*>(b + L.off_chunk_tile);
+    ws.toff = toff;
+    ws.chunk_tile = chunk_tile;
+    ws.bidx = reinterpret_cast<uint32_t*>(b + L.off_bidx);
+    ws.slot = reinterpret_cast<uint16_t*>(b + L.off_slot);
+    ws.gval = reinterpret_cast<float*>(b + L.off_gval);
+    ws.prefix = reinterpret_cast<uint32_t*>(b + L.off_prefix);
+    ws.chunks = L.chunks;
+    ws.max_set = L.chunks * kChunk < max_set ? L.chunks * kChunk : max_set;
+    if (ws.max_set > n) ws.max_set = n;
+    hipLaunchKernelGGL(k_dcount, dim3((uint32_t)L.tiles), dim3(kDecWords), 0, s, bitmap, n, nwords,
+                       tcount);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    e = launch_scan(1, L.tiles, tcount, toff, reinterpret_cast<uint64_t*>(b + L.off_total),
+                    chunk_tile, L.chunks, ws.max_set, s);
+    if (e != hipSuccess) return e;
+    if (L.chunks > 0) {
+      const size_t lds = (L.partitions + 1) * sizeof(uint32_t);
+      e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_dbin),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+      if (e != hipSuccess) return e;
+      hipLaunchKernelGGL(k_dbin, dim3((uint32_t)L.chunks), dim3(kDBinThreads), lds, s, h, n,
+                         bitmap, nwords, L.tiles, ws, (uint32_t)L.partitions);
+      e = hipGetLastError();
+      if (e != hipSuccess) return e;
+      const size_t tlds = ((size_t)p.d << p.log2_part) * sizeof(float);
+      const int vec4 = (p.log2_part >= 2 && (reinterpret_cast<uintptr_t>(sketch) % 16) == 0);
+      S2R_DISPATCH_D(p.d, {
+        e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_dmedian<D>),
+                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)tlds);
+        if (e == hipSuccess)
+          hipLaunchKernelGGL((k_dmedian<D>), dim3((uint32_t)L.partitions), dim3(kAccThreads), tlds,
+                             s, h, L.tiles, sketch, w, ws, (uint32_t)L.partitions, vec4);
+      });
+      if (e != hipSuccess) return e;
+      e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
+  }
+  const uint64_t tiles = (n + kDecTile - 1) / kDecTile;
+  S2R_DISPATCH_D(p.d, hipLaunchKernelGGL((k_dwrite<D>), dim3((uint32_t)tiles), dim3(kDecThreads),
+                                         0, s, h, n, nwords, bitmap, sketch, w, out, ws, tiles,
+                                         part ? 1 : 0));
   return hipGetLastError();
 }
 

@@ -5,21 +5,21 @@
 // s_j(i) * g(i) into bucket h_j(i) of each row j for every non-zero g(i).
 //
 // Pipeline on gfx950 (all W workers batched in every launch):
-//   k_stream      streams the gradient once with 128-bit loads; four 64-lane ballots per
-//                 load round give four element-ordered bitmap words; writes the bitmap and
-//                 one non-zero count per 8192-element tile.
-//   k_scan        per worker: exclusive prefix of the tile counts (list offsets), the exact
-//                 nnz, and for every 8192-entry list chunk the tile where it starts.
-//   k_list_*      per list chunk: expands the chunk's bitmap bits into ascending
-//                 (index, value) pairs in LDS, re-reading only the 16-byte groups of the
-//                 gradient that hold a set bit, and writes the list with coalesced stores.
-//                 Then either
-//                   _atomic: adds every pair into the d rows with global fp32 atomics, or
-//                   _bin:    counting-sorts the chunk by partition P(i) in LDS and writes
-//                            the partition-ordered copy plus per-partition offsets;
-//   k_accumulate  (partitioned path) one workgroup per (worker, partition): accumulates the
-//                 partition's d x 2^K buckets in LDS with ds_add_f32 and writes them to the
-//                 sketch with dense coalesced stores (no zero fill, no global atomics).
+//   k_stream      streams the gradient once with 128-bit loads, packs the non-zero tests
+//                 into element-ordered bitmap words through LDS; writes the bitmap and one
+//                 non-zero count per 8192-element tile.
+//   k_scan        per worker: exclusive prefix of the tile counts (list offsets) and nnz.
+//   k_expand      per tile: expands the bitmap words into ascending (index, value) pairs at
+//                 their list offsets, re-reading only the 16-byte gradient groups that hold
+//                 a set bit.
+//   then either (d x w table larger than LDS, independent rows)
+//     k_scatter   reads 8192-entry list chunks and adds each pair into the d rows with
+//                 global fp32 atomics (after a zero fill), or (partitioned path)
+//     k_bin       counting-sorts each list chunk by partition P(i) and writes the
+//                 partition-ordered copy plus per-partition offsets;
+//     k_accumulate one workgroup per (worker, partition): accumulates the partition's
+//                 d x 2^K buckets in LDS and writes them to the sketch with dense coalesced
+//                 stores (no zero fill, no global atomics).
 #include "s2r_launch.hpp"
 
 namespace s2r {
@@ -28,49 +28,62 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 // ---------------------------------------------------------------------------------------
 // k_stream: grid (tiles, W), 256 threads.  Wave w of a tile owns 2048 consecutive elements
-// (8 load rounds of 256): lane l of round r holds elements base + 256 r + 4 l .. +3, so the
-// ballot of component c has bit l = element 4 l + c; interleaving the four ballots' 16-bit
-// slices gives the 64-bit words of elements base + 256 r + 64 q.
-__global__ __launch_bounds__(kStreamThreads) void k_stream(
-    const float* __restrict__ grad, uint64_t n, uint64_t ld, uint64_t tiles, uint64_t words,
-    uint64_t* __restrict__ bitmaps, uint32_t* __restrict__ counts) {
-  const uint32_t t = blockIdx.x, k = blockIdx.y;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const float* row = grad + (uint64_t)k * ld;
-  const uint64_t wave_base = (uint64_t)t * kTile + (uint64_t)wave * (kTile / 4);
+// (8 load rounds of 256): lane l of round r holds elements base + 256 r + 4 l .. +3 in one
+// 128-bit load.  Each lane folds its four non-zero tests into a nibble with vector ops
+// (min(bits << 1, 1) is 1 exactly when the magnitude bits are not all zero), a DPP swap
+// pairs adjacent lanes' nibbles into one byte, and the even lanes drop the bytes into LDS
+// in element order, so the tile's 128 bitmap words assemble in LDS with no scalar-unit work
+// and leave with one coalesced 1 KiB store.
+__device__ __forceinline__ uint32_t nz_bit(float x) { return min(__float_as_uint(x) << 1, 1u); }
 
+template <bool TAIL>
+__device__ __forceinline__ uint32_t stream_tile(const float* __restrict__ row, uint64_t wave_base,
+                                                uint64_t n, uint8_t* lbytes, int lane) {
   f32x4 v[kStreamVec];
 #pragma unroll
   for (int r = 0; r < kStreamVec; ++r) {
     const uint64_t e = wave_base + r * 256 + lane * 4;
     // e is a multiple of 4 and ld % 4 == 0, so e < n <= ld keeps all four lanes in the row
-    if (e < n) v[r] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(row + e));
+    if (!TAIL || e < n) v[r] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(row + e));
     else v[r] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
-
-  uint64_t myword = 0;
+  uint32_t cnt = 0;
 #pragma unroll
   for (int r = 0; r < kStreamVec; ++r) {
-    const uint64_t e = wave_base + r * 256 + lane * 4;
-    const uint64_t b0 = __ballot(e + 0 < n && nonzero_bits(v[r].x));
-    const uint64_t b1 = __ballot(e + 1 < n && nonzero_bits(v[r].y));
-    const uint64_t b2 = __ballot(e + 2 < n && nonzero_bits(v[r].z));
-    const uint64_t b3 = __ballot(e + 3 < n && nonzero_bits(v[r].w));
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int sh = 16 * q;
-      const uint64_t word = spread4(b0 >> sh) | (spread4(b1 >> sh) << 1) |
-                            (spread4(b2 >> sh) << 2) | (spread4(b3 >> sh) << 3);
-      if (lane == r * 4 + q) myword = word;
+    uint32_t nib = nz_bit(v[r].x) | (nz_bit(v[r].y) << 1) | (nz_bit(v[r].z) << 2) |
+                   (nz_bit(v[r].w) << 3);
+    if (TAIL) {  // clear the bits of elements at or beyond n
+      const uint64_t e = wave_base + r * 256 + lane * 4;
+      const uint64_t left = e < n ? n - e : 0;
+      nib &= left >= 4 ? 0xFu : ((1u << left) - 1u);
     }
+    cnt += __popc(nib);
+    const uint32_t odd = __builtin_amdgcn_mov_dpp(nib, 0xB1, 0xF, 0xF, false);  // lane ^ 1
+    if (!(lane & 1)) lbytes[r * 32 + (lane >> 1)] = (uint8_t)(nib | (odd << 4));
   }
-  const uint64_t gw = (uint64_t)t * kTileWords + wave * 32 + lane;
-  if (lane < 32 && gw < words) bitmaps[(uint64_t)k * words + gw] = myword;
+  return cnt;
+}
 
-  uint32_t c = wave_sum(lane < 32 ? (uint32_t)__popcll(myword) : 0u);
+__global__ __launch_bounds__(kStreamThreads) void k_stream(
+    const float* __restrict__ grad, uint64_t n, uint64_t ld, uint64_t tiles, uint64_t words,
+    uint64_t* __restrict__ bitmaps, uint32_t* __restrict__ counts) {
+  __shared__ uint64_t lwords[kTileWords];
   __shared__ uint32_t wcount[kStreamThreads / kWave];
+  const uint32_t t = blockIdx.x, k = blockIdx.y;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const float* row = grad + (uint64_t)k * ld;
+  const uint64_t tile_base = (uint64_t)t * kTile;
+  const uint64_t wave_base = tile_base + (uint64_t)wave * (kTile / 4);
+  uint8_t* lbytes = reinterpret_cast<uint8_t*>(lwords) + wave * (kTile / 4 / 8);
+  uint32_t c = (tile_base + kTile <= n) ? stream_tile<false>(row, wave_base, n, lbytes, lane)
+                                        : stream_tile<true>(row, wave_base, n, lbytes, lane);
+  c = wave_sum(c);
   if (lane == 0) wcount[wave] = c;
   __syncthreads();
+  if (tid < kTileWords) {
+    const uint64_t gw = (uint64_t)t * kTileWords + tid;
+    if (gw < words) bitmaps[(uint64_t)k * words + gw] = lwords[tid];
+  }
   if (tid == 0) counts[(uint64_t)k * tiles + t] = wcount[0] + wcount[1] + wcount[2] + wcount[3];
 }
 
@@ -121,192 +134,203 @@ __global__ __launch_bounds__(kScanThreads) void k_scan(
 }
 
 // ---------------------------------------------------------------------------------------
-// Shared front half of k_list_*: fill lidx/lval[0..cnt) with list positions
-// [start, start + cnt) of worker k in ascending order.  Returns cnt (uniform).
-struct ListChunk {
-  uint32_t k, c;
-  uint64_t start, end;
-};
-
-__device__ __forceinline__ bool next_chunk(uint64_t& g, uint32_t W, uint64_t chunks,
-                                           const uint32_t* offsets, uint64_t tiles,
-                                           uint64_t cap, ListChunk& out) {
-  // walk global chunk ids g, g + gridDim.x, ... skipping chunks beyond a worker's list
-  for (; g < (uint64_t)W * chunks; g += gridDim.x) {
-    const uint32_t k = (uint32_t)(g / chunks);
-    const uint32_t c = (uint32_t)(g % chunks);
-    const uint64_t total = offsets[(uint64_t)k * (tiles + 1) + tiles];
-    const uint64_t lim = total < cap ? total : cap;
-    const uint64_t start = (uint64_t)c * kChunk;
-    if (start >= lim) continue;
-    out.k = k;
-    out.c = c;
-    out.start = start;
-    out.end = start + kChunk < lim ? start + kChunk : lim;
-    return true;
-  }
-  return false;
-}
-
-template <int NT>
-__device__ void expand_chunk(const ListChunk& ch, const float* __restrict__ grad, uint64_t ld,
-                             uint64_t tiles, const uint64_t* __restrict__ bitmaps,
-                             uint64_t words, const uint32_t* __restrict__ offsets,
-                             const uint32_t* __restrict__ chunk_tile, uint64_t chunks,
-                             uint32_t* lidx, float* lval, uint64_t* lwords, uint32_t* lwoff) {
+// k_expand: grid (tiles, W), 256 threads.  Lists the tile's non-zeros at list positions
+// offsets[t] + (rank within the tile): the 128 bitmap words and their popcount prefix go to
+// LDS, then each thread takes 8 groups of four elements and, for the groups holding a set
+// bit, re-reads only that 16-byte group of the gradient (all 8 loads issued before use).
+__global__ __launch_bounds__(kExpandThreads) void k_expand(
+    const float* __restrict__ grad, uint64_t ld, uint64_t tiles,
+    const uint64_t* __restrict__ bitmaps, uint64_t words, const uint32_t* __restrict__ offsets,
+    uint32_t* __restrict__ idx, float* __restrict__ val, uint64_t cap) {
+  const uint32_t t = blockIdx.x, k = blockIdx.y;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const uint32_t* off = offsets + (uint64_t)ch.k * (tiles + 1);
-  const uint64_t* bm = bitmaps + (uint64_t)ch.k * words;
-  const float* row = grad + (uint64_t)ch.k * ld;
-  for (uint64_t t = chunk_tile[(uint64_t)ch.k * chunks + ch.c]; t < tiles; ++t) {
-    const uint64_t o_t = off[t];
-    if (o_t >= ch.end) break;
-    if (off[t + 1] == o_t) continue;  // empty tile
-    // the tile's 128 words and their exclusive popcount prefix
-    if (tid < kTileWords) {
-      const uint64_t q = t * kTileWords + tid;
-      const uint64_t wv = q < words ? bm[q] : 0ull;
-      const uint32_t pc = (uint32_t)__popcll(wv);
-      const uint32_t inc = wave_inclusive_sum(pc);
-      lwords[tid] = wv;
-      lwoff[tid] = inc - pc;
-      if (lane == kWave - 1) lwoff[kTileWords + wave] = inc;  // per-wave totals
-    }
-    __syncthreads();
-    // 2048 groups of four elements per tile
-    for (int gidx = tid; gidx < kTile / 4; gidx += NT) {
-      const int q = gidx >> 4;
-      const uint64_t wv = lwords[q];
-      const uint32_t nib = (uint32_t)(wv >> (4 * (gidx & 15))) & 0xFu;
-      if (!nib) continue;
-      const uint32_t below = (uint32_t)__popcll(wv & ((1ull << (4 * (gidx & 15))) - 1ull));
-      const uint32_t wbase = lwoff[q] + (q >= kWave ? lwoff[kTileWords] : 0u);
-      const uint64_t pos0 = o_t + wbase + below;
-      // a set bit lies below n <= ld and the group is 4-aligned: the 16-byte load stays in
-      // the row
-      const uint64_t e0 = t * kTile + (uint64_t)gidx * 4;
-      const f32x4 v = *reinterpret_cast<const f32x4*>(row + e0);
-      uint32_t r = 0;
+  const uint32_t* off = offsets + (uint64_t)k * (tiles + 1);
+  const uint64_t o_t = off[t];
+  if (off[t + 1] == o_t || o_t >= cap) return;  // nothing of this tile is listed
+  __shared__ uint64_t lwords[kTileWords];
+  __shared__ uint32_t lwoff[kTileWords + 2];
+  if (tid < kTileWords) {
+    const uint64_t q = (uint64_t)t * kTileWords + tid;
+    const uint64_t wv = q < words ? bitmaps[(uint64_t)k * words + q] : 0ull;
+    const uint32_t pc = (uint32_t)__popcll(wv);
+    const uint32_t inc = wave_inclusive_sum(pc);
+    lwords[tid] = wv;
+    lwoff[tid] = inc - pc;
+    if (lane == kWave - 1) lwoff[kTileWords + wave] = inc;
+  }
+  __syncthreads();
+  const float* row = grad + (uint64_t)k * ld + (uint64_t)t * kTile;
+  constexpr int G = kTile / 4 / kExpandThreads;  // groups per thread
+  f32x4 v[G];
+  uint32_t nib[G], pos0[G];
 #pragma unroll
-      for (int c4 = 0; c4 < 4; ++c4) {
-        if (nib & (1u << c4)) {
-          const uint64_t pos = pos0 + r;
-          ++r;
-          if (pos >= ch.start && pos < ch.end) {
-            const uint32_t slot = (uint32_t)(pos - ch.start);
-            lidx[slot] = (uint32_t)(e0 + c4);
-            lval[slot] = v[c4];
-          }
+  for (int m = 0; m < G; ++m) {
+    const int gidx = tid + kExpandThreads * m;
+    const int q = gidx >> 4, sh = 4 * (gidx & 15);
+    const uint64_t wv = lwords[q];
+    nib[m] = (uint32_t)(wv >> sh) & 0xFu;
+    pos0[m] = lwoff[q] + (q >= kWave ? lwoff[kTileWords] : 0u) +
+              (uint32_t)__popcll(wv & ((1ull << sh) - 1ull));
+    // a set bit lies below n <= ld and the group is 4-aligned: the load stays in the row
+    if (nib[m]) v[m] = *reinterpret_cast<const f32x4*>(row + 4 * gidx);
+  }
+  uint32_t* oi = idx + (uint64_t)k * cap;
+  float* ov = val + (uint64_t)k * cap;
+#pragma unroll
+  for (int m = 0; m < G; ++m) {
+    if (!nib[m]) continue;
+    const uint32_t e0 = t * (uint32_t)kTile + 4u * (uint32_t)(tid + kExpandThreads * m);
+    uint64_t pos = o_t + pos0[m];
+#pragma unroll
+    for (int c4 = 0; c4 < 4; ++c4) {
+      if (nib[m] & (1u << c4)) {
+        if (pos < cap) {
+          oi[pos] = e0 + c4;
+          ov[pos] = v[m][c4];
         }
+        ++pos;
       }
     }
-    __syncthreads();
   }
 }
 
+// ---------------------------------------------------------------------------------------
+// k_scatter (independent-row path when the table exceeds LDS): grid (chunks, W).  Reads the
+// chunk's list entries and adds s_j(i) g(i) into every row with global fp32 atomics.
 template <int D>
-__global__ __launch_bounds__(kListThreads) void k_list_atomic(
-    HashArgs h, uint32_t W, const float* __restrict__ grad, uint64_t ld, uint64_t tiles,
-    const uint64_t* __restrict__ bitmaps, uint64_t words, const uint32_t* __restrict__ offsets,
-    const uint32_t* __restrict__ chunk_tile, uint32_t* __restrict__ idx,
-    float* __restrict__ val, uint64_t cap, uint64_t chunks, float* __restrict__ sketches,
-    uint64_t dw) {
-  __shared__ uint32_t lidx[kChunk];
-  __shared__ float lval[kChunk];
-  __shared__ uint64_t lwords[kTileWords];
-  __shared__ uint32_t lwoff[kTileWords + 2];
-  const uint64_t w = dw / D;
-  ListChunk ch;
-  for (uint64_t g = blockIdx.x; next_chunk(g, W, chunks, offsets, tiles, cap, ch);
-       g += gridDim.x) {
-    expand_chunk<kListThreads>(ch, grad, ld, tiles, bitmaps, words, offsets, chunk_tile, chunks,
-                               lidx, lval, lwords, lwoff);
-    const uint32_t cnt = (uint32_t)(ch.end - ch.start);
-    uint32_t* oi = idx + (uint64_t)ch.k * cap + ch.start;
-    float* ov = val + (uint64_t)ch.k * cap + ch.start;
-    for (uint32_t s = threadIdx.x; s < cnt; s += kListThreads) {
-      oi[s] = lidx[s];
-      ov[s] = lval[s];
-    }
-    float* sk = sketches + (uint64_t)ch.k * dw;
-    for (uint32_t pr = threadIdx.x; pr < cnt * D; pr += kListThreads) {
-      const uint32_t s = pr / D;
-      const int j = (int)(pr - s * D);
-      const uint32_t i = lidx[s];
-      const uint32_t b = bucket_of(h, partition_of(h, i), j, i);
-      unsafeAtomicAdd(sk + (uint64_t)j * w + b, apply_sign(lval[s], sign_mask(h, j, i)));
-    }
-    __syncthreads();
+__global__ __launch_bounds__(kScatterThreads) void k_scatter(
+    HashArgs h, uint64_t tiles, const uint32_t* __restrict__ offsets,
+    const uint32_t* __restrict__ idx, const float* __restrict__ val, uint64_t cap,
+    float* __restrict__ sketches, uint64_t w) {
+  const uint32_t c = blockIdx.x, k = blockIdx.y;
+  const uint64_t total = offsets[(uint64_t)k * (tiles + 1) + tiles];
+  const uint64_t lim = total < cap ? total : cap;
+  const uint64_t start = (uint64_t)c * kChunk;
+  if (start >= lim) return;
+  const uint32_t cnt = (uint32_t)(lim - start < kChunk ? lim - start : kChunk);
+  const uint32_t* li = idx + (uint64_t)k * cap + start;
+  const float* lv = val + (uint64_t)k * cap + start;
+  float* sk = sketches + (uint64_t)k * D * w;
+  for (uint32_t s = threadIdx.x; s < cnt; s += kScatterThreads) {
+    const uint32_t i = li[s];
+    const float g = lv[s];
+    const uint32_t part = partition_of(h, i);
+#pragma unroll
+    for (int j = 0; j < D; ++j)
+      unsafeAtomicAdd(sk + (uint64_t)j * w + bucket_of(h, part, j, i),
+                      apply_sign(g, sign_mask(h, j, i)));
   }
 }
 
-// Partitioned path, first half: list + partition-ordered copy of each chunk.
-//   bidx/bval[k][c * kChunk + X[p] ...]: chunk c's pairs grouped by partition p
-//   prefix[k][p][c] = X[p] (p = 0..P), the start of partition p inside chunk c
-__global__ __launch_bounds__(kListThreads) void k_list_bin(
-    HashArgs h, uint32_t W, const float* __restrict__ grad, uint64_t ld, uint64_t tiles,
-    const uint64_t* __restrict__ bitmaps, uint64_t words, const uint32_t* __restrict__ offsets,
-    const uint32_t* __restrict__ chunk_tile, uint32_t* __restrict__ idx,
-    float* __restrict__ val, uint64_t cap, uint64_t chunks, uint32_t partitions,
-    uint32_t* __restrict__ bidx, float* __restrict__ bval, uint32_t* __restrict__ prefix) {
-  __shared__ uint32_t lidx[kChunk];
-  __shared__ float lval[kChunk];
-  __shared__ uint64_t lwords[kTileWords];
-  __shared__ uint32_t lwoff[kTileWords + 2];
-  __shared__ uint32_t wtot[kListThreads / kWave];
-  extern __shared__ uint32_t hist[];  // partitions + 1 counters
+// ---------------------------------------------------------------------------------------
+// Block-wide exclusive scan of hist[0..P) in place (each thread owns a contiguous run).
+template <int NT>
+__device__ __forceinline__ void block_exclusive_scan(uint32_t* hist, uint32_t P, uint32_t* wtot) {
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const uint32_t P = partitions;
-  ListChunk ch;
-  for (uint64_t g = blockIdx.x; next_chunk(g, W, chunks, offsets, tiles, cap, ch);
-       g += gridDim.x) {
-    for (uint32_t p = tid; p <= P; p += kListThreads) hist[p] = 0;
-    expand_chunk<kListThreads>(ch, grad, ld, tiles, bitmaps, words, offsets, chunk_tile, chunks,
-                               lidx, lval, lwords, lwoff);
-    const uint32_t cnt = (uint32_t)(ch.end - ch.start);
-    uint32_t* oi = idx + (uint64_t)ch.k * cap + ch.start;
-    float* ov = val + (uint64_t)ch.k * cap + ch.start;
-    for (uint32_t s = tid; s < cnt; s += kListThreads) {
-      const uint32_t i = lidx[s];
-      oi[s] = i;
-      ov[s] = lval[s];
-      atomicAdd(&hist[partition_of(h, i)], 1u);
+  const uint32_t per = (P + NT - 1) / NT;
+  const uint32_t lo = tid * per < P ? tid * per : P;
+  const uint32_t hi = lo + per < P ? lo + per : P;
+  uint32_t sum = 0;
+  for (uint32_t p = lo; p < hi; ++p) sum += hist[p];
+  const uint32_t inc = wave_inclusive_sum(sum);
+  if (lane == kWave - 1) wtot[wave] = inc;
+  __syncthreads();
+  uint32_t run = inc - sum;
+  for (int v = 0; v < wave; ++v) run += wtot[v];
+  for (uint32_t p = lo; p < hi; ++p) {
+    const uint32_t x = hist[p];
+    hist[p] = run;
+    run += x;
+  }
+  __syncthreads();
+}
+
+// k_bin (partitioned path): grid (chunks, W), 512 threads.  Counting-sorts the chunk's list
+// entries by partition P(i) (u32 LDS atomics give each entry its slot), assembles the sorted
+// chunk in LDS and writes it out with coalesced 128-bit stores:
+//   bidx/bval[k][c * kChunk + X[p] ...]   the chunk's pairs grouped by partition
+//   prefix[k][p][c] = X[p], p = 0..P       the start of partition p inside chunk c
+__global__ __launch_bounds__(kBinThreads) void k_bin(
+    HashArgs h, uint64_t tiles, const uint32_t* __restrict__ offsets,
+    const uint32_t* __restrict__ idx, const float* __restrict__ val, uint64_t cap,
+    uint64_t chunks, uint32_t P, uint32_t* __restrict__ bidx, float* __restrict__ bval,
+    uint32_t* __restrict__ prefix) {
+  extern __shared__ uint32_t hist[];  // P + 1 counters
+  __shared__ uint32_t sidx[kChunk];
+  __shared__ float sval[kChunk];
+  __shared__ uint32_t wtot[kBinThreads / kWave];
+  const uint32_t c = blockIdx.x, k = blockIdx.y;
+  const int tid = threadIdx.x;
+  const uint64_t total = offsets[(uint64_t)k * (tiles + 1) + tiles];
+  const uint64_t lim = total < cap ? total : cap;
+  const uint64_t start = (uint64_t)c * kChunk;
+  if (start >= lim) return;
+  const uint32_t cnt = (uint32_t)(lim - start < kChunk ? lim - start : kChunk);
+  for (uint32_t p = tid; p <= P; p += kBinThreads) hist[p] = 0;
+  __syncthreads();
+  constexpr int R = kChunk / kBinThreads;
+  uint32_t ii[R], pp[R], rk[R];
+  float gg[R];
+  const uint32_t* li = idx + (uint64_t)k * cap + start;
+  const float* lv = val + (uint64_t)k * cap + start;
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const uint32_t s = tid + kBinThreads * r;
+    if (s < cnt) {
+      ii[r] = li[s];
+      gg[r] = lv[s];
     }
-    __syncthreads();
-    // exclusive scan of hist[0..P) in place; each thread owns a contiguous run
-    const uint32_t per = (P + kListThreads - 1) / kListThreads;
-    const uint32_t lo = tid * per < P ? tid * per : P;
-    const uint32_t hi = lo + per < P ? lo + per : P;
-    uint32_t sum = 0;
-    for (uint32_t p = lo; p < hi; ++p) sum += hist[p];
-    const uint32_t inc = wave_inclusive_sum(sum);
-    if (lane == kWave - 1) wtot[wave] = inc;
-    __syncthreads();
-    uint32_t run = inc - sum;
-    for (int v = 0; v < wave; ++v) run += wtot[v];
-    for (uint32_t p = lo; p < hi; ++p) {
-      const uint32_t x = hist[p];
-      hist[p] = run;
-      run += x;
+  }
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const uint32_t s = tid + kBinThreads * r;
+    if (s < cnt) {
+      pp[r] = partition_of(h, ii[r]);
+      rk[r] = atomicAdd(&hist[pp[r]], 1u);
     }
-    __syncthreads();
-    uint32_t* pf = prefix + (uint64_t)ch.k * (P + 1) * chunks + ch.c;
-    for (uint32_t p = tid; p < P; p += kListThreads) pf[(uint64_t)p * chunks] = hist[p];
-    if (tid == 0) pf[(uint64_t)P * chunks] = cnt;
-    __syncthreads();
-    // scatter into partition order; hist[] now serves as the running cursor
-    const uint64_t bbase = ((uint64_t)ch.k * chunks + ch.c) * kChunk;
-    for (uint32_t s = tid; s < cnt; s += kListThreads) {
-      const uint32_t i = lidx[s];
-      const uint32_t pos = atomicAdd(&hist[partition_of(h, i)], 1u);
-      bidx[bbase + pos] = i;
-      bval[bbase + pos] = lval[s];
+  }
+  __syncthreads();
+  block_exclusive_scan<kBinThreads>(hist, P, wtot);
+  uint32_t* pf = prefix + (uint64_t)k * (P + 1) * chunks + c;
+  for (uint32_t p = tid; p < P; p += kBinThreads) pf[(uint64_t)p * chunks] = hist[p];
+  if (tid == 0) pf[(uint64_t)P * chunks] = cnt;
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const uint32_t s = tid + kBinThreads * r;
+    if (s < cnt) {
+      const uint32_t pos = hist[pp[r]] + rk[r];
+      sidx[pos] = ii[r];
+      sval[pos] = gg[r];
     }
-    __syncthreads();
+  }
+  __syncthreads();
+  const uint64_t bbase = ((uint64_t)k * chunks + c) * kChunk;  // 16-byte aligned
+  const uint32_t cnt4 = cnt / 4;
+  for (uint32_t q = tid; q < cnt4; q += kBinThreads) {
+    *reinterpret_cast<uint4*>(bidx + bbase + 4 * q) = *reinterpret_cast<const uint4*>(&sidx[4 * q]);
+    *reinterpret_cast<f32x4*>(bval + bbase + 4 * q) = *reinterpret_cast<const f32x4*>(&sval[4 * q]);
+  }
+  for (uint32_t s = 4 * cnt4 + tid; s < cnt; s += kBinThreads) {
+    bidx[bbase + s] = sidx[s];
+    bval[bbase + s] = sval[s];
   }
 }
 
-// Partitioned path, second half: grid (P, W).  The partition tile is d x 2^K fp32 in LDS.
+// fp32 add into LDS through a 32-bit compare-and-swap loop.  On gfx950 this sustains about
+// 9x the rate of ds_add_f32 for scattered addresses, and the sum is the same fp32 addition.
+__device__ __forceinline__ void lds_add_f32(float* p, float v) {
+  uint32_t* w = reinterpret_cast<uint32_t*>(p);
+  uint32_t old = *w, assumed;
+  do {
+    assumed = old;
+    old = atomicCAS(w, assumed, __float_as_uint(__uint_as_float(assumed) + v));
+  } while (old != assumed);
+}
+
+// k_accumulate (partitioned path): grid (P, W), 512 threads.  The partition's d x 2^K
+// buckets live in LDS.  Its entries are spread over one short segment per list chunk; the
+// segments of up to kSegBatch chunks are flattened with a prefix sum so that consecutive
+// threads read consecutive entries, four per thread in flight.
 template <int D>
 __global__ __launch_bounds__(kAccThreads) void k_accumulate(
     HashArgs h, uint64_t tiles, const uint32_t* __restrict__ offsets, uint64_t cap,
@@ -314,26 +338,72 @@ __global__ __launch_bounds__(kAccThreads) void k_accumulate(
     const float* __restrict__ bval, const uint32_t* __restrict__ prefix,
     float* __restrict__ sketches, uint64_t w, int vec4) {
   extern __shared__ float tile[];  // D * 2^K
+  __shared__ uint32_t seg_src[kSegBatch];
+  __shared__ uint32_t seg_off[kSegBatch + 1];
+  __shared__ uint32_t wtot[kAccThreads / kWave];
   const uint32_t p = blockIdx.x, k = blockIdx.y;
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const uint32_t pw = 1u << h.K;
   const uint32_t cells = D * pw;
   for (uint32_t c = tid; c < cells; c += kAccThreads) tile[c] = 0.f;
-  __syncthreads();
 
   const uint64_t total = offsets[(uint64_t)k * (tiles + 1) + tiles];
   const uint64_t lim = total < cap ? total : cap;
-  const uint64_t nch = (lim + kChunk - 1) / kChunk;
+  const uint32_t nch = (uint32_t)((lim + kChunk - 1) / kChunk);
   const uint32_t* pf = prefix + ((uint64_t)k * (partitions + 1) + p) * chunks;
-  for (uint64_t c = tid; c < nch; c += kAccThreads) {
-    const uint32_t lo = pf[c], hi = pf[chunks + c];
-    const uint64_t base = ((uint64_t)k * chunks + c) * kChunk;
-    for (uint32_t e = lo; e < hi; ++e) {
-      const uint32_t i = bidx[base + e];
-      const float g = bval[base + e];
+  const uint64_t kbase = (uint64_t)k * chunks * kChunk;
+  constexpr int PER = kSegBatch / kAccThreads;
+  for (uint32_t cb = 0; cb < nch; cb += kSegBatch) {
+    const uint32_t nb = nch - cb < (uint32_t)kSegBatch ? nch - cb : (uint32_t)kSegBatch;
+    __syncthreads();  // the previous batch is consumed (and the tile is zeroed)
+    uint32_t len[PER], sum = 0;
 #pragma unroll
-      for (int j = 0; j < D; ++j)
-        atomicAdd(&tile[j * pw + row_bucket(h, j, i)], apply_sign(g, sign_mask(h, j, i)));
+    for (int u = 0; u < PER; ++u) {
+      const uint32_t c = tid * PER + u;
+      len[u] = 0;
+      if (c < nb) {
+        const uint32_t lo = pf[cb + c], hi = pf[chunks + cb + c];
+        seg_src[c] = (cb + c) * (uint32_t)kChunk + lo;
+        len[u] = hi - lo;
+      }
+      sum += len[u];
+    }
+    const uint32_t inc = wave_inclusive_sum(sum);
+    if (lane == kWave - 1) wtot[wave] = inc;
+    __syncthreads();
+    uint32_t run = inc - sum;
+    for (int v = 0; v < wave; ++v) run += wtot[v];
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const uint32_t c = tid * PER + u;
+      if (c <= nb) seg_off[c] = run;  // seg_off[nb] = total entries of the batch
+      run += len[u];
+    }
+    if (tid == kAccThreads - 1 && nb == (uint32_t)kSegBatch) seg_off[kSegBatch] = run;
+    __syncthreads();
+    const uint32_t E = seg_off[nb];
+    for (uint32_t e0 = 0; e0 < E; e0 += 4 * kAccThreads) {
+      uint32_t ii[4];
+      float gg[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const uint32_t e = e0 + u * kAccThreads + tid;
+        if (e < E) {
+          const uint32_t c = segment_of(seg_off, nb, e);
+          const uint64_t pos = kbase + seg_src[c] + (e - seg_off[c]);
+          ii[u] = bidx[pos];
+          gg[u] = bval[pos];
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        if (e0 + u * kAccThreads + tid < E) {
+#pragma unroll
+          for (int j = 0; j < D; ++j)
+            lds_add_f32(&tile[j * pw + row_bucket(h, j, ii[u])],
+                        apply_sign(gg[u], sign_mask(h, j, ii[u])));
+        }
+      }
     }
   }
   __syncthreads();
@@ -388,39 +458,36 @@ hipError_t launch_fill_zero(float* p, uint64_t count, hipStream_t s) {
   return hipGetLastError();
 }
 
-static uint32_t list_grid(uint32_t W, uint64_t chunks) {
-  const uint64_t total = (uint64_t)W * chunks;
-  return (uint32_t)(total < 2048 ? total : 2048);
-}
-
-hipError_t launch_list_atomic(const HashArgs& h, uint32_t W, const float* grad, uint64_t ld,
-                              uint64_t tiles, const uint64_t* bitmaps, uint64_t words,
-                              const uint32_t* offsets, const uint32_t* chunk_tile, uint32_t* idx,
-                              float* val, uint64_t cap, uint64_t chunks, float* sketches,
-                              uint64_t dw, hipStream_t s) {
-  if (chunks == 0) return hipSuccess;
-  const uint32_t grid = list_grid(W, chunks);
-  S2R_DISPATCH_D(h.d, hipLaunchKernelGGL((k_list_atomic<D>), dim3(grid), dim3(kListThreads), 0,
-                                         s, h, W, grad, ld, tiles, bitmaps, words, offsets,
-                                         chunk_tile, idx, val, cap, chunks, sketches, dw));
+hipError_t launch_expand(uint32_t W, const float* grad, uint64_t ld, uint64_t tiles,
+                         const uint64_t* bitmaps, uint64_t words, const uint32_t* offsets,
+                         uint32_t* idx, float* val, uint64_t cap, hipStream_t s) {
+  if (tiles == 0 || cap == 0) return hipSuccess;
+  hipLaunchKernelGGL(k_expand, dim3((uint32_t)tiles, W), dim3(kExpandThreads), 0, s, grad, ld,
+                     tiles, bitmaps, words, offsets, idx, val, cap);
   return hipGetLastError();
 }
 
-hipError_t launch_list_bin(const HashArgs& h, uint32_t W, const float* grad, uint64_t ld,
-                           uint64_t tiles, const uint64_t* bitmaps, uint64_t words,
-                           const uint32_t* offsets, const uint32_t* chunk_tile, uint32_t* idx,
-                           float* val, uint64_t cap, uint64_t chunks, uint64_t partitions,
-                           uint32_t* bidx, float* bval, uint32_t* prefix, hipStream_t s) {
+hipError_t launch_scatter(const HashArgs& h, uint32_t W, uint64_t tiles, const uint32_t* offsets,
+                          const uint32_t* idx, const float* val, uint64_t cap, uint64_t chunks,
+                          float* sketches, uint64_t w, hipStream_t s) {
   if (chunks == 0) return hipSuccess;
-  const uint32_t grid = list_grid(W, chunks);
+  S2R_DISPATCH_D(h.d, hipLaunchKernelGGL((k_scatter<D>), dim3((uint32_t)chunks, W),
+                                         dim3(kScatterThreads), 0, s, h, tiles, offsets, idx, val,
+                                         cap, sketches, w));
+  return hipGetLastError();
+}
+
+hipError_t launch_bin(const HashArgs& h, uint32_t W, uint64_t tiles, const uint32_t* offsets,
+                      const uint32_t* idx, const float* val, uint64_t cap, uint64_t chunks,
+                      uint64_t partitions, uint32_t* bidx, float* bval, uint32_t* prefix,
+                      hipStream_t s) {
+  if (chunks == 0) return hipSuccess;
   const size_t lds = (partitions + 1) * sizeof(uint32_t);
-  // static LDS (66 KiB) + the histogram exceeds the default dynamic limit
-  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_list_bin),
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_bin),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_list_bin, dim3(grid), dim3(kListThreads), lds, s, h, W, grad, ld, tiles,
-                     bitmaps, words, offsets, chunk_tile, idx, val, cap, chunks,
-                     (uint32_t)partitions, bidx, bval, prefix);
+  hipLaunchKernelGGL(k_bin, dim3((uint32_t)chunks, W), dim3(kBinThreads), lds, s, h, tiles,
+                     offsets, idx, val, cap, chunks, (uint32_t)partitions, bidx, bval, prefix);
   return hipGetLastError();
 }
 

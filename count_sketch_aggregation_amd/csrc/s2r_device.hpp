@@ -65,20 +65,6 @@ __device__ __forceinline__ float apply_sign(float v, uint32_t mask) {
   return __uint_as_float(__float_as_uint(v) ^ mask);
 }
 
-__device__ __forceinline__ bool nonzero_bits(float x) {
-  return (__float_as_uint(x) & 0x7FFFFFFFu) != 0u;
-}
-
-// Place bit m of a 16-bit value at bit 4m of a 64-bit word.
-__device__ __forceinline__ uint64_t spread4(uint64_t x) {
-  x &= 0xFFFFull;
-  x = (x | (x << 24)) & 0x000000FF000000FFull;
-  x = (x | (x << 12)) & 0x000F000F000F000Full;
-  x = (x | (x << 6)) & 0x0303030303030303ull;
-  x = (x | (x << 3)) & 0x1111111111111111ull;
-  return x;
-}
-
 // Median of D values (D <= 16), exact selection for odd D; even D gives the mean of the
 // two middle values rounded once (halving is exact away from the subnormal range).
 template <int D>
@@ -125,6 +111,17 @@ __device__ __forceinline__ uint32_t wave_sum(uint32_t x) {
 #pragma unroll
   for (int off = kWave / 2; off > 0; off >>= 1) x += __shfl_xor(x, off, kWave);
   return x;
+}
+
+// Largest c in [0, nb) with off[c] <= e (off non-decreasing, off[0] = 0).
+__device__ __forceinline__ uint32_t segment_of(const uint32_t* off, uint32_t nb, uint32_t e) {
+  uint32_t lo = 0, hi = nb;
+  while (hi - lo > 1) {
+    const uint32_t mid = (lo + hi) >> 1;
+    if (off[mid] <= e) lo = mid;
+    else hi = mid;
+  }
+  return lo;
 }
 
 }  // namespace s2r

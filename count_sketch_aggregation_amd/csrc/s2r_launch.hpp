@@ -15,10 +15,13 @@ constexpr int kStreamVec = 8;                       // float4 loads per thread
 constexpr int kTile = kStreamThreads * kStreamVec * 4;  // 8192 elements per tile
 constexpr int kTileWords = kTile / 64;              // 128 bitmap words per tile
 
-constexpr int kListThreads = 256;
+constexpr int kExpandThreads = 256;
+constexpr int kScatterThreads = 256;
 constexpr int kChunk = 8192;                        // list entries per chunk
+constexpr int kBinThreads = 512;                    // 16 entries per thread
 constexpr int kMaxPartitions = 8192;                // LDS histogram limit of the binning pass
-constexpr int kAccThreads = 512;
+constexpr int kAccThreads = 1024;
+constexpr int kSegBatch = 1024;                     // chunk segments flattened per round
 constexpr size_t kAccLdsBytes = 128 * 1024;         // LDS of one partition tile
 
 constexpr int kScanThreads = 1024;
@@ -29,7 +32,7 @@ struct EncodeLayout {
   uint64_t chunks;       // list chunks per worker (bounded by min(cap, n))
   uint64_t partitions;   // 2^(L-K) on the partitioned path, 0 otherwise
   bool partitioned;
-  size_t off_counts, off_offsets, off_chunk_tile, off_bidx, off_bval, off_prefix, total;
+  size_t off_counts, off_offsets, off_bidx, off_bval, off_prefix, total;
 };
 EncodeLayout encode_layout(const s2r_params& p, uint32_t W, uint64_t n, uint64_t cap);
 bool use_partitioned(const s2r_params& p);
@@ -42,16 +45,16 @@ hipError_t launch_scan(uint32_t W, uint64_t tiles, const uint32_t* counts, uint3
                        uint64_t* nnz, uint32_t* chunk_tile, uint64_t chunks, uint64_t cap,
                        hipStream_t s);
 hipError_t launch_fill_zero(float* p, uint64_t count, hipStream_t s);
-hipError_t launch_list_atomic(const HashArgs& h, uint32_t W, const float* grad, uint64_t ld,
-                              uint64_t tiles, const uint64_t* bitmaps, uint64_t words,
-                              const uint32_t* offsets, const uint32_t* chunk_tile, uint32_t* idx,
-                              float* val, uint64_t cap, uint64_t chunks, float* sketches,
-                              uint64_t dw, hipStream_t s);
-hipError_t launch_list_bin(const HashArgs& h, uint32_t W, const float* grad, uint64_t ld,
-                           uint64_t tiles, const uint64_t* bitmaps, uint64_t words,
-                           const uint32_t* offsets, const uint32_t* chunk_tile, uint32_t* idx,
-                           float* val, uint64_t cap, uint64_t chunks, uint64_t partitions,
-                           uint32_t* bidx, float* bval, uint32_t* prefix, hipStream_t s);
+hipError_t launch_expand(uint32_t W, const float* grad, uint64_t ld, uint64_t tiles,
+                         const uint64_t* bitmaps, uint64_t words, const uint32_t* offsets,
+                         uint32_t* idx, float* val, uint64_t cap, hipStream_t s);
+hipError_t launch_scatter(const HashArgs& h, uint32_t W, uint64_t tiles, const uint32_t* offsets,
+                          const uint32_t* idx, const float* val, uint64_t cap, uint64_t chunks,
+                          float* sketches, uint64_t w, hipStream_t s);
+hipError_t launch_bin(const HashArgs& h, uint32_t W, uint64_t tiles, const uint32_t* offsets,
+                      const uint32_t* idx, const float* val, uint64_t cap, uint64_t chunks,
+                      uint64_t partitions, uint32_t* bidx, float* bval, uint32_t* prefix,
+                      hipStream_t s);
 hipError_t launch_accumulate(const HashArgs& h, uint32_t W, uint64_t tiles,
                              const uint32_t* offsets, uint64_t cap, uint64_t chunks,
                              uint64_t partitions, const uint32_t* bidx, const float* bval,
@@ -61,8 +64,17 @@ hipError_t launch_reduce(uint32_t W, uint64_t cells, uint64_t words, const uint6
                          const float* sketches, uint64_t* bitmap_out, float* sketch_out,
                          hipStream_t s);
 
-hipError_t launch_decode_direct(const HashArgs& h, uint64_t n, const uint64_t* bitmap,
-                                const float* sketch, uint64_t w, float* out, hipStream_t s);
+// Workspace layout of the partitioned decode (total == 0 when the direct path applies).
+struct DecodeLayout {
+  uint64_t tiles, chunks, partitions;
+  bool partitioned;
+  size_t off_tcount, off_toff, off_total, off_chunk_tile, off_bidx, off_slot, off_gval,
+      off_prefix, total;
+};
+DecodeLayout decode_layout(const s2r_params& p, uint64_t n, uint64_t max_set);
+hipError_t launch_decode(const HashArgs& h, const s2r_params& p, uint64_t n,
+                         const uint64_t* bitmap, const float* sketch, float* out,
+                         uint64_t max_set, void* workspace, size_t ws_bytes, hipStream_t s);
 
 hipError_t launch_hash(const HashArgs& h, const uint32_t* keys, uint64_t m, uint32_t* buckets,
                        int8_t* signs, hipStream_t s);

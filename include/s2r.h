@@ -129,6 +129,11 @@ s2r_status s2r_reduce(const s2r_params* p, uint32_t W, uint64_t n, const uint64_
                       const float* sketches, uint64_t* bitmap_out, float* sketch_out,
                       void* stream);
 
+/* Bytes of device workspace that let s2r_decode take the partitioned path for up to
+ * `max_set` set bits (0 when the params do not partition, i.e. the d x 2^K partition tile
+ * does not fit the LDS budget; then s2r_decode always gathers directly). */
+size_t s2r_decode_workspace_bytes(const s2r_params* p, uint64_t n, uint64_t max_set);
+
 /* Decompression (Section 3.1; the query loop of Algorithm 1):
  *   out[i] = median_j s_j(i) * sketch[j][h_j(i)]  if bit i of bitmap is set,
  *   out[i] = +0.0                                 otherwise,           for i < n.
@@ -136,9 +141,17 @@ s2r_status s2r_reduce(const s2r_params* p, uint32_t W, uint64_t n, const uint64_
  * bitmap [s2r_bitmap_words(n)] uint64 (bits >= n are ignored), sketch [d][w] fp32,
  * out [n] fp32, 16-byte aligned.  Must use the same params as the encode that produced
  * the sketch.  out may not overlap the inputs.
- * Errors: S2R_ERR_NULL, S2R_ERR_DIM, S2R_ERR_ALIGN, S2R_ERR_HIP. */
+ * Paths: with workspace == NULL (or ws_bytes == 0) every set bit gathers its d cells from
+ * the sketch directly.  With a workspace of s2r_decode_workspace_bytes(p, n, max_set)
+ * bytes (contents on entry irrelevant) the set bits are grouped by partition and each
+ * partition's cells are read once into LDS; if the bitmap turns out to hold more than
+ * max_set set bits below n, the call still completes correctly through direct gathers
+ * (decided on the device).  Both paths give identical results.
+ * Errors: S2R_ERR_NULL, S2R_ERR_DIM, S2R_ERR_ALIGN, S2R_ERR_WORKSPACE (a non-NULL workspace
+ * smaller than the query), S2R_ERR_HIP. */
 s2r_status s2r_decode(const s2r_params* p, uint64_t n, const uint64_t* bitmap,
-                      const float* sketch, float* out, void* stream);
+                      const float* sketch, float* out, uint64_t max_set, void* workspace,
+                      size_t ws_bytes, void* stream);
 
 /* Test hook: the same device hash the other calls use, on arbitrary keys.
  *   buckets[j * m + t] = h_j(keys[t]),  signs[j * m + t] = s_j(keys[t])  (int8, +1/-1)

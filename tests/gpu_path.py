@@ -86,12 +86,23 @@ def run_reduce(p, n: int, bitmaps: np.ndarray, sketches: np.ndarray, inplace: bo
         else sk[0].cpu().numpy()
 
 
-def run_decode(p, n: int, bitmap: np.ndarray, sketch: np.ndarray) -> np.ndarray:
+def run_decode(p, n: int, bitmap: np.ndarray, sketch: np.ndarray, path: str = "partitioned",
+               max_set: int | None = None) -> np.ndarray:
+    """path: "direct" (no workspace), "partitioned" (workspace for max_set set bits,
+    default n), or "overflow" (workspace far smaller than the set bits: the device must
+    fall back to direct gathers)."""
     bm = torch.from_numpy(np.ascontiguousarray(bitmap).view(np.int64)).to(DEV) if bitmap.size else \
         torch.zeros(1, dtype=torch.int64, device=DEV)
     sk = torch.from_numpy(np.ascontiguousarray(sketch, dtype=np.float32)).to(DEV)
     out = torch.full((max(n, 1),), float("nan"), dtype=torch.float32, device=DEV)
-    s2r.s2r_decode(p, n, bm, sk, out)
+    ws = None
+    if path != "direct":
+        if max_set is None:
+            max_set = n if path == "partitioned" else 1
+        ws = s2r.alloc_decode_workspace(p, n, max_set, DEV)
+        if ws is not None:
+            ws.fill_(0xCD)  # contents on entry must not matter
+    s2r.s2r_decode(p, n, bm, sk, out, max_set=max_set or 0, workspace=ws)
     torch.cuda.synchronize()
     return out.cpu().numpy()[:n]
 

@@ -104,9 +104,16 @@ def test_reduce_decode_hash_argument_errors(s2r):
     assert L.s2r_reduce(pr, 2, 100, FAKE, None, FAKE, FAKE, 0) == s2r.S2R_ERR_NULL
     assert L.s2r_reduce(pr, 0, 100, FAKE, FAKE, FAKE, FAKE, 0) == s2r.S2R_ERR_DIM
     assert L.s2r_reduce(pr, 2, 100, FAKE + 4, FAKE, FAKE, FAKE, 0) == s2r.S2R_ERR_ALIGN
-    assert L.s2r_decode(pr, 100, None, FAKE, FAKE, 0) == s2r.S2R_ERR_NULL
-    assert L.s2r_decode(pr, 2**32, FAKE, FAKE, FAKE, 0) == s2r.S2R_ERR_DIM
-    assert L.s2r_decode(pr, 100, FAKE, FAKE, FAKE + 4, 0) == s2r.S2R_ERR_ALIGN  # out 16-byte
+    assert L.s2r_decode(pr, 100, None, FAKE, FAKE, 0, None, 0, 0) == s2r.S2R_ERR_NULL
+    assert L.s2r_decode(pr, 2**32, FAKE, FAKE, FAKE, 0, None, 0, 0) == s2r.S2R_ERR_DIM
+    assert L.s2r_decode(pr, 100, FAKE, FAKE, FAKE + 4, 0, None, 0, 0) == s2r.S2R_ERR_ALIGN
+    q = s2r.s2r_params_from_seed(3, 3, 14, 13)
+    need = s2r.s2r_decode_workspace_bytes(q, 100_000, 5000)
+    assert need > 0
+    assert L.s2r_decode(ctypes.byref(q), 100_000, FAKE, FAKE, FAKE, 5000, FAKE, need - 1, 0) == \
+        s2r.S2R_ERR_WORKSPACE
+    # no partitioned decode for a table beyond the LDS budget with independent rows
+    assert s2r.s2r_decode_workspace_bytes(s2r.s2r_params_from_seed(3, 5, 20, 20), 1000, 1000) == 0
     assert L.s2r_hash(pr, None, 10, FAKE, FAKE, 0) == s2r.S2R_ERR_NULL
     assert L.s2r_hash(None, FAKE, 10, FAKE, FAKE, 0) == s2r.S2R_ERR_NULL
 

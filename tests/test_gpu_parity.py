@@ -169,32 +169,51 @@ def test_reduce_integer_exact():
 # decode (on a generated bitmap and sketch)
 
 
-@pytest.mark.parametrize("d,L,K,n,density", [(3, 14, 13, 1 << 20, 0.04), (5, 16, 12, 100_003, 0.3),
-                                             (1, 10, 10, 4097, 0.5), (2, 10, 4, 5000, 0.5),
-                                             (4, 12, 12, 65, 1.0), (7, 9, 3, 9000, 0.2),
-                                             (16, 11, 11, 3000, 0.2), (5, 20, 12, 1, 1.0)])
-def test_decode(d, L, K, n, density):
-    gp.say(f"decode d={d} L={L} K={K} n={n}")
+DECODE_CASES = [(3, 14, 13, 1 << 20, 0.04), (5, 16, 12, 100_003, 0.3), (1, 10, 10, 4097, 0.5),
+                (2, 10, 4, 5000, 0.5), (4, 12, 12, 65, 1.0), (7, 9, 3, 9000, 0.2),
+                (16, 11, 11, 3000, 0.2), (5, 20, 12, 1, 1.0), (3, 18, 0, 300_000, 0.6),
+                (5, 22, 12, 200_000, 0.02), (3, 20, 20, 50_000, 0.1)]
+
+
+@pytest.mark.parametrize("path", ["direct", "partitioned", "overflow"])
+@pytest.mark.parametrize("d,L,K,n,density", DECODE_CASES)
+def test_decode(d, L, K, n, density, path):
+    gp.say(f"decode d={d} L={L} K={K} n={n} path={path}")
     p, op = gp.params_pair(55 + d, d, L, K)
     sketch = WL.random_sketch((d, 1 << L), 7 * d)
     bm = WL.random_bitmap(n, density, 9 * d)
     # set bits beyond n in the input: they must be ignored
     if n % 64:
         bm[-1] |= np.uint64(~((1 << (n % 64)) - 1) & 0xFFFFFFFFFFFFFFFF)
-    out = gp.run_decode(p, n, bm, sketch)
+    out = gp.run_decode(p, n, bm, sketch, path=path)
     want, tol = oracle.decode_dense(op, n, bm, sketch.astype(np.float64))
     setmask = gp.bits_of(bm, n)
     # odd d: the median selects one of the fp32 inputs, so the result is exact
     gp.assert_decode_matches(out, want, tol, setmask, exact=(d % 2 == 1))
 
 
-def test_decode_empty_bitmap():
-    gp.say("decode empty")
+@pytest.mark.parametrize("path", ["direct", "partitioned"])
+def test_decode_empty_bitmap(path):
+    gp.say(f"decode empty {path}")
     p, op = gp.params_pair(1, 3, 12)
     n = 10_000
-    out = gp.run_decode(p, n, np.zeros(WL.workload(0).N // 64, np.uint64)[: (n + 63) // 64],
-                        WL.random_sketch((3, 1 << 12), 2))
+    out = gp.run_decode(p, n, np.zeros((n + 63) // 64, np.uint64), WL.random_sketch((3, 1 << 12), 2),
+                        path=path)
     assert np.all(out.view(np.uint32) == 0)
+
+
+def test_decode_capacity_boundary():
+    """max_set exactly U, and U + 1, and U - 1 (the last falls back on the device)."""
+    d, L, n = 5, 16, 200_000
+    p, op = gp.params_pair(8, d, L)
+    sketch = WL.random_sketch((d, 1 << L), 3)
+    bm = WL.random_bitmap(n, 0.25, 4)
+    U = int(gp.bits_of(bm, n).sum())
+    want, tol = oracle.decode_dense(op, n, bm, sketch.astype(np.float64))
+    for ms in (U - 1, U, U + 1, 8192, 8193):
+        gp.say(f"decode capacity U={U} max_set={ms}")
+        out = gp.run_decode(p, n, bm, sketch, path="partitioned", max_set=ms)
+        gp.assert_decode_matches(out, want, tol, gp.bits_of(bm, n), exact=True)
 
 
 # ---------------------------------------------------------------------------------------
