@@ -60,13 +60,11 @@ EncodeLayout encode_layout(const s2r_params& p, uint32_t W, uint64_t n, uint64_t
   off = align256(off + (size_t)W * L.tiles * 4);
   L.off_offsets = off;
   off = align256(off + (size_t)W * (L.tiles + 1) * 4);
-  L.off_bidx = L.off_bval = L.off_prefix = off;
+  L.off_bins = L.off_prefix = off;
   if (L.partitioned) {
     const size_t slots = (size_t)W * L.chunks * kChunk;
-    L.off_bidx = off;
-    off = align256(off + slots * 4);
-    L.off_bval = off;
-    off = align256(off + slots * 4);
+    L.off_bins = off;
+    off = align256(off + slots * 8);
     L.off_prefix = off;
     off = align256(off + (size_t)W * (L.partitions + 1) * L.chunks * 4);
   }
@@ -151,13 +149,12 @@ s2r_status s2r_encode(const s2r_params* p, uint32_t W, const float* grad, uint64
   S2R_TRY(launch_scan(W, L.tiles, counts, offsets, nnz, nullptr, 0, cap, s));
   S2R_TRY(launch_expand(W, grad, ld, L.tiles, bitmaps, words, offsets, idx, val, cap, s));
   if (L.partitioned) {
-    uint32_t* bidx = reinterpret_cast<uint32_t*>(ws + L.off_bidx);
-    float* bval = reinterpret_cast<float*>(ws + L.off_bval);
+    uint2* bins = reinterpret_cast<uint2*>(ws + L.off_bins);
     uint32_t* prefix = reinterpret_cast<uint32_t*>(ws + L.off_prefix);
-    S2R_TRY(launch_bin(h, W, L.tiles, offsets, idx, val, cap, L.chunks, L.partitions, bidx, bval,
-                       prefix, s));
-    S2R_TRY(launch_accumulate(h, W, L.tiles, offsets, cap, L.chunks, L.partitions, bidx, bval,
-                              prefix, sketches, w, s));
+    S2R_TRY(launch_bin(h, W, L.tiles, offsets, idx, val, cap, L.chunks, L.partitions, bins, prefix,
+                       s));
+    S2R_TRY(launch_accumulate(h, W, L.tiles, offsets, cap, L.chunks, L.partitions, bins, prefix,
+                              sketches, w, s));
   } else {
     S2R_TRY(launch_scatter(h, W, L.tiles, offsets, idx, val, cap, L.chunks, sketches, w, s));
   }

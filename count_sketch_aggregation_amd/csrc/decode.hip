@@ -80,7 +80,12 @@ __global__ __launch_bounds__(kDBinThreads) void k_dbin(HashArgs h, uint64_t n,
                                                        DecodeWs ws, uint32_t P) {
   extern __shared__ uint32_t hist[];  // P + 1
   __shared__ uint32_t litem[kChunk];  // indices in rank order
-  __shared__ uint32_t sitem[kChunk];  // indices in partition order
+  // phase 1: one round of bitmap words and their rank offsets; phase 2: indices in
+  // partition order
+  __shared__ __align__(16) uint8_t scratch[kChunk * sizeof(uint32_t)];
+  uint64_t* lw = reinterpret_cast<uint64_t*>(scratch);
+  uint32_t* lwo = reinterpret_cast<uint32_t*>(scratch + kDBinBatchWords * sizeof(uint64_t));
+  uint32_t* sitem = reinterpret_cast<uint32_t*>(scratch);
   __shared__ uint32_t wtot[kDBinThreads / kWave];
   const uint32_t c = blockIdx.x;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -91,7 +96,8 @@ __global__ __launch_bounds__(kDBinThreads) void k_dbin(HashArgs h, uint64_t n,
   const uint32_t cnt = (uint32_t)(U - start < kChunk ? U - start : kChunk);
   const uint64_t end = start + cnt;
 
-  // 1. expand ranks [start, end) into litem, 2048 bitmap words per round
+  // 1. expand ranks [start, end) into litem, 2048 bitmap words per round: each rank finds
+  //    its word by binary search over the round's word offsets and its bit by select_bit
   const uint32_t t0 = ws.chunk_tile[c];
   uint64_t q0 = (uint64_t)t0 * kDecWords;
   uint64_t rank0 = ws.toff[t0];
@@ -111,26 +117,24 @@ __global__ __launch_bounds__(kDBinThreads) void k_dbin(HashArgs h, uint64_t n,
       if (v < wave) before += wtot[v];
       batch_total += wtot[v];
     }
-    uint64_t r = rank0 + before;
 #pragma unroll
     for (int u = 0; u < kDBinWordsPerThread; ++u) {
-      uint64_t bits = wv[u];
-      const uint64_t pc = (uint64_t)__popcll(bits);
-      if (r + pc > start && r < end) {
-        const uint32_t ibase = (uint32_t)((q0 + (uint64_t)tid * kDBinWordsPerThread + u) * 64);
-        uint64_t rr = r;
-        while (bits) {
-          const int b = __builtin_ctzll(bits);
-          bits &= bits - 1;
-          if (rr >= start && rr < end) litem[rr - start] = ibase + b;
-          ++rr;
-        }
-      }
-      r += pc;
+      lw[tid * kDBinWordsPerThread + u] = wv[u];
+      lwo[tid * kDBinWordsPerThread + u] = before;
+      before += (uint32_t)__popcll(wv[u]);
+    }
+    __syncthreads();
+    const uint64_t lo_r = rank0 > start ? rank0 : start;
+    const uint64_t hi_r = rank0 + batch_total < end ? rank0 + batch_total : end;
+    for (uint64_t r = lo_r + tid; r < hi_r; r += kDBinThreads) {
+      const uint32_t e = (uint32_t)(r - rank0);
+      const uint32_t q = segment_of(lwo, kDBinBatchWords, e);
+      const uint32_t b = select_bit(lw[q], e - lwo[q]);
+      litem[r - start] = (uint32_t)((q0 + q) * 64) + b;
     }
     rank0 += batch_total;
     q0 += kDBinBatchWords;
-    __syncthreads();  // wtot is reused next round
+    __syncthreads();  // lw, lwo and wtot are reused next round
   }
   for (uint32_t p = tid; p <= P; p += kDBinThreads) hist[p] = 0;
   __syncthreads();
@@ -193,7 +197,7 @@ __global__ __launch_bounds__(kAccThreads) void k_dmedian(HashArgs h, uint64_t ti
                                                          const float* __restrict__ sketch,
                                                          uint64_t w, DecodeWs ws, uint32_t P,
                                                          int vec4) {
-  extern __shared__ float tile[];  // D * 2^K
+  extern __shared__ __align__(16) float tile[];  // D * 2^K
   __shared__ uint32_t seg_src[kSegBatch];
   __shared__ uint32_t seg_off[kSegBatch + 1];
   __shared__ uint32_t wtot[kAccThreads / kWave];
@@ -248,21 +252,22 @@ __global__ __launch_bounds__(kAccThreads) void k_dmedian(HashArgs h, uint64_t ti
     if (tid == kAccThreads - 1 && nb == (uint32_t)kSegBatch) seg_off[kSegBatch] = run;
     __syncthreads();
     const uint32_t E = seg_off[nb];
-    for (uint32_t e0 = 0; e0 < E; e0 += 4 * kAccThreads) {
-      uint32_t ii[4];
-      uint64_t at[4];
+    for (uint32_t e0 = tid * kAccEntries; e0 < E; e0 += kAccThreads * kAccEntries) {
+      uint32_t c = segment_of(seg_off, nb, e0);
+      uint32_t ii[kAccEntries];
+      uint64_t at[kAccEntries];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const uint32_t e = e0 + u * kAccThreads + tid;
+      for (int u = 0; u < kAccEntries; ++u) {
+        const uint32_t e = e0 + u;
         if (e < E) {
-          const uint32_t c = segment_of(seg_off, nb, e);
+          while (seg_off[c + 1] <= e) ++c;
           at[u] = (uint64_t)seg_src[c] + (e - seg_off[c]);
           ii[u] = ws.bidx[at[u]];
         }
       }
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        if (e0 + u * kAccThreads + tid < E) {
+      for (int u = 0; u < kAccEntries; ++u) {
+        if (e0 + u < E) {
           float v[D];
 #pragma unroll
           for (int j = 0; j < D; ++j)
@@ -284,8 +289,9 @@ __global__ __launch_bounds__(kDecThreads) void k_dwrite(HashArgs h, uint64_t n, 
                                                         uint64_t w, float* __restrict__ out,
                                                         DecodeWs ws, uint64_t tiles,
                                                         int partitioned) {
-  __shared__ float otile[kDecTile];
-  __shared__ uint16_t items[kDecTile];
+  __shared__ __align__(16) float otile[kDecTile];
+  __shared__ uint64_t lw[kDecWords];
+  __shared__ uint32_t lwo[kDecWords];
   __shared__ uint32_t wtot[2];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const uint64_t base = (uint64_t)blockIdx.x * kDecTile;
@@ -295,15 +301,9 @@ __global__ __launch_bounds__(kDecThreads) void k_dwrite(HashArgs h, uint64_t n, 
   const uint32_t pc = (uint32_t)__popcll(wv);
   const uint32_t inc = wave_inclusive_sum(pc);
   if (tid < kDecWords && lane == kWave - 1) wtot[wave] = inc;
+  if (tid < kDecWords) lw[tid] = wv;
   __syncthreads();
-  if (tid < kDecWords) {
-    uint32_t slot_i = inc - pc + (wave ? wtot[0] : 0u);
-    while (wv) {
-      const int b = __builtin_ctzll(wv);
-      wv &= wv - 1;
-      items[slot_i++] = (uint16_t)(tid * 64 + b);
-    }
-  }
+  if (tid < kDecWords) lwo[tid] = inc - pc + (wave ? wtot[0] : 0u);
   __syncthreads();
   const uint32_t cnt = wtot[0] + wtot[1];
   bool direct = !partitioned;
@@ -312,22 +312,51 @@ __global__ __launch_bounds__(kDecThreads) void k_dwrite(HashArgs h, uint64_t n, 
     direct = ws.toff[tiles] > ws.max_set;
     rank0 = ws.toff[blockIdx.x];
   }
+  constexpr int UN = 4;  // items per thread in flight
   if (direct) {
-    for (uint32_t e = tid; e < cnt; e += kDecThreads) {
-      const uint32_t li = items[e];
-      const uint32_t i = (uint32_t)(base + li);
-      const uint32_t part = partition_of(h, i);
-      float v[D];
+    for (uint32_t e0 = tid; e0 < cnt; e0 += UN * kDecThreads) {
+      uint32_t li[UN];
+      float v[UN][D];
 #pragma unroll
-      for (int j = 0; j < D; ++j)
-        v[j] = apply_sign(sketch[(uint64_t)j * w + bucket_of(h, part, j, i)], sign_mask(h, j, i));
-      otile[li] = median_of<D>(v);
+      for (int u = 0; u < UN; ++u) {
+        const uint32_t e = e0 + u * kDecThreads;
+        if (e < cnt) {
+          const uint32_t q = segment_of(lwo, kDecWords, e);
+          li[u] = q * 64 + select_bit(lw[q], e - lwo[q]);
+          const uint32_t i = (uint32_t)(base + li[u]);
+          const uint32_t part = partition_of(h, i);
+#pragma unroll
+          for (int j = 0; j < D; ++j)
+            v[u][j] = apply_sign(sketch[(uint64_t)j * w + bucket_of(h, part, j, i)],
+                                 sign_mask(h, j, i));
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < UN; ++u)
+        if (e0 + u * kDecThreads < cnt) otile[li[u]] = median_of<D>(v[u]);
     }
   } else {
-    for (uint32_t e = tid; e < cnt; e += kDecThreads) {
-      const uint64_t r = rank0 + e;
-      const uint64_t chunk_base = r / kChunk * kChunk;
-      otile[items[e]] = ws.gval[chunk_base + ws.slot[r]];
+    for (uint32_t e0 = tid; e0 < cnt; e0 += UN * kDecThreads) {
+      uint32_t li[UN];
+      uint16_t sl[UN];
+#pragma unroll
+      for (int u = 0; u < UN; ++u) {
+        const uint32_t e = e0 + u * kDecThreads;
+        if (e < cnt) {
+          const uint32_t q = segment_of(lwo, kDecWords, e);
+          li[u] = q * 64 + select_bit(lw[q], e - lwo[q]);
+          sl[u] = ws.slot[rank0 + e];
+        }
+      }
+      float g[UN];
+#pragma unroll
+      for (int u = 0; u < UN; ++u) {
+        const uint64_t r = rank0 + e0 + u * kDecThreads;
+        if (e0 + u * kDecThreads < cnt) g[u] = ws.gval[r / kChunk * kChunk + sl[u]];
+      }
+#pragma unroll
+      for (int u = 0; u < UN; ++u)
+        if (e0 + u * kDecThreads < cnt) otile[li[u]] = g[u];
     }
   }
   __syncthreads();

@@ -88,56 +88,64 @@ __global__ __launch_bounds__(kStreamThreads) void k_stream(
 }
 
 // ---------------------------------------------------------------------------------------
-// k_scan: grid W, 1024 threads.  Thread t owns a contiguous run of tiles.
+// k_scan: grid W, 1024 threads.  Passes of 16 counts per thread: all 16 loads are issued
+// at once and kept in registers for the offsets, so a pass costs about one load latency.
+// Also records, for every chunk of kChunk consecutive list positions below `limit`, the
+// tile holding its first position.
 __global__ __launch_bounds__(kScanThreads) void k_scan(
     uint64_t tiles, const uint32_t* __restrict__ counts, uint32_t* __restrict__ offsets,
     uint64_t* __restrict__ nnz, uint32_t* __restrict__ chunk_tile, uint64_t chunks,
-    uint64_t cap) {
+    uint64_t limit) {
+  constexpr int PER = 16;
   const uint32_t k = blockIdx.x;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const uint32_t* cnt = counts + (uint64_t)k * tiles;
   uint32_t* off = offsets + (uint64_t)k * (tiles + 1);
   uint32_t* ct = chunk_tile + (uint64_t)k * chunks;
-
-  const uint64_t per = (tiles + kScanThreads - 1) / kScanThreads;
-  const uint64_t lo = (uint64_t)tid * per;
-  const uint64_t hi = lo + per < tiles ? lo + per : tiles;
-  uint32_t sum = 0;
-#pragma unroll 8
-  for (uint64_t t = lo; t < hi; ++t) sum += cnt[t];
-
   __shared__ uint32_t wsum[kScanThreads / kWave];
-  const uint32_t inc = wave_inclusive_sum(sum);
-  if (lane == kWave - 1) wsum[wave] = inc;
-  __syncthreads();
-  if (wave == 0) {
-    const uint32_t x = lane < kScanThreads / kWave ? wsum[lane] : 0u;
-    const uint32_t xi = wave_inclusive_sum(x);
-    if (lane < kScanThreads / kWave) wsum[lane] = xi - x;
+  uint32_t carry = 0;
+  for (uint64_t base = 0; base < tiles; base += (uint64_t)kScanThreads * PER) {
+    const uint64_t t0 = base + (uint64_t)tid * PER;
+    uint32_t v[PER], sum = 0;
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      v[u] = t0 + u < tiles ? cnt[t0 + u] : 0u;
+      sum += v[u];
+    }
+    const uint32_t inc = wave_inclusive_sum(sum);
+    if (lane == kWave - 1) wsum[wave] = inc;
+    __syncthreads();
+    uint32_t run = carry + inc - sum, pass_total = 0;
+    for (int w = 0; w < kScanThreads / kWave; ++w) {
+      if (w < wave) run += wsum[w];
+      pass_total += wsum[w];
+    }
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      if (t0 + u < tiles) {
+        off[t0 + u] = run;
+        // chunks whose first position falls inside this tile start here
+        for (uint64_t c0 = ((uint64_t)run + kChunk - 1) / kChunk;
+             c0 < chunks && c0 * kChunk < (uint64_t)run + v[u] && c0 * kChunk < limit; ++c0)
+          ct[c0] = (uint32_t)(t0 + u);
+      }
+      run += v[u];
+    }
+    carry += pass_total;
+    __syncthreads();  // wsum is rewritten next pass
   }
-  __syncthreads();
-  uint32_t run = wsum[wave] + inc - sum;
-  const uint64_t limit = cap;  // list positions that get a chunk: [0, min(nnz, cap))
-  for (uint64_t t = lo; t < hi; ++t) {
-    const uint32_t c_t = cnt[t];
-    off[t] = run;
-    // chunks whose first position falls inside this tile start here
-    uint64_t c0 = ((uint64_t)run + kChunk - 1) / kChunk;
-    for (; c0 < chunks && c0 * kChunk < (uint64_t)run + c_t && c0 * kChunk < limit; ++c0)
-      ct[c0] = (uint32_t)t;
-    run += c_t;
-  }
-  if (tid == kScanThreads - 1) {
-    off[tiles] = run;
-    nnz[k] = run;
+  if (tid == 0) {
+    off[tiles] = carry;
+    nnz[k] = carry;
   }
 }
 
 // ---------------------------------------------------------------------------------------
 // k_expand: grid (tiles, W), 256 threads.  Lists the tile's non-zeros at list positions
 // offsets[t] + (rank within the tile): the 128 bitmap words and their popcount prefix go to
-// LDS, then each thread takes 8 groups of four elements and, for the groups holding a set
-// bit, re-reads only that 16-byte group of the gradient (all 8 loads issued before use).
+// LDS, each thread takes 8 groups of four elements and, for the groups holding a set bit,
+// re-reads only that 16-byte group of the gradient (all 8 loads issued before use) and
+// stores its pairs straight to their list positions (a tile's positions are contiguous).
 __global__ __launch_bounds__(kExpandThreads) void k_expand(
     const float* __restrict__ grad, uint64_t ld, uint64_t tiles,
     const uint64_t* __restrict__ bitmaps, uint64_t words, const uint32_t* __restrict__ offsets,
@@ -248,16 +256,15 @@ __device__ __forceinline__ void block_exclusive_scan(uint32_t* hist, uint32_t P,
 // k_bin (partitioned path): grid (chunks, W), 512 threads.  Counting-sorts the chunk's list
 // entries by partition P(i) (u32 LDS atomics give each entry its slot), assembles the sorted
 // chunk in LDS and writes it out with coalesced 128-bit stores:
-//   bidx/bval[k][c * kChunk + X[p] ...]   the chunk's pairs grouped by partition
+//   bins[k][c * kChunk + X[p] ...]        the chunk's (index, value bits) pairs grouped by
+//                                         partition, interleaved so a segment is one run
 //   prefix[k][p][c] = X[p], p = 0..P       the start of partition p inside chunk c
 __global__ __launch_bounds__(kBinThreads) void k_bin(
     HashArgs h, uint64_t tiles, const uint32_t* __restrict__ offsets,
     const uint32_t* __restrict__ idx, const float* __restrict__ val, uint64_t cap,
-    uint64_t chunks, uint32_t P, uint32_t* __restrict__ bidx, float* __restrict__ bval,
-    uint32_t* __restrict__ prefix) {
+    uint64_t chunks, uint32_t P, uint2* __restrict__ bins, uint32_t* __restrict__ prefix) {
   extern __shared__ uint32_t hist[];  // P + 1 counters
-  __shared__ uint32_t sidx[kChunk];
-  __shared__ float sval[kChunk];
+  __shared__ __align__(16) uint2 spair[kChunk];
   __shared__ uint32_t wtot[kBinThreads / kWave];
   const uint32_t c = blockIdx.x, k = blockIdx.y;
   const int tid = threadIdx.x;
@@ -299,32 +306,15 @@ __global__ __launch_bounds__(kBinThreads) void k_bin(
     const uint32_t s = tid + kBinThreads * r;
     if (s < cnt) {
       const uint32_t pos = hist[pp[r]] + rk[r];
-      sidx[pos] = ii[r];
-      sval[pos] = gg[r];
+      spair[pos] = make_uint2(ii[r], __float_as_uint(gg[r]));
     }
   }
   __syncthreads();
-  const uint64_t bbase = ((uint64_t)k * chunks + c) * kChunk;  // 16-byte aligned
-  const uint32_t cnt4 = cnt / 4;
-  for (uint32_t q = tid; q < cnt4; q += kBinThreads) {
-    *reinterpret_cast<uint4*>(bidx + bbase + 4 * q) = *reinterpret_cast<const uint4*>(&sidx[4 * q]);
-    *reinterpret_cast<f32x4*>(bval + bbase + 4 * q) = *reinterpret_cast<const f32x4*>(&sval[4 * q]);
-  }
-  for (uint32_t s = 4 * cnt4 + tid; s < cnt; s += kBinThreads) {
-    bidx[bbase + s] = sidx[s];
-    bval[bbase + s] = sval[s];
-  }
-}
-
-// fp32 add into LDS through a 32-bit compare-and-swap loop.  On gfx950 this sustains about
-// 9x the rate of ds_add_f32 for scattered addresses, and the sum is the same fp32 addition.
-__device__ __forceinline__ void lds_add_f32(float* p, float v) {
-  uint32_t* w = reinterpret_cast<uint32_t*>(p);
-  uint32_t old = *w, assumed;
-  do {
-    assumed = old;
-    old = atomicCAS(w, assumed, __float_as_uint(__uint_as_float(assumed) + v));
-  } while (old != assumed);
+  uint2* out = bins + ((uint64_t)k * chunks + c) * kChunk;  // 16-byte aligned
+  const uint32_t cnt2 = cnt / 2;
+  for (uint32_t q = tid; q < cnt2; q += kBinThreads)
+    *reinterpret_cast<uint4*>(out + 2 * q) = *reinterpret_cast<const uint4*>(&spair[2 * q]);
+  if ((cnt & 1u) && tid == 0) out[cnt - 1] = spair[cnt - 1];
 }
 
 // k_accumulate (partitioned path): grid (P, W), 512 threads.  The partition's d x 2^K
@@ -334,10 +324,9 @@ __device__ __forceinline__ void lds_add_f32(float* p, float v) {
 template <int D>
 __global__ __launch_bounds__(kAccThreads) void k_accumulate(
     HashArgs h, uint64_t tiles, const uint32_t* __restrict__ offsets, uint64_t cap,
-    uint64_t chunks, uint32_t partitions, const uint32_t* __restrict__ bidx,
-    const float* __restrict__ bval, const uint32_t* __restrict__ prefix,
-    float* __restrict__ sketches, uint64_t w, int vec4) {
-  extern __shared__ float tile[];  // D * 2^K
+    uint64_t chunks, uint32_t partitions, const uint2* __restrict__ bins,
+    const uint32_t* __restrict__ prefix, float* __restrict__ sketches, uint64_t w, int vec4) {
+  extern __shared__ __align__(16) float tile[];  // D * 2^K
   __shared__ uint32_t seg_src[kSegBatch];
   __shared__ uint32_t seg_off[kSegBatch + 1];
   __shared__ uint32_t wtot[kAccThreads / kWave];
@@ -382,28 +371,36 @@ __global__ __launch_bounds__(kAccThreads) void k_accumulate(
     if (tid == kAccThreads - 1 && nb == (uint32_t)kSegBatch) seg_off[kSegBatch] = run;
     __syncthreads();
     const uint32_t E = seg_off[nb];
-    for (uint32_t e0 = 0; e0 < E; e0 += 4 * kAccThreads) {
-      uint32_t ii[4];
-      float gg[4];
+    for (uint32_t e0 = tid * kAccEntries; e0 < E; e0 += kAccThreads * kAccEntries) {
+      // four consecutive entries: one search, then walk forward across segment ends
+      uint32_t c = segment_of(seg_off, nb, e0);
+      uint32_t ii[kAccEntries];
+      float gg[kAccEntries];
+      bool on[kAccEntries];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const uint32_t e = e0 + u * kAccThreads + tid;
-        if (e < E) {
-          const uint32_t c = segment_of(seg_off, nb, e);
-          const uint64_t pos = kbase + seg_src[c] + (e - seg_off[c]);
-          ii[u] = bidx[pos];
-          gg[u] = bval[pos];
+      for (int u = 0; u < kAccEntries; ++u) {
+        const uint32_t e = e0 + u;
+        on[u] = e < E;
+        if (on[u]) {
+          while (seg_off[c + 1] <= e) ++c;
+          const uint2 pr = bins[kbase + seg_src[c] + (e - seg_off[c])];
+          ii[u] = pr.x;
+          gg[u] = __uint_as_float(pr.y);
         }
       }
+      uint32_t cell[kAccEntries * D];
+      float add[kAccEntries * D];
+      bool live[kAccEntries * D];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        if (e0 + u * kAccThreads + tid < E) {
+      for (int u = 0; u < kAccEntries; ++u) {
 #pragma unroll
-          for (int j = 0; j < D; ++j)
-            lds_add_f32(&tile[j * pw + row_bucket(h, j, ii[u])],
-                        apply_sign(gg[u], sign_mask(h, j, ii[u])));
+        for (int j = 0; j < D; ++j) {
+          live[u * D + j] = on[u];
+          cell[u * D + j] = j * pw + (on[u] ? row_bucket(h, j, ii[u]) : 0u);
+          add[u * D + j] = on[u] ? apply_sign(gg[u], sign_mask(h, j, ii[u])) : 0.f;
         }
       }
+      lds_add_f32_many<kAccEntries * D>(tile, cell, add, live);
     }
   }
   __syncthreads();
@@ -479,23 +476,21 @@ hipError_t launch_scatter(const HashArgs& h, uint32_t W, uint64_t tiles, const u
 
 hipError_t launch_bin(const HashArgs& h, uint32_t W, uint64_t tiles, const uint32_t* offsets,
                       const uint32_t* idx, const float* val, uint64_t cap, uint64_t chunks,
-                      uint64_t partitions, uint32_t* bidx, float* bval, uint32_t* prefix,
-                      hipStream_t s) {
+                      uint64_t partitions, uint2* bins, uint32_t* prefix, hipStream_t s) {
   if (chunks == 0) return hipSuccess;
   const size_t lds = (partitions + 1) * sizeof(uint32_t);
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_bin),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(k_bin, dim3((uint32_t)chunks, W), dim3(kBinThreads), lds, s, h, tiles,
-                     offsets, idx, val, cap, chunks, (uint32_t)partitions, bidx, bval, prefix);
+                     offsets, idx, val, cap, chunks, (uint32_t)partitions, bins, prefix);
   return hipGetLastError();
 }
 
 hipError_t launch_accumulate(const HashArgs& h, uint32_t W, uint64_t tiles,
                              const uint32_t* offsets, uint64_t cap, uint64_t chunks,
-                             uint64_t partitions, const uint32_t* bidx, const float* bval,
-                             const uint32_t* prefix, float* sketches, uint64_t w,
-                             hipStream_t s) {
+                             uint64_t partitions, const uint2* bins, const uint32_t* prefix,
+                             float* sketches, uint64_t w, hipStream_t s) {
   const size_t lds = ((size_t)h.d << h.K) * sizeof(float);
   const int vec4 = (h.K >= 2 && (reinterpret_cast<uintptr_t>(sketches) % 16) == 0) ? 1 : 0;
   hipError_t e = hipSuccess;
@@ -504,8 +499,8 @@ hipError_t launch_accumulate(const HashArgs& h, uint32_t W, uint64_t tiles,
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e == hipSuccess)
       hipLaunchKernelGGL((k_accumulate<D>), dim3((uint32_t)partitions, W), dim3(kAccThreads), lds,
-                         s, h, tiles, offsets, cap, chunks, (uint32_t)partitions, bidx, bval,
-                         prefix, sketches, w, vec4);
+                         s, h, tiles, offsets, cap, chunks, (uint32_t)partitions, bins, prefix,
+                         sketches, w, vec4);
   });
   if (e != hipSuccess) return e;
   return hipGetLastError();

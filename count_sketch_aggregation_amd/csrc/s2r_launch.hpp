@@ -20,9 +20,10 @@ constexpr int kScatterThreads = 256;
 constexpr int kChunk = 8192;                        // list entries per chunk
 constexpr int kBinThreads = 512;                    // 16 entries per thread
 constexpr int kMaxPartitions = 8192;                // LDS histogram limit of the binning pass
-constexpr int kAccThreads = 1024;
-constexpr int kSegBatch = 1024;                     // chunk segments flattened per round
-constexpr size_t kAccLdsBytes = 128 * 1024;         // LDS of one partition tile
+constexpr int kAccThreads = 512;
+constexpr int kAccEntries = 1;                    // consecutive entries per thread and round
+constexpr int kSegBatch = 1024;                     // chunk segments flattened per batch
+constexpr size_t kAccLdsBytes = 64 * 1024;          // LDS of one partition tile
 
 constexpr int kScanThreads = 1024;
 
@@ -32,7 +33,7 @@ struct EncodeLayout {
   uint64_t chunks;       // list chunks per worker (bounded by min(cap, n))
   uint64_t partitions;   // 2^(L-K) on the partitioned path, 0 otherwise
   bool partitioned;
-  size_t off_counts, off_offsets, off_bidx, off_bval, off_prefix, total;
+  size_t off_counts, off_offsets, off_bins, off_prefix, total;
 };
 EncodeLayout encode_layout(const s2r_params& p, uint32_t W, uint64_t n, uint64_t cap);
 bool use_partitioned(const s2r_params& p);
@@ -53,12 +54,11 @@ hipError_t launch_scatter(const HashArgs& h, uint32_t W, uint64_t tiles, const u
                           float* sketches, uint64_t w, hipStream_t s);
 hipError_t launch_bin(const HashArgs& h, uint32_t W, uint64_t tiles, const uint32_t* offsets,
                       const uint32_t* idx, const float* val, uint64_t cap, uint64_t chunks,
-                      uint64_t partitions, uint32_t* bidx, float* bval, uint32_t* prefix,
-                      hipStream_t s);
+                      uint64_t partitions, uint2* bins, uint32_t* prefix, hipStream_t s);
 hipError_t launch_accumulate(const HashArgs& h, uint32_t W, uint64_t tiles,
                              const uint32_t* offsets, uint64_t cap, uint64_t chunks,
-                             uint64_t partitions, const uint32_t* bidx, const float* bval,
-                             const uint32_t* prefix, float* sketches, uint64_t w, hipStream_t s);
+                             uint64_t partitions, const uint2* bins, const uint32_t* prefix,
+                             float* sketches, uint64_t w, hipStream_t s);
 
 hipError_t launch_reduce(uint32_t W, uint64_t cells, uint64_t words, const uint64_t* bitmaps,
                          const float* sketches, uint64_t* bitmap_out, float* sketch_out,

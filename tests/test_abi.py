@@ -52,11 +52,12 @@ def test_params_range_checks(s2r):
 
 def test_small_helpers(s2r):
     assert [s2r.s2r_bitmap_words(n) for n in (0, 1, 64, 65, 2**32 - 1)] == [0, 1, 1, 2, 2**26]
-    # partition tile = d x 2^K fp32 must fit 128 KiB of LDS
-    assert s2r.s2r_default_log2_part(5, 23) == 12
-    assert s2r.s2r_default_log2_part(3, 19) == 13
+    # partition tile = d x 2^K fp32 must fit 64 KiB of LDS
+    assert s2r.s2r_default_log2_part(5, 23) == 11
+    assert s2r.s2r_default_log2_part(3, 19) == 12
     assert s2r.s2r_default_log2_part(1, 10) == 10
-    assert s2r.s2r_default_log2_part(16, 31) == 11
+    assert s2r.s2r_default_log2_part(1, 20) == 14
+    assert s2r.s2r_default_log2_part(16, 31) == 10
     p = s2r.s2r_params_from_seed(1, 3, 14, 13)
     assert s2r.s2r_encode_workspace_bytes(p, 4, 1 << 20, 1 << 20) > 0
     assert s2r.s2r_encode_workspace_bytes(p, 0, 1 << 20, 1 << 20) == 0
@@ -107,7 +108,7 @@ def test_reduce_decode_hash_argument_errors(s2r):
     assert L.s2r_decode(pr, 100, None, FAKE, FAKE, 0, None, 0, 0) == s2r.S2R_ERR_NULL
     assert L.s2r_decode(pr, 2**32, FAKE, FAKE, FAKE, 0, None, 0, 0) == s2r.S2R_ERR_DIM
     assert L.s2r_decode(pr, 100, FAKE, FAKE, FAKE + 4, 0, None, 0, 0) == s2r.S2R_ERR_ALIGN
-    q = s2r.s2r_params_from_seed(3, 3, 14, 13)
+    q = s2r.s2r_params_from_seed(3, 3, 14, 12)
     need = s2r.s2r_decode_workspace_bytes(q, 100_000, 5000)
     assert need > 0
     assert L.s2r_decode(ctypes.byref(q), 100_000, FAKE, FAKE, FAKE, 5000, FAKE, need - 1, 0) == \
