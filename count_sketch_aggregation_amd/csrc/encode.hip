@@ -7,7 +7,7 @@
 // Pipeline on gfx950 (all W workers batched in every launch):
 //   k_stream      streams the gradient once with 128-bit loads, packs the non-zero tests
 //                 into element-ordered bitmap words through LDS; writes the bitmap and one
-//                 non-zero count per 8192-element tile.
+//                 non-zero count per 4096-element tile.
 //   k_scan        per worker: exclusive prefix of the tile counts (list offsets) and nnz.
 //   k_expand      per tile: expands the bitmap words into ascending (index, value) pairs at
 //                 their list offsets, re-reading only the 16-byte gradient groups that hold
@@ -27,9 +27,10 @@ namespace s2r {
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 // ---------------------------------------------------------------------------------------
-// k_stream: grid (tiles, W), 256 threads.  Wave w of a tile owns 2048 consecutive elements
-// (8 load rounds of 256): lane l of round r holds elements base + 256 r + 4 l .. +3 in one
-// 128-bit load.  Each lane folds its four non-zero tests into a nibble with vector ops
+// k_stream: grid (tiles, W), 512 threads.  Wave w of a 4096-element tile owns 512
+// consecutive elements (2 load rounds of 256): lane l of round r holds elements
+// base + 256 r + 4 l .. +3 in one 128-bit load.  (Measured on MI355X: 2 loads per lane on
+// 2048-4096-element tiles streamed at 6.3 TB/s, 8 loads on 8192 at 5.9 TB/s.)  Each lane folds its four non-zero tests into a nibble with vector ops
 // (min(bits << 1, 1) is 1 exactly when the magnitude bits are not all zero), a DPP swap
 // pairs adjacent lanes' nibbles into one byte, and the even lanes drop the bytes into LDS
 // in element order, so the tile's 128 bitmap words assemble in LDS with no scalar-unit work
@@ -73,8 +74,8 @@ __global__ __launch_bounds__(kStreamThreads) void k_stream(
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const float* row = grad + (uint64_t)k * ld;
   const uint64_t tile_base = (uint64_t)t * kTile;
-  const uint64_t wave_base = tile_base + (uint64_t)wave * (kTile / 4);
-  uint8_t* lbytes = reinterpret_cast<uint8_t*>(lwords) + wave * (kTile / 4 / 8);
+  const uint64_t wave_base = tile_base + (uint64_t)wave * kStreamWaveSpan;
+  uint8_t* lbytes = reinterpret_cast<uint8_t*>(lwords) + wave * (kStreamWaveSpan / 8);
   uint32_t c = (tile_base + kTile <= n) ? stream_tile<false>(row, wave_base, n, lbytes, lane)
                                         : stream_tile<true>(row, wave_base, n, lbytes, lane);
   c = wave_sum(c);
@@ -84,32 +85,47 @@ __global__ __launch_bounds__(kStreamThreads) void k_stream(
     const uint64_t gw = (uint64_t)t * kTileWords + tid;
     if (gw < words) bitmaps[(uint64_t)k * words + gw] = lwords[tid];
   }
-  if (tid == 0) counts[(uint64_t)k * tiles + t] = wcount[0] + wcount[1] + wcount[2] + wcount[3];
+  if (tid == 0) {
+    uint32_t sum = 0;
+#pragma unroll
+    for (int v = 0; v < kStreamThreads / kWave; ++v) sum += wcount[v];
+    counts[(uint64_t)k * tiles + t] = sum;
+  }
 }
 
 // ---------------------------------------------------------------------------------------
-// k_scan: grid W, 1024 threads.  Passes of 16 counts per thread: all 16 loads are issued
-// at once and kept in registers for the offsets, so a pass costs about one load latency.
+// k_scan: grid W, 1024 threads.  Passes of 16384 counts: coalesced loads into LDS, one
+// contiguous run of 16 per thread for the block scan (read with a 1-in-16 padding so the
+// 64 lanes hit distinct banks), offsets written back through LDS with coalesced stores.
 // Also records, for every chunk of kChunk consecutive list positions below `limit`, the
 // tile holding its first position.
+__device__ __forceinline__ uint32_t scan_pad(uint32_t i) { return i + (i >> 4); }
+
 __global__ __launch_bounds__(kScanThreads) void k_scan(
     uint64_t tiles, const uint32_t* __restrict__ counts, uint32_t* __restrict__ offsets,
     uint64_t* __restrict__ nnz, uint32_t* __restrict__ chunk_tile, uint64_t chunks,
     uint64_t limit) {
   constexpr int PER = 16;
+  constexpr uint32_t PASS = kScanThreads * PER;
+  __shared__ uint32_t lc[PASS + PASS / 16];
+  __shared__ uint32_t wsum[kScanThreads / kWave];
   const uint32_t k = blockIdx.x;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const uint32_t* cnt = counts + (uint64_t)k * tiles;
   uint32_t* off = offsets + (uint64_t)k * (tiles + 1);
   uint32_t* ct = chunk_tile + (uint64_t)k * chunks;
-  __shared__ uint32_t wsum[kScanThreads / kWave];
   uint32_t carry = 0;
-  for (uint64_t base = 0; base < tiles; base += (uint64_t)kScanThreads * PER) {
-    const uint64_t t0 = base + (uint64_t)tid * PER;
+  for (uint64_t base = 0; base < tiles; base += PASS) {
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const uint32_t i = tid + kScanThreads * u;
+      lc[scan_pad(i)] = base + i < tiles ? cnt[base + i] : 0u;
+    }
+    __syncthreads();
     uint32_t v[PER], sum = 0;
 #pragma unroll
     for (int u = 0; u < PER; ++u) {
-      v[u] = t0 + u < tiles ? cnt[t0 + u] : 0u;
+      v[u] = lc[scan_pad(tid * PER + u)];
       sum += v[u];
     }
     const uint32_t inc = wave_inclusive_sum(sum);
@@ -120,10 +136,11 @@ __global__ __launch_bounds__(kScanThreads) void k_scan(
       if (w < wave) run += wsum[w];
       pass_total += wsum[w];
     }
+    const uint64_t t0 = base + (uint64_t)tid * PER;
 #pragma unroll
     for (int u = 0; u < PER; ++u) {
-      if (t0 + u < tiles) {
-        off[t0 + u] = run;
+      lc[scan_pad(tid * PER + u)] = run;
+      if (chunks && t0 + u < tiles) {
         // chunks whose first position falls inside this tile start here
         for (uint64_t c0 = ((uint64_t)run + kChunk - 1) / kChunk;
              c0 < chunks && c0 * kChunk < (uint64_t)run + v[u] && c0 * kChunk < limit; ++c0)
@@ -131,8 +148,14 @@ __global__ __launch_bounds__(kScanThreads) void k_scan(
       }
       run += v[u];
     }
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const uint32_t i = tid + kScanThreads * u;
+      if (base + i < tiles) off[base + i] = lc[scan_pad(i)];
+    }
     carry += pass_total;
-    __syncthreads();  // wsum is rewritten next pass
+    __syncthreads();  // lc and wsum are rewritten next pass
   }
   if (tid == 0) {
     off[tiles] = carry;
@@ -141,11 +164,14 @@ __global__ __launch_bounds__(kScanThreads) void k_scan(
 }
 
 // ---------------------------------------------------------------------------------------
-// k_expand: grid (tiles, W), 256 threads.  Lists the tile's non-zeros at list positions
-// offsets[t] + (rank within the tile): the 128 bitmap words and their popcount prefix go to
-// LDS, each thread takes 8 groups of four elements and, for the groups holding a set bit,
-// re-reads only that 16-byte group of the gradient (all 8 loads issued before use) and
-// stores its pairs straight to their list positions (a tile's positions are contiguous).
+// k_expand: grid (ceil(tiles / 2), W), 256 threads; one workgroup lists two stream tiles
+// (8192 elements, 128 words) at list positions offsets[2e] + (rank within the span): the
+// words and their popcount prefix go to LDS, each thread takes 8 groups of four elements
+// and, for the groups holding a set bit, re-reads only that 16-byte group of the gradient
+// (all 8 loads issued before use) and stores its pairs straight to their list positions
+// (the span's positions are contiguous).
+constexpr int kExpandSpan = 2 * kTile;
+constexpr int kExpandWords = kExpandSpan / 64;
 __global__ __launch_bounds__(kExpandThreads) void k_expand(
     const float* __restrict__ grad, uint64_t ld, uint64_t tiles,
     const uint64_t* __restrict__ bitmaps, uint64_t words, const uint32_t* __restrict__ offsets,
@@ -153,22 +179,24 @@ __global__ __launch_bounds__(kExpandThreads) void k_expand(
   const uint32_t t = blockIdx.x, k = blockIdx.y;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const uint32_t* off = offsets + (uint64_t)k * (tiles + 1);
-  const uint64_t o_t = off[t];
-  if (off[t + 1] == o_t || o_t >= cap) return;  // nothing of this tile is listed
-  __shared__ uint64_t lwords[kTileWords];
-  __shared__ uint32_t lwoff[kTileWords + 2];
-  if (tid < kTileWords) {
-    const uint64_t q = (uint64_t)t * kTileWords + tid;
+  const uint64_t t_lo = 2ull * t;
+  const uint64_t t_hi = t_lo + 2 < tiles ? t_lo + 2 : tiles;
+  const uint64_t o_t = off[t_lo];
+  if (off[t_hi] == o_t || o_t >= cap) return;  // nothing of this span is listed
+  __shared__ uint64_t lwords[kExpandWords];
+  __shared__ uint32_t lwoff[kExpandWords + 2];
+  if (tid < kExpandWords) {
+    const uint64_t q = (uint64_t)t * kExpandWords + tid;
     const uint64_t wv = q < words ? bitmaps[(uint64_t)k * words + q] : 0ull;
     const uint32_t pc = (uint32_t)__popcll(wv);
     const uint32_t inc = wave_inclusive_sum(pc);
     lwords[tid] = wv;
     lwoff[tid] = inc - pc;
-    if (lane == kWave - 1) lwoff[kTileWords + wave] = inc;
+    if (lane == kWave - 1) lwoff[kExpandWords + wave] = inc;
   }
   __syncthreads();
-  const float* row = grad + (uint64_t)k * ld + (uint64_t)t * kTile;
-  constexpr int G = kTile / 4 / kExpandThreads;  // groups per thread
+  const float* row = grad + (uint64_t)k * ld + (uint64_t)t * kExpandSpan;
+  constexpr int G = kExpandSpan / 4 / kExpandThreads;  // groups per thread
   f32x4 v[G];
   uint32_t nib[G], pos0[G];
 #pragma unroll
@@ -177,7 +205,7 @@ __global__ __launch_bounds__(kExpandThreads) void k_expand(
     const int q = gidx >> 4, sh = 4 * (gidx & 15);
     const uint64_t wv = lwords[q];
     nib[m] = (uint32_t)(wv >> sh) & 0xFu;
-    pos0[m] = lwoff[q] + (q >= kWave ? lwoff[kTileWords] : 0u) +
+    pos0[m] = lwoff[q] + (q >= kWave ? lwoff[kExpandWords] : 0u) +
               (uint32_t)__popcll(wv & ((1ull << sh) - 1ull));
     // a set bit lies below n <= ld and the group is 4-aligned: the load stays in the row
     if (nib[m]) v[m] = *reinterpret_cast<const f32x4*>(row + 4 * gidx);
@@ -187,7 +215,7 @@ __global__ __launch_bounds__(kExpandThreads) void k_expand(
 #pragma unroll
   for (int m = 0; m < G; ++m) {
     if (!nib[m]) continue;
-    const uint32_t e0 = t * (uint32_t)kTile + 4u * (uint32_t)(tid + kExpandThreads * m);
+    const uint32_t e0 = t * (uint32_t)kExpandSpan + 4u * (uint32_t)(tid + kExpandThreads * m);
     uint64_t pos = o_t + pos0[m];
 #pragma unroll
     for (int c4 = 0; c4 < 4; ++c4) {
@@ -459,7 +487,7 @@ hipError_t launch_expand(uint32_t W, const float* grad, uint64_t ld, uint64_t ti
                          const uint64_t* bitmaps, uint64_t words, const uint32_t* offsets,
                          uint32_t* idx, float* val, uint64_t cap, hipStream_t s) {
   if (tiles == 0 || cap == 0) return hipSuccess;
-  hipLaunchKernelGGL(k_expand, dim3((uint32_t)tiles, W), dim3(kExpandThreads), 0, s, grad, ld,
+  hipLaunchKernelGGL(k_expand, dim3((uint32_t)((tiles + 1) / 2), W), dim3(kExpandThreads), 0, s, grad, ld,
                      tiles, bitmaps, words, offsets, idx, val, cap);
   return hipGetLastError();
 }

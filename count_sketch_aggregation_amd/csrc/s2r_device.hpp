@@ -113,6 +113,43 @@ __device__ __forceinline__ uint32_t wave_sum(uint32_t x) {
   return x;
 }
 
+// Number of set bits of w below this lane's position (v_mbcnt_lo/hi): with one lane per bit
+// of a 64-bit word, it is the rank of the lane's bit among the word's set bits.
+__device__ __forceinline__ uint32_t bits_below_lane(uint64_t w) {
+  return __builtin_amdgcn_mbcnt_hi((uint32_t)(w >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)w, 0u));
+}
+
+__device__ __forceinline__ uint64_t readlane64(uint64_t v, int l) {
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, l);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), l);
+  return ((uint64_t)hi << 32) | lo;
+}
+
+// List expansion of bitmap words held in registers: lane l of the wave owns words
+// qbase(l) + u (u < WPT) whose first set bit has list rank rank[u].  Writes
+// item[r - start] = 64 * word + bit for every set bit with rank r in [start, end).  The wave
+// visits only lanes whose word is non-empty and meets the range (a ballot), broadcasts that
+// word, and expands its 64 bits with one lane per bit (v_mbcnt gives each bit's rank), so the
+// cost follows the set bits in range, not the span of words.
+template <int WPT>
+__device__ __forceinline__ void expand_owned_words(const uint64_t* wv, const uint64_t* rank,
+                                                   uint64_t qbase, uint64_t start, uint64_t end,
+                                                   uint32_t* item, int lane) {
+#pragma unroll
+  for (int u = 0; u < WPT; ++u) {
+    const uint64_t pc = (uint64_t)__popcll(wv[u]);
+    uint64_t m = __ballot(pc != 0 && rank[u] < end && rank[u] + pc > start);
+    while (m) {
+      const int l = __builtin_ctzll(m);
+      m &= m - 1;
+      const uint64_t w = readlane64(wv[u], l);
+      const uint64_t r = readlane64(rank[u], l) + bits_below_lane(w);
+      const uint64_t q = readlane64(qbase, l) + u;
+      if (((w >> lane) & 1ull) && r >= start && r < end) item[r - start] = (uint32_t)(q * 64) + lane;
+    }
+  }
+}
+
 // Bit position (0..63) of the k-th set bit of w, k < popcount(w): halve the window six
 // times by comparing k with the popcount of its low half.
 __device__ __forceinline__ uint32_t select_bit(uint64_t w, uint32_t k) {

@@ -10,10 +10,11 @@
 namespace s2r {
 
 // ---- encode geometry -------------------------------------------------------------------
-constexpr int kStreamThreads = 256;                 // 4 waves
-constexpr int kStreamVec = 8;                       // float4 loads per thread
-constexpr int kTile = kStreamThreads * kStreamVec * 4;  // 8192 elements per tile
-constexpr int kTileWords = kTile / 64;              // 128 bitmap words per tile
+constexpr int kStreamThreads = 512;                 // 8 waves
+constexpr int kStreamVec = 2;                       // float4 loads per thread
+constexpr int kTile = kStreamThreads * kStreamVec * 4;  // 4096 elements per tile
+constexpr int kTileWords = kTile / 64;              // 64 bitmap words per tile
+constexpr int kStreamWaveSpan = kTile / (kStreamThreads / 64);  // elements per wave
 
 constexpr int kExpandThreads = 256;
 constexpr int kScatterThreads = 256;

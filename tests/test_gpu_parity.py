@@ -58,6 +58,7 @@ ENCODE_CASES = [
     ("n64", 2, 64, 64, 0.5, 3, 10, 10, {}),
     ("n65_pad_garbage", 3, 65, 72, 0.5, 2, 8, None, {"pad": 7.0}),
     ("tile_edges", 2, 8193, 8196, 0.3, 5, 16, None, {}),
+    ("tile_edge_4097", 3, 4097, 4100, 0.6, 3, 12, None, {}),
     ("ragged_many_tiles", 3, 100_003, 100_008, 0.05, 3, 15, None, {"pad": float("nan")}),
     ("dense_all", 2, 20_000, 20_000, 1.0, 3, 12, None, {}),
     ("all_zero", 2, 30_000, 30_000, 0.0, 3, 12, None, {}),
