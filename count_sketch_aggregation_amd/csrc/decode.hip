@@ -6,9 +6,9 @@
 //
 // Two paths.
 //
-// Direct (no workspace, or a table that does not partition): k_dwrite lists the set bits of
-// each 8192-element tile in LDS and, per item, gathers its d sketch cells from HBM and takes
-// a register median; the tile is written with 128-bit coalesced stores, zeros included.
+// Direct (no workspace, or a table small enough to stay cache-resident): k_dwrite gathers,
+// for every set bit of its 8192-element tile, the d sketch cells from memory and takes a
+// register median; the tile is written with 128-bit coalesced stores, zeros included.
 // Random gathers into a table larger than L2 run at ~55-80 G/s on MI355X, so this path is
 // bound by the d*U gathers.
 //
@@ -19,9 +19,12 @@
 //   k_dbin     per rank chunk: expands its indices from the bitmap, counting-sorts them by
 //              partition in LDS, writes them partition-ordered with per-partition offsets,
 //              and records for every rank its slot in that order;
-//   k_dmedian  per partition: loads the partition's d x 2^K cells into LDS once and takes
-//              every item's median from LDS, writing it at the item's slot;
-//   k_dwrite   per tile: fetches each set bit's median through its slot and writes the tile.
+//   k_dmedian  per partition (split over rank-chunk ranges): loads the partition's d x 2^K
+//              cells into LDS and takes every item's median from LDS, writing it at the
+//              item's slot;
+//   k_dunsort  per rank chunk: moves the medians from slot order to rank order;
+//   k_dwrite   per tile: reads the medians of its set bits in rank order and writes the
+//              tile.
 // If U exceeds the workspace capacity the first three steps do nothing and k_dwrite falls
 // back to the direct gathers, decided on the device.
 #include <string.h>
@@ -37,6 +40,10 @@ constexpr int kDecTile = 8192;
 constexpr int kDecWords = kDecTile / 64;     // 128
 constexpr uint64_t kDirectTableBytes = 8ull << 20;
 constexpr int kDBinThreads = 512;
+constexpr int kDUnsortThreads = 512;
+constexpr int kDMedianUnroll = 4;  // items in flight per thread (stride kAccThreads)
+constexpr uint64_t kDMedianTargetGroups = 1536;
+constexpr uint32_t kDMedianMaxSplits = 8;
 constexpr int kDBinWordsPerThread = 4;
 constexpr int kDBinBatchWords = kDBinThreads * kDBinWordsPerThread;  // 2048 words per round
 
@@ -69,7 +76,8 @@ struct DecodeWs {
   const uint32_t* chunk_tile; // [chunks] tile holding rank c * kChunk
   uint32_t* bidx;             // [chunks][kChunk] indices, partition-ordered per chunk
   uint16_t* slot;             // [chunks][kChunk] rank -> slot in that order
-  float* gval;                // [chunks][kChunk] median of the item at each slot
+  float* gval;                // [chunks][kChunk] median of the item at each slot (k_dmedian),
+                              // then of each rank (k_dunsort)
   uint32_t* prefix;           // [P + 1][chunks] partition starts per chunk
   uint64_t chunks;            // capacity in chunks (max_set rounded up)
   uint64_t max_set;
@@ -181,7 +189,10 @@ __global__ __launch_bounds__(kDBinThreads) void k_dbin(HashArgs h, uint64_t n,
 }
 
 // ---------------------------------------------------------------------------------------
-// k_dmedian: grid = partitions, 1024 threads.  LDS holds the partition's d x 2^K cells.
+// k_dmedian: grid (partitions, splits), kAccThreads threads.  LDS holds the partition's
+// d x 2^K cells; workgroup (p, s) takes the partition-p items of the s-th of `splits` equal
+// ranges of rank chunks (their segments flattened as in the encode accumulation, kDMedianUnroll
+// items per thread in flight) and writes each median at its item's slot.
 template <int D>
 __global__ __launch_bounds__(kAccThreads) void k_dmedian(HashArgs h, uint64_t tiles,
                                                          const float* __restrict__ sketch,
@@ -195,6 +206,10 @@ __global__ __launch_bounds__(kAccThreads) void k_dmedian(HashArgs h, uint64_t ti
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const uint64_t U = ws.toff[tiles];
   if (U > ws.max_set || U == 0) return;
+  const uint64_t nch = (U + kChunk - 1) / kChunk;
+  const uint32_t c_lo = (uint32_t)(nch * blockIdx.y / gridDim.y);
+  const uint32_t c_hi = (uint32_t)(nch * (blockIdx.y + 1) / gridDim.y);
+  if (c_lo >= c_hi) return;
   const uint32_t pw = 1u << h.K;
   const float* sk = sketch + (uint64_t)p * pw;
   if (vec4) {
@@ -210,12 +225,11 @@ __global__ __launch_bounds__(kAccThreads) void k_dmedian(HashArgs h, uint64_t ti
       tile[c] = sk[(uint64_t)j * w + q];
     }
   }
-  const uint32_t nch = (uint32_t)((U + kChunk - 1) / kChunk);
   const uint32_t* pf = ws.prefix + (uint64_t)p * ws.chunks;
   constexpr int PER = kSegBatch / kAccThreads;
-  for (uint32_t cb = 0; cb < nch; cb += kSegBatch) {
-    const uint32_t nb = nch - cb < (uint32_t)kSegBatch ? nch - cb : (uint32_t)kSegBatch;
-    __syncthreads();
+  for (uint32_t cb = c_lo; cb < c_hi; cb += kSegBatch) {
+    const uint32_t nb = c_hi - cb < (uint32_t)kSegBatch ? c_hi - cb : (uint32_t)kSegBatch;
+    __syncthreads();  // the previous batch is consumed (and the tile is loaded)
     uint32_t len[PER], sum = 0;
 #pragma unroll
     for (int u = 0; u < PER; ++u) {
@@ -242,22 +256,22 @@ __global__ __launch_bounds__(kAccThreads) void k_dmedian(HashArgs h, uint64_t ti
     if (tid == kAccThreads - 1 && nb == (uint32_t)kSegBatch) seg_off[kSegBatch] = run;
     __syncthreads();
     const uint32_t E = seg_off[nb];
-    for (uint32_t e0 = tid * kAccEntries; e0 < E; e0 += kAccThreads * kAccEntries) {
-      uint32_t c = segment_of(seg_off, nb, e0);
-      uint32_t ii[kAccEntries];
-      uint64_t at[kAccEntries];
+    for (uint32_t e0 = tid; e0 < E; e0 += kAccThreads * kDMedianUnroll) {
+      uint32_t e[kDMedianUnroll], c[kDMedianUnroll];
 #pragma unroll
-      for (int u = 0; u < kAccEntries; ++u) {
-        const uint32_t e = e0 + u;
-        if (e < E) {
-          while (seg_off[c + 1] <= e) ++c;
-          at[u] = (uint64_t)seg_src[c] + (e - seg_off[c]);
+      for (int u = 0; u < kDMedianUnroll; ++u) e[u] = e0 + u * kAccThreads;
+      segments_of<kDMedianUnroll>(seg_off, nb, e, c);
+      uint32_t at[kDMedianUnroll], ii[kDMedianUnroll];
+#pragma unroll
+      for (int u = 0; u < kDMedianUnroll; ++u) {
+        if (e[u] < E) {
+          at[u] = seg_src[c[u]] + (e[u] - seg_off[c[u]]);
           ii[u] = ws.bidx[at[u]];
         }
       }
 #pragma unroll
-      for (int u = 0; u < kAccEntries; ++u) {
-        if (e0 + u < E) {
+      for (int u = 0; u < kDMedianUnroll; ++u) {
+        if (e[u] < E) {
           float v[D];
 #pragma unroll
           for (int j = 0; j < D; ++j)
@@ -270,8 +284,36 @@ __global__ __launch_bounds__(kAccThreads) void k_dmedian(HashArgs h, uint64_t ti
 }
 
 // ---------------------------------------------------------------------------------------
-// k_dwrite: grid = tiles, 256 threads.  partitioned = 0: direct gathers for every item;
-// partitioned = 1: medians from k_dmedian (direct gathers if U exceeded the capacity).
+// k_dunsort: grid = rank chunks, kDUnsortThreads threads.  Puts a chunk's medians from slot
+// order into rank order in place: the chunk's 8192 values are staged in LDS with coalesced
+// loads, then rank r takes the value at its slot, with coalesced slot reads and stores.
+__global__ __launch_bounds__(kDUnsortThreads) void k_dunsort(uint64_t tiles, DecodeWs ws) {
+  __shared__ __align__(16) float lv[kChunk];
+  const uint32_t c = blockIdx.x;
+  const int tid = threadIdx.x;
+  const uint64_t U = ws.toff[tiles];
+  if (U > ws.max_set) return;
+  const uint64_t start = (uint64_t)c * kChunk;
+  if (start >= U) return;
+  const uint32_t cnt = (uint32_t)(U - start < kChunk ? U - start : kChunk);
+  float* g = ws.gval + start;
+  const uint16_t* sl = ws.slot + start;
+  const uint32_t cnt4 = cnt / 4;
+  for (uint32_t q = tid; q < cnt4; q += kDUnsortThreads)
+    *reinterpret_cast<f32x4*>(&lv[4 * q]) = *reinterpret_cast<const f32x4*>(g + 4 * q);
+  for (uint32_t s = 4 * cnt4 + tid; s < cnt; s += kDUnsortThreads) lv[s] = g[s];
+  __syncthreads();
+  for (uint32_t r = tid; r < cnt; r += kDUnsortThreads) g[r] = lv[sl[r]];
+}
+
+// ---------------------------------------------------------------------------------------
+// k_dwrite: grid = tiles, 256 threads.  Thread t writes the float4 groups g = t + 256 r
+// (elements base + 4g .. 4g + 3, r = 0..7) straight from registers, zeros included.  The
+// tile's 128 bitmap words and their rank offsets sit in LDS; the set bits of a group take
+// consecutive ranks starting at the word's offset plus the popcount of the bits below the
+// group.  partitioned = 1 reads the medians in rank order (after k_dunsort); direct
+// (partitioned = 0, or U over the capacity) gathers each set bit's d cells and takes the
+// median in registers.
 template <int D>
 __global__ __launch_bounds__(kDecThreads) void k_dwrite(HashArgs h, uint64_t n, uint64_t nwords,
                                                         const uint64_t* __restrict__ bitmap,
@@ -279,84 +321,90 @@ __global__ __launch_bounds__(kDecThreads) void k_dwrite(HashArgs h, uint64_t n, 
                                                         uint64_t w, float* __restrict__ out,
                                                         DecodeWs ws, uint64_t tiles,
                                                         int partitioned) {
-  __shared__ __align__(16) float otile[kDecTile];
   __shared__ uint64_t lw[kDecWords];
   __shared__ uint32_t lwo[kDecWords];
   __shared__ uint32_t wtot[2];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const uint64_t base = (uint64_t)blockIdx.x * kDecTile;
-  for (int c = tid; c < kDecTile; c += kDecThreads) otile[c] = 0.f;
   uint64_t wv = 0;
   if (tid < kDecWords) wv = masked_word(bitmap, nwords, n, (uint64_t)blockIdx.x * kDecWords + tid);
   const uint32_t pc = (uint32_t)__popcll(wv);
   const uint32_t inc = wave_inclusive_sum(pc);
-  if (tid < kDecWords && lane == kWave - 1) wtot[wave] = inc;
-  if (tid < kDecWords) lw[tid] = wv;
+  if (tid < kDecWords) {
+    lw[tid] = wv;
+    if (lane == kWave - 1) wtot[wave] = inc;
+  }
   __syncthreads();
   if (tid < kDecWords) lwo[tid] = inc - pc + (wave ? wtot[0] : 0u);
   __syncthreads();
-  const uint32_t cnt = wtot[0] + wtot[1];
   bool direct = !partitioned;
   uint64_t rank0 = 0;
   if (partitioned) {
     direct = ws.toff[tiles] > ws.max_set;
     rank0 = ws.toff[blockIdx.x];
   }
-  constexpr int UN = 4;  // items per thread in flight
-  if (direct) {
-    for (uint32_t e0 = tid; e0 < cnt; e0 += UN * kDecThreads) {
-      uint32_t li[UN];
-      float v[UN][D];
+  constexpr int RPT = kDecTile / 4 / kDecThreads;  // 8 groups per thread
+  uint32_t nib[RPT], rk[RPT];
 #pragma unroll
-      for (int u = 0; u < UN; ++u) {
-        const uint32_t e = e0 + u * kDecThreads;
-        if (e < cnt) {
-          const uint32_t q = segment_of(lwo, kDecWords, e);
-          li[u] = q * 64 + select_bit(lw[q], e - lwo[q]);
-          const uint32_t i = (uint32_t)(base + li[u]);
-          const uint32_t part = partition_of(h, i);
+  for (int r = 0; r < RPT; ++r) {
+    const uint32_t g = tid + kDecThreads * r;
+    const uint32_t q = g >> 4, sh = 4 * (g & 15);
+    const uint64_t word = lw[q];
+    nib[r] = (uint32_t)(word >> sh) & 0xFu;
+    rk[r] = lwo[q] + (uint32_t)__popcll(word & ((1ull << sh) - 1ull));
+  }
+  f32x4 o[RPT];
+  if (!direct) {
 #pragma unroll
-          for (int j = 0; j < D; ++j)
-            v[u][j] = apply_sign(sketch[(uint64_t)j * w + bucket_of(h, part, j, i)],
-                                 sign_mask(h, j, i));
-        }
+    for (int r = 0; r < RPT; ++r) {
+      // a group's set bits have consecutive ranks
+      float v[4];
+      uint32_t k = rk[r];
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        v[b] = 0.f;
+        if ((nib[r] >> b) & 1u) v[b] = ws.gval[rank0 + k++];
       }
-#pragma unroll
-      for (int u = 0; u < UN; ++u)
-        if (e0 + u * kDecThreads < cnt) otile[li[u]] = median_of<D>(v[u]);
+      o[r] = f32x4{v[0], v[1], v[2], v[3]};
     }
   } else {
-    for (uint32_t e0 = tid; e0 < cnt; e0 += UN * kDecThreads) {
-      uint32_t li[UN];
-      uint16_t sl[UN];
 #pragma unroll
-      for (int u = 0; u < UN; ++u) {
-        const uint32_t e = e0 + u * kDecThreads;
-        if (e < cnt) {
-          const uint32_t q = segment_of(lwo, kDecWords, e);
-          li[u] = q * 64 + select_bit(lw[q], e - lwo[q]);
-          sl[u] = ws.slot[rank0 + e];
+    for (int r = 0; r < RPT; ++r) {
+      float m[4] = {0.f, 0.f, 0.f, 0.f};
+      if (nib[r]) {
+        const uint32_t i0 = (uint32_t)(base + 4 * (tid + kDecThreads * r));
+        float v[4][D];
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+          if ((nib[r] >> b) & 1u) {
+            const uint32_t i = i0 + b;
+            const uint32_t part = partition_of(h, i);
+#pragma unroll
+            for (int j = 0; j < D; ++j)
+              v[b][j] = apply_sign(sketch[(uint64_t)j * w + bucket_of(h, part, j, i)],
+                                   sign_mask(h, j, i));
+          }
         }
-      }
-      float g[UN];
 #pragma unroll
-      for (int u = 0; u < UN; ++u) {
-        const uint64_t r = rank0 + e0 + u * kDecThreads;
-        if (e0 + u * kDecThreads < cnt) g[u] = ws.gval[r / kChunk * kChunk + sl[u]];
+        for (int b = 0; b < 4; ++b)
+          if ((nib[r] >> b) & 1u) m[b] = median_of<D>(v[b]);
       }
-#pragma unroll
-      for (int u = 0; u < UN; ++u)
-        if (e0 + u * kDecThreads < cnt) otile[li[u]] = g[u];
+      o[r] = f32x4{m[0], m[1], m[2], m[3]};
     }
   }
-  __syncthreads();
   if (base + kDecTile <= n) {
-    f32x4* o = reinterpret_cast<f32x4*>(out + base);
-    for (int c = tid; c < kDecTile / 4; c += kDecThreads)
-      o[c] = *reinterpret_cast<const f32x4*>(&otile[4 * c]);
+    f32x4* o4 = reinterpret_cast<f32x4*>(out + base);
+#pragma unroll
+    for (int r = 0; r < RPT; ++r) o4[tid + kDecThreads * r] = o[r];
   } else {
-    for (int c = tid; c < kDecTile; c += kDecThreads)
-      if (base + c < n) out[base + c] = otile[c];
+#pragma unroll
+    for (int r = 0; r < RPT; ++r) {
+      const uint64_t e = base + 4 * (uint64_t)(tid + kDecThreads * r);
+      if (e + 0 < n) out[e + 0] = o[r].x;
+      if (e + 1 < n) out[e + 1] = o[r].y;
+      if (e + 2 < n) out[e + 2] = o[r].z;
+      if (e + 3 < n) out[e + 3] = o[r].w;
+    }
   }
 }
 
@@ -439,14 +487,24 @@ hipError_t launch_decode(const HashArgs& h, const s2r_params& p, uint64_t n,
       if (e != hipSuccess) return e;
       const size_t tlds = ((size_t)p.d << p.log2_part) * sizeof(float);
       const int vec4 = (p.log2_part >= 2 && (reinterpret_cast<uintptr_t>(sketch) % 16) == 0);
+      // enough workgroups to fill the chip about twice at a few per CU; each split reloads
+      // the partition's cells, so never more splits than rank chunks
+      uint32_t splits = (uint32_t)((kDMedianTargetGroups + L.partitions - 1) / L.partitions);
+      if (splits > kDMedianMaxSplits) splits = kDMedianMaxSplits;
+      if (splits > L.chunks) splits = (uint32_t)L.chunks;
+      if (splits < 1) splits = 1;
       S2R_DISPATCH_D(p.d, {
         e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_dmedian<D>),
                                 hipFuncAttributeMaxDynamicSharedMemorySize, (int)tlds);
         if (e == hipSuccess)
-          hipLaunchKernelGGL((k_dmedian<D>), dim3((uint32_t)L.partitions), dim3(kAccThreads), tlds,
+          hipLaunchKernelGGL((k_dmedian<D>), dim3((uint32_t)L.partitions, splits), dim3(kAccThreads), tlds,
                              s, h, L.tiles, sketch, w, ws, (uint32_t)L.partitions, vec4);
       });
       if (e != hipSuccess) return e;
+      e = hipGetLastError();
+      if (e != hipSuccess) return e;
+      hipLaunchKernelGGL(k_dunsort, dim3((uint32_t)L.chunks), dim3(kDUnsortThreads), 0, s, L.tiles,
+                         ws);
       e = hipGetLastError();
       if (e != hipSuccess) return e;
     }

@@ -348,7 +348,7 @@ __global__ __launch_bounds__(kBinThreads) void k_bin(
 // k_accumulate (partitioned path): grid (P, W), 512 threads.  The partition's d x 2^K
 // buckets live in LDS.  Its entries are spread over one short segment per list chunk; the
 // segments of up to kSegBatch chunks are flattened with a prefix sum so that consecutive
-// threads read consecutive entries, four per thread in flight.
+// threads read consecutive entries, several per thread in flight.
 template <int D>
 __global__ __launch_bounds__(kAccThreads) void k_accumulate(
     HashArgs h, uint64_t tiles, const uint32_t* __restrict__ offsets, uint64_t cap,
@@ -399,36 +399,41 @@ __global__ __launch_bounds__(kAccThreads) void k_accumulate(
     if (tid == kAccThreads - 1 && nb == (uint32_t)kSegBatch) seg_off[kSegBatch] = run;
     __syncthreads();
     const uint32_t E = seg_off[nb];
-    for (uint32_t e0 = tid * kAccEntries; e0 < E; e0 += kAccThreads * kAccEntries) {
-      // four consecutive entries: one search, then walk forward across segment ends
-      uint32_t c = segment_of(seg_off, nb, e0);
-      uint32_t ii[kAccEntries];
-      float gg[kAccEntries];
-      bool on[kAccEntries];
+    constexpr int UN = acc_unroll(D);
+    for (uint32_t e0 = tid; e0 < E; e0 += kAccThreads * UN) {
+      // UN entries e0 + u * kAccThreads: coalesced across the wave, searched,
+      // loaded and added with all of them in flight
+      uint32_t e[UN], c[UN];
 #pragma unroll
-      for (int u = 0; u < kAccEntries; ++u) {
-        const uint32_t e = e0 + u;
-        on[u] = e < E;
+      for (int u = 0; u < UN; ++u) e[u] = e0 + u * kAccThreads;
+      segments_of<UN>(seg_off, nb, e, c);
+      uint32_t ii[UN];
+      float gg[UN];
+      bool on[UN];
+#pragma unroll
+      for (int u = 0; u < UN; ++u) {
+        on[u] = e[u] < E;
+        ii[u] = 0;
+        gg[u] = 0.f;
         if (on[u]) {
-          while (seg_off[c + 1] <= e) ++c;
-          const uint2 pr = bins[kbase + seg_src[c] + (e - seg_off[c])];
+          const uint2 pr = bins[kbase + seg_src[c[u]] + (e[u] - seg_off[c[u]])];
           ii[u] = pr.x;
           gg[u] = __uint_as_float(pr.y);
         }
       }
-      uint32_t cell[kAccEntries * D];
-      float add[kAccEntries * D];
-      bool live[kAccEntries * D];
+      uint32_t cell[UN * D];
+      float add[UN * D];
+      bool live[UN * D];
 #pragma unroll
-      for (int u = 0; u < kAccEntries; ++u) {
+      for (int u = 0; u < UN; ++u) {
 #pragma unroll
         for (int j = 0; j < D; ++j) {
           live[u * D + j] = on[u];
-          cell[u * D + j] = j * pw + (on[u] ? row_bucket(h, j, ii[u]) : 0u);
-          add[u * D + j] = on[u] ? apply_sign(gg[u], sign_mask(h, j, ii[u])) : 0.f;
+          cell[u * D + j] = j * pw + row_bucket(h, j, ii[u]);
+          add[u * D + j] = apply_sign(gg[u], sign_mask(h, j, ii[u]));
         }
       }
-      lds_add_f32_many<kAccEntries * D>(tile, cell, add, live);
+      lds_add_f32_many<UN * D>(tile, cell, add, live);
     }
   }
   __syncthreads();

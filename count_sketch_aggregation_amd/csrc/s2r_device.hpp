@@ -131,10 +131,10 @@ __device__ __forceinline__ uint64_t readlane64(uint64_t v, int l) {
 // visits only lanes whose word is non-empty and meets the range (a ballot), broadcasts that
 // word, and expands its 64 bits with one lane per bit (v_mbcnt gives each bit's rank), so the
 // cost follows the set bits in range, not the span of words.
-template <int WPT>
+template <int WPT, typename T = uint32_t>
 __device__ __forceinline__ void expand_owned_words(const uint64_t* wv, const uint64_t* rank,
                                                    uint64_t qbase, uint64_t start, uint64_t end,
-                                                   uint32_t* item, int lane) {
+                                                   T* item, int lane) {
 #pragma unroll
   for (int u = 0; u < WPT; ++u) {
     const uint64_t pc = (uint64_t)__popcll(wv[u]);
@@ -145,7 +145,7 @@ __device__ __forceinline__ void expand_owned_words(const uint64_t* wv, const uin
       const uint64_t w = readlane64(wv[u], l);
       const uint64_t r = readlane64(rank[u], l) + bits_below_lane(w);
       const uint64_t q = readlane64(qbase, l) + u;
-      if (((w >> lane) & 1ull) && r >= start && r < end) item[r - start] = (uint32_t)(q * 64) + lane;
+      if (((w >> lane) & 1ull) && r >= start && r < end) item[r - start] = (T)(q * 64 + lane);
     }
   }
 }
@@ -193,15 +193,21 @@ __device__ __forceinline__ void lds_add_f32_many(float* tile, const uint32_t* ce
   }
 }
 
-// Largest c in [0, nb) with off[c] <= e (off non-decreasing, off[0] = 0).
-__device__ __forceinline__ uint32_t segment_of(const uint32_t* off, uint32_t nb, uint32_t e) {
-  uint32_t lo = 0, hi = nb;
-  while (hi - lo > 1) {
-    const uint32_t mid = (lo + hi) >> 1;
-    if (off[mid] <= e) lo = mid;
-    else hi = mid;
+// For each of U positions e[u]: the largest c in [0, nb) with off[c] <= e[u] (off
+// non-decreasing, off[0] = 0).  Branch-free search whose step count depends only on nb, so
+// the U searches advance together with U independent LDS reads per step.
+template <int U>
+__device__ __forceinline__ void segments_of(const uint32_t* off, uint32_t nb, const uint32_t* e,
+                                            uint32_t* c) {
+#pragma unroll
+  for (int u = 0; u < U; ++u) c[u] = 0;
+  uint32_t len = nb;
+  while (len > 1) {
+    const uint32_t half = len >> 1;
+#pragma unroll
+    for (int u = 0; u < U; ++u) c[u] += (off[c[u] + half] <= e[u]) ? half : 0u;
+    len -= half;
   }
-  return lo;
 }
 
 }  // namespace s2r

@@ -22,7 +22,9 @@ constexpr int kChunk = 8192;                        // list entries per chunk
 constexpr int kBinThreads = 512;                    // 16 entries per thread
 constexpr int kMaxPartitions = 8192;                // LDS histogram limit of the binning pass
 constexpr int kAccThreads = 512;
-constexpr int kAccEntries = 1;                    // consecutive entries per thread and round
+// entries in flight per thread of the encode accumulation (measured on MI355X: 2 beats 1
+// and 4, which costs occupancy at d = 5); one for many rows keeps it out of scratch
+constexpr int acc_unroll(int d) { return d <= 5 ? 2 : 1; }
 constexpr int kSegBatch = 1024;                     // chunk segments flattened per batch
 constexpr size_t kAccLdsBytes = 64 * 1024;          // LDS of one partition tile
 
