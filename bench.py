@@ -15,6 +15,10 @@ traffic of the implementation are not credited.
 
 Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--workload embedding]
 Prints ONE JSON line on stdout; progress goes to stderr.
+
+`python bench.py --copy-reference` instead runs a plain 1 GiB device copy (an elementwise
+kernel that reads 1 GiB and writes 1 GiB), the known-size reference that scales the
+FETCH_SIZE / WRITE_SIZE hardware counters into bytes.
 """
 from __future__ import annotations
 
@@ -29,6 +33,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
+COPY_REF_BYTES = 1 << 30
 
 
 def log(msg: str) -> None:
@@ -57,6 +62,39 @@ def build_inputs(wl, dev, hash_family: str):
         log(f"  worker {k}: nnz={idx.size}")
     cap = nnz_max
     return p, grad, ld, cap, sparse
+
+
+def library_source_sha256() -> str:
+    """sha256 over the library's sources (kernels, launchers, C header), by file name."""
+    import glob
+    import hashlib
+
+    h = hashlib.sha256()
+    files = sorted(glob.glob(os.path.join(ROOT, "count_sketch_aggregation_amd", "csrc", "*")))
+    files.append(os.path.join(ROOT, "include", "s2r.h"))
+    for f in files:
+        h.update(os.path.basename(f).encode())
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload: str, phase: str):
+    """HBM bytes per call of `phase` from the committed counter summary
+    (profiles/<workload>_traffic.md: FETCH_SIZE and WRITE_SIZE passes scaled by the copy
+    reference), or None if there is none or the library sources changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", f"{workload}_traffic.md")
+    if phase != "encode" or not os.path.exists(path):
+        return None
+    vals = {}
+    with open(path) as fh:
+        for line in fh:
+            if ":" in line and line.split(":", 1)[0] in ("traffic_bytes_per_call", "source_sha256"):
+                k, v = line.split(":", 1)
+                vals[k] = v.strip()
+    if vals.get("source_sha256") != library_source_sha256() or "traffic_bytes_per_call" not in vals:
+        return None
+    return int(vals["traffic_bytes_per_call"])
 
 
 def cpu_baseline(wl, sparse, p_dict, budget_s: float = 20.0):
@@ -97,6 +135,25 @@ def cpu_baseline(wl, sparse, p_dict, budget_s: float = 20.0):
     }
 
 
+def copy_reference() -> int:
+    import torch
+
+    dev = torch.device("cuda:0")
+    src = torch.ones(COPY_REF_BYTES // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    torch.mul(src, 1.0, out=dst)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(3):
+        torch.mul(src, 1.0, out=dst)
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / 3
+    print(json.dumps({"copy_reference_bytes_read": COPY_REF_BYTES,
+                      "copy_reference_bytes_written": COPY_REF_BYTES,
+                      "GBs": round(2 * COPY_REF_BYTES / dt / 1e9, 1)}), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -107,7 +164,11 @@ def main() -> int:
     ap.add_argument("--hash", dest="hash_family", default="partitioned",
                     choices=["partitioned", "independent"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-reference", action="store_true",
+                    help="run the 1 GiB copy that calibrates the traffic counters, then exit")
     args = ap.parse_args()
+    if args.copy_reference:
+        return copy_reference()
 
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the W data-parallel "
@@ -207,7 +268,7 @@ def main() -> int:
                    "set_bits_merged": U},
         "roofline": {"bound": "hbm", "kernel": f"s2r_{dom}", "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": None},
+                     "traffic": measured_traffic(wl.name, dom)},
         "step_alg_GBs": round(step_alg, 1),
         "step_hbm_frac": round(step_alg / HBM_PEAK_GBS, 4),
         "phases": phases,

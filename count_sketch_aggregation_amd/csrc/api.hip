@@ -60,6 +60,12 @@ EncodeLayout encode_layout(const s2r_params& p, uint32_t W, uint64_t n, uint64_t
   off = align256(off + (size_t)W * L.tiles * 4);
   L.off_offsets = off;
   off = align256(off + (size_t)W * (L.tiles + 1) * 4);
+  L.off_btot = off;
+  off = align256(off + (size_t)W * scan_blocks(L.tiles) * 8);
+  L.off_spans = off;
+  off = align256(off + (size_t)W * ((L.tiles + 1) / 2) * 4);
+  L.off_nspan = off;
+  off = align256(off + (size_t)W * 4);
   L.off_bins = L.off_prefix = off;
   if (L.partitioned) {
     const size_t slots = (size_t)W * L.chunks * kChunk;
@@ -146,8 +152,12 @@ s2r_status s2r_encode(const s2r_params* p, uint32_t W, const float* grad, uint64
 
   if (!L.partitioned) S2R_TRY(launch_fill_zero(sketches, (uint64_t)W * dw, s));
   S2R_TRY(launch_stream(W, grad, n, ld, L.tiles, bitmaps, counts, s));
-  S2R_TRY(launch_scan(W, L.tiles, counts, offsets, nnz, nullptr, 0, cap, s));
-  S2R_TRY(launch_expand(W, grad, ld, L.tiles, bitmaps, words, offsets, idx, val, cap, s));
+  uint32_t* spans = reinterpret_cast<uint32_t*>(ws + L.off_spans);
+  uint32_t* nspan = reinterpret_cast<uint32_t*>(ws + L.off_nspan);
+  S2R_TRY(launch_scan(W, L.tiles, counts, offsets, nnz, nullptr, 0, cap,
+                      reinterpret_cast<uint2*>(ws + L.off_btot), spans, nspan, s));
+  S2R_TRY(launch_expand(W, grad, ld, L.tiles, bitmaps, words, offsets, spans, nspan, idx, val, cap,
+                        s));
   if (L.partitioned) {
     uint2* bins = reinterpret_cast<uint2*>(ws + L.off_bins);
     uint32_t* prefix = reinterpret_cast<uint32_t*>(ws + L.off_prefix);

@@ -189,7 +189,7 @@ __global__ __launch_bounds__(kDBinThreads) void k_dbin(HashArgs h, uint64_t n,
 }
 
 // ---------------------------------------------------------------------------------------
-// k_dmedian: grid (partitions, splits), kAccThreads threads.  LDS holds the partition's
+// k_dmedian: grid (partitions, splits), kAccThreads threads, items XCD-grouped.  LDS holds the partition's
 // d x 2^K cells; workgroup (p, s) takes the partition-p items of the s-th of `splits` equal
 // ranges of rank chunks (their segments flattened as in the encode accumulation, kDMedianUnroll
 // items per thread in flight) and writes each median at its item's slot.
@@ -202,13 +202,14 @@ __global__ __launch_bounds__(kAccThreads) void k_dmedian(HashArgs h, uint64_t ti
   __shared__ uint32_t seg_src[kSegBatch];
   __shared__ uint32_t seg_off[kSegBatch + 1];
   __shared__ uint32_t wtot[kAccThreads / kWave];
-  const uint32_t p = blockIdx.x;
+  const uint32_t item = xcd_grouped_item();
+  const uint32_t p = item % P, split = item / P;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const uint64_t U = ws.toff[tiles];
   if (U > ws.max_set || U == 0) return;
   const uint64_t nch = (U + kChunk - 1) / kChunk;
-  const uint32_t c_lo = (uint32_t)(nch * blockIdx.y / gridDim.y);
-  const uint32_t c_hi = (uint32_t)(nch * (blockIdx.y + 1) / gridDim.y);
+  const uint32_t c_lo = (uint32_t)(nch * split / gridDim.y);
+  const uint32_t c_hi = (uint32_t)(nch * (split + 1) / gridDim.y);
   if (c_lo >= c_hi) return;
   const uint32_t pw = 1u << h.K;
   const float* sk = sketch + (uint64_t)p * pw;
@@ -425,6 +426,8 @@ DecodeLayout decode_layout(const s2r_params& p, uint64_t n, uint64_t max_set) {
   off = align256(off + L.tiles * 4);
   L.off_toff = off;
   off = align256(off + (L.tiles + 1) * 4);
+  L.off_btot = off;
+  off = align256(off + (size_t)scan_blocks(L.tiles) * 8);
   L.off_total = off;
   off = align256(off + 8);
   L.off_chunk_tile = off;
@@ -474,7 +477,8 @@ hipError_t launch_decode(const HashArgs& h, const s2r_params& p, uint64_t n,
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     e = launch_scan(1, L.tiles, tcount, toff, reinterpret_cast<uint64_t*>(b + L.off_total),
-                    chunk_tile, L.chunks, ws.max_set, s);
+                    chunk_tile, L.chunks, ws.max_set, reinterpret_cast<uint2*>(b + L.off_btot),
+                    nullptr, nullptr, s);
     if (e != hipSuccess) return e;
     if (L.chunks > 0) {
       const size_t lds = (L.partitions + 1) * sizeof(uint32_t);

@@ -94,139 +94,212 @@ __global__ __launch_bounds__(kStreamThreads) void k_stream(
 }
 
 // ---------------------------------------------------------------------------------------
-// k_scan: grid W, 1024 threads.  Passes of 16384 counts: coalesced loads into LDS, one
-// contiguous run of 16 per thread for the block scan (read with a 1-in-16 padding so the
-// 64 lanes hit distinct banks), offsets written back through LDS with coalesced stores.
-// Also records, for every chunk of kChunk consecutive list positions below `limit`, the
-// tile holding its first position.
+// k_scan: grid (blocks, W), 1024 threads; block b of worker k scans tiles
+// [b * kScanPass, (b + 1) * kScanPass): coalesced loads into LDS, one contiguous run of 16 per
+// thread for the block scan (read with a 1-in-16 padding so the 64 lanes hit distinct
+// banks), offsets written back through LDS with coalesced stores.  The block starts from the
+// totals of the blocks before it (btot, from k_scan_sum; none with one block).
+// Optionally (spans != nullptr) it also lists, in order, the spans (tile pairs) that hold a
+// non-zero, for k_expand, with their count in nspan.  And, for every chunk of kChunk
+// consecutive list positions below `limit`, it records the tile holding its first position.
 __device__ __forceinline__ uint32_t scan_pad(uint32_t i) { return i + (i >> 4); }
+
+__global__ __launch_bounds__(kScanThreads) void k_scan_sum(uint64_t tiles,
+                                                           const uint32_t* __restrict__ counts,
+                                                           uint2* __restrict__ btot) {
+  __shared__ uint32_t wsum[2][kScanThreads / kWave];
+  const uint32_t b = blockIdx.x, k = blockIdx.y;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const uint32_t* cnt = counts + (uint64_t)k * tiles;
+  const uint64_t base = (uint64_t)b * kScanPass;
+  uint32_t sum = 0, ne = 0;
+#pragma unroll
+  for (int u = 0; u < kScanPass / 2 / kScanThreads; ++u) {
+    const uint64_t i = base + 2 * (uint64_t)(tid + kScanThreads * u);  // a span's first tile
+    const uint32_t c = (i < tiles ? cnt[i] : 0u) + (i + 1 < tiles ? cnt[i + 1] : 0u);
+    sum += c;
+    ne += c ? 1u : 0u;
+  }
+  sum = wave_sum(sum);
+  ne = wave_sum(ne);
+  if (lane == 0) {
+    wsum[0][wave] = sum;
+    wsum[1][wave] = ne;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    uint2 t = {0u, 0u};
+    for (int v = 0; v < kScanThreads / kWave; ++v) {
+      t.x += wsum[0][v];
+      t.y += wsum[1][v];
+    }
+    btot[(uint64_t)k * gridDim.x + b] = t;
+  }
+}
 
 __global__ __launch_bounds__(kScanThreads) void k_scan(
     uint64_t tiles, const uint32_t* __restrict__ counts, uint32_t* __restrict__ offsets,
     uint64_t* __restrict__ nnz, uint32_t* __restrict__ chunk_tile, uint64_t chunks,
-    uint64_t limit) {
-  constexpr int PER = 16;
-  constexpr uint32_t PASS = kScanThreads * PER;
-  __shared__ uint32_t lc[PASS + PASS / 16];
-  __shared__ uint32_t wsum[kScanThreads / kWave];
-  const uint32_t k = blockIdx.x;
+    uint64_t limit, const uint2* __restrict__ btot, uint32_t* __restrict__ spans,
+    uint32_t* __restrict__ nspan) {
+  constexpr int PER = kScanPass / kScanThreads;  // 16 tiles = 8 spans per thread
+  __shared__ uint32_t lc[kScanPass + kScanPass / 16];
+  __shared__ uint32_t wsum[2][kScanThreads / kWave];
+  const uint32_t b = blockIdx.x, k = blockIdx.y, nb = gridDim.x;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const uint32_t* cnt = counts + (uint64_t)k * tiles;
   uint32_t* off = offsets + (uint64_t)k * (tiles + 1);
   uint32_t* ct = chunk_tile + (uint64_t)k * chunks;
-  uint32_t carry = 0;
-  for (uint64_t base = 0; base < tiles; base += PASS) {
-#pragma unroll
-    for (int u = 0; u < PER; ++u) {
-      const uint32_t i = tid + kScanThreads * u;
-      lc[scan_pad(i)] = base + i < tiles ? cnt[base + i] : 0u;
+  uint32_t* sp = spans ? spans + (uint64_t)k * ((tiles + 1) / 2) : nullptr;
+  const uint64_t base = (uint64_t)b * kScanPass;
+  uint32_t carry = 0, scarry = 0;
+  if (b > 0) {  // totals of the blocks before this one
+    uint32_t c = 0, e = 0;
+    for (uint32_t i = tid; i < b; i += kScanThreads) {
+      const uint2 t = btot[(uint64_t)k * nb + i];
+      c += t.x;
+      e += t.y;
+    }
+    c = wave_sum(c);
+    e = wave_sum(e);
+    if (lane == 0) {
+      wsum[0][wave] = c;
+      wsum[1][wave] = e;
     }
     __syncthreads();
-    uint32_t v[PER], sum = 0;
-#pragma unroll
-    for (int u = 0; u < PER; ++u) {
-      v[u] = lc[scan_pad(tid * PER + u)];
-      sum += v[u];
+    for (int v = 0; v < kScanThreads / kWave; ++v) {
+      carry += wsum[0][v];
+      scarry += wsum[1][v];
     }
-    const uint32_t inc = wave_inclusive_sum(sum);
-    if (lane == kWave - 1) wsum[wave] = inc;
-    __syncthreads();
-    uint32_t run = carry + inc - sum, pass_total = 0;
-    for (int w = 0; w < kScanThreads / kWave; ++w) {
-      if (w < wave) run += wsum[w];
-      pass_total += wsum[w];
-    }
-    const uint64_t t0 = base + (uint64_t)tid * PER;
-#pragma unroll
-    for (int u = 0; u < PER; ++u) {
-      lc[scan_pad(tid * PER + u)] = run;
-      if (chunks && t0 + u < tiles) {
-        // chunks whose first position falls inside this tile start here
-        for (uint64_t c0 = ((uint64_t)run + kChunk - 1) / kChunk;
-             c0 < chunks && c0 * kChunk < (uint64_t)run + v[u] && c0 * kChunk < limit; ++c0)
-          ct[c0] = (uint32_t)(t0 + u);
-      }
-      run += v[u];
-    }
-    __syncthreads();
-#pragma unroll
-    for (int u = 0; u < PER; ++u) {
-      const uint32_t i = tid + kScanThreads * u;
-      if (base + i < tiles) off[base + i] = lc[scan_pad(i)];
-    }
-    carry += pass_total;
-    __syncthreads();  // lc and wsum are rewritten next pass
+    __syncthreads();  // wsum is reused below
   }
-  if (tid == 0) {
-    off[tiles] = carry;
-    nnz[k] = carry;
+#pragma unroll
+  for (int u = 0; u < PER; ++u) {
+    const uint32_t i = tid + kScanThreads * u;
+    lc[scan_pad(i)] = base + i < tiles ? cnt[base + i] : 0u;
+  }
+  __syncthreads();
+  uint32_t v[PER], sum = 0, ne = 0;
+#pragma unroll
+  for (int u = 0; u < PER; ++u) {
+    v[u] = lc[scan_pad(tid * PER + u)];
+    sum += v[u];
+    if (u & 1) ne += (v[u - 1] | v[u]) ? 1u : 0u;
+  }
+  const uint32_t inc = wave_inclusive_sum(sum);
+  const uint32_t sinc = wave_inclusive_sum(ne);
+  if (lane == kWave - 1) {
+    wsum[0][wave] = inc;
+    wsum[1][wave] = sinc;
+  }
+  __syncthreads();
+  uint32_t run = carry + inc - sum, block_total = 0;
+  uint32_t srun = scarry + sinc - ne, block_spans = 0;
+  for (int w = 0; w < kScanThreads / kWave; ++w) {
+    if (w < wave) {
+      run += wsum[0][w];
+      srun += wsum[1][w];
+    }
+    block_total += wsum[0][w];
+    block_spans += wsum[1][w];
+  }
+  const uint64_t t0 = base + (uint64_t)tid * PER;
+#pragma unroll
+  for (int u = 0; u < PER; ++u) {
+    lc[scan_pad(tid * PER + u)] = run;
+    if (chunks && t0 + u < tiles) {
+      // chunks whose first position falls inside this tile start here
+      for (uint64_t c0 = ((uint64_t)run + kChunk - 1) / kChunk;
+           c0 < chunks && c0 * kChunk < (uint64_t)run + v[u] && c0 * kChunk < limit; ++c0)
+        ct[c0] = (uint32_t)(t0 + u);
+    }
+    if (sp && (u & 1) && (v[u - 1] | v[u])) sp[srun++] = (uint32_t)((t0 + u) >> 1);
+    run += v[u];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int u = 0; u < PER; ++u) {
+    const uint32_t i = tid + kScanThreads * u;
+    if (base + i < tiles) off[base + i] = lc[scan_pad(i)];
+  }
+  if (b == nb - 1 && tid == 0) {
+    off[tiles] = carry + block_total;
+    nnz[k] = carry + block_total;
+    if (nspan) nspan[k] = scarry + block_spans;
   }
 }
 
 // ---------------------------------------------------------------------------------------
-// k_expand: grid (ceil(tiles / 2), W), 256 threads; one workgroup lists two stream tiles
-// (8192 elements, 128 words) at list positions offsets[2e] + (rank within the span): the
-// words and their popcount prefix go to LDS, each thread takes 8 groups of four elements
-// and, for the groups holding a set bit, re-reads only that 16-byte group of the gradient
-// (all 8 loads issued before use) and stores its pairs straight to their list positions
-// (the span's positions are contiguous).
+// k_expand: grid (G, W), 256 threads.  Workgroup g of worker k lists the non-empty spans
+// spans[g], spans[g + G], ... (tile pairs, 8192 elements, 128 words, from k_scan), so empty
+// regions cost no workgroups.  Per span, at list positions offsets[2 t] + (rank within the
+// span): the words and their popcount prefix go to LDS, each thread takes 8 groups of four
+// elements and, for the groups holding a set bit, re-reads only that 16-byte group of the
+// gradient (all 8 loads issued before use) and stores its pairs straight to their list
+// positions (the span's positions are contiguous).
 constexpr int kExpandSpan = 2 * kTile;
 constexpr int kExpandWords = kExpandSpan / 64;
 __global__ __launch_bounds__(kExpandThreads) void k_expand(
     const float* __restrict__ grad, uint64_t ld, uint64_t tiles,
     const uint64_t* __restrict__ bitmaps, uint64_t words, const uint32_t* __restrict__ offsets,
+    const uint32_t* __restrict__ spans, const uint32_t* __restrict__ nspan,
     uint32_t* __restrict__ idx, float* __restrict__ val, uint64_t cap) {
-  const uint32_t t = blockIdx.x, k = blockIdx.y;
+  const uint32_t k = blockIdx.y;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const uint32_t* off = offsets + (uint64_t)k * (tiles + 1);
-  const uint64_t t_lo = 2ull * t;
-  const uint64_t t_hi = t_lo + 2 < tiles ? t_lo + 2 : tiles;
-  const uint64_t o_t = off[t_lo];
-  if (off[t_hi] == o_t || o_t >= cap) return;  // nothing of this span is listed
+  const uint64_t nsp = (tiles + 1) / 2;
+  const uint32_t* sl = spans + (uint64_t)k * nsp;
+  const uint32_t ns = nspan[k];
   __shared__ uint64_t lwords[kExpandWords];
   __shared__ uint32_t lwoff[kExpandWords + 2];
-  if (tid < kExpandWords) {
-    const uint64_t q = (uint64_t)t * kExpandWords + tid;
-    const uint64_t wv = q < words ? bitmaps[(uint64_t)k * words + q] : 0ull;
-    const uint32_t pc = (uint32_t)__popcll(wv);
-    const uint32_t inc = wave_inclusive_sum(pc);
-    lwords[tid] = wv;
-    lwoff[tid] = inc - pc;
-    if (lane == kWave - 1) lwoff[kExpandWords + wave] = inc;
-  }
-  __syncthreads();
-  const float* row = grad + (uint64_t)k * ld + (uint64_t)t * kExpandSpan;
-  constexpr int G = kExpandSpan / 4 / kExpandThreads;  // groups per thread
-  f32x4 v[G];
-  uint32_t nib[G], pos0[G];
-#pragma unroll
-  for (int m = 0; m < G; ++m) {
-    const int gidx = tid + kExpandThreads * m;
-    const int q = gidx >> 4, sh = 4 * (gidx & 15);
-    const uint64_t wv = lwords[q];
-    nib[m] = (uint32_t)(wv >> sh) & 0xFu;
-    pos0[m] = lwoff[q] + (q >= kWave ? lwoff[kExpandWords] : 0u) +
-              (uint32_t)__popcll(wv & ((1ull << sh) - 1ull));
-    // a set bit lies below n <= ld and the group is 4-aligned: the load stays in the row
-    if (nib[m]) v[m] = *reinterpret_cast<const f32x4*>(row + 4 * gidx);
-  }
   uint32_t* oi = idx + (uint64_t)k * cap;
   float* ov = val + (uint64_t)k * cap;
+  for (uint32_t si = blockIdx.x; si < ns; si += gridDim.x) {
+    const uint32_t t = sl[si];
+    const uint64_t o_t = off[2ull * t];
+    if (o_t >= cap) continue;  // beyond the list capacity (uniform)
+    if (tid < kExpandWords) {
+      const uint64_t q = (uint64_t)t * kExpandWords + tid;
+      const uint64_t wv = q < words ? bitmaps[(uint64_t)k * words + q] : 0ull;
+      const uint32_t pc = (uint32_t)__popcll(wv);
+      const uint32_t inc = wave_inclusive_sum(pc);
+      lwords[tid] = wv;
+      lwoff[tid] = inc - pc;
+      if (lane == kWave - 1) lwoff[kExpandWords + wave] = inc;
+    }
+    __syncthreads();
+    const float* row = grad + (uint64_t)k * ld + (uint64_t)t * kExpandSpan;
+    constexpr int G = kExpandSpan / 4 / kExpandThreads;  // groups per thread
+    f32x4 v[G];
+    uint32_t nib[G], pos0[G];
 #pragma unroll
-  for (int m = 0; m < G; ++m) {
-    if (!nib[m]) continue;
-    const uint32_t e0 = t * (uint32_t)kExpandSpan + 4u * (uint32_t)(tid + kExpandThreads * m);
-    uint64_t pos = o_t + pos0[m];
+    for (int m = 0; m < G; ++m) {
+      const int gidx = tid + kExpandThreads * m;
+      const int q = gidx >> 4, sh = 4 * (gidx & 15);
+      const uint64_t wv = lwords[q];
+      nib[m] = (uint32_t)(wv >> sh) & 0xFu;
+      pos0[m] = lwoff[q] + (q >= kWave ? lwoff[kExpandWords] : 0u) +
+                (uint32_t)__popcll(wv & ((1ull << sh) - 1ull));
+      // a set bit lies below n <= ld and the group is 4-aligned: the load stays in the row
+      if (nib[m]) v[m] = *reinterpret_cast<const f32x4*>(row + 4 * gidx);
+    }
 #pragma unroll
-    for (int c4 = 0; c4 < 4; ++c4) {
-      if (nib[m] & (1u << c4)) {
-        if (pos < cap) {
-          oi[pos] = e0 + c4;
-          ov[pos] = v[m][c4];
+    for (int m = 0; m < G; ++m) {
+      if (!nib[m]) continue;
+      const uint32_t e0 = t * (uint32_t)kExpandSpan + 4u * (uint32_t)(tid + kExpandThreads * m);
+      uint64_t pos = o_t + pos0[m];
+#pragma unroll
+      for (int c4 = 0; c4 < 4; ++c4) {
+        if (nib[m] & (1u << c4)) {
+          if (pos < cap) {
+            oi[pos] = e0 + c4;
+            ov[pos] = v[m][c4];
+          }
+          ++pos;
         }
-        ++pos;
       }
     }
+    __syncthreads();  // lwords and lwoff are rewritten for the next span
   }
 }
 
@@ -345,7 +418,7 @@ __global__ __launch_bounds__(kBinThreads) void k_bin(
   if ((cnt & 1u) && tid == 0) out[cnt - 1] = spair[cnt - 1];
 }
 
-// k_accumulate (partitioned path): grid (P, W), 512 threads.  The partition's d x 2^K
+// k_accumulate (partitioned path): grid (P, W), 512 threads, items XCD-grouped.  The partition's d x 2^K
 // buckets live in LDS.  Its entries are spread over one short segment per list chunk; the
 // segments of up to kSegBatch chunks are flattened with a prefix sum so that consecutive
 // threads read consecutive entries, several per thread in flight.
@@ -358,7 +431,8 @@ __global__ __launch_bounds__(kAccThreads) void k_accumulate(
   __shared__ uint32_t seg_src[kSegBatch];
   __shared__ uint32_t seg_off[kSegBatch + 1];
   __shared__ uint32_t wtot[kAccThreads / kWave];
-  const uint32_t p = blockIdx.x, k = blockIdx.y;
+  const uint32_t item = xcd_grouped_item();
+  const uint32_t p = item % partitions, k = item / partitions;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const uint32_t pw = 1u << h.K;
   const uint32_t cells = D * pw;
@@ -472,11 +546,21 @@ hipError_t launch_stream(uint32_t W, const float* grad, uint64_t n, uint64_t ld,
   return hipGetLastError();
 }
 
+uint32_t scan_blocks(uint64_t tiles) {
+  return (uint32_t)((tiles + kScanPass - 1) / kScanPass);
+}
+
 hipError_t launch_scan(uint32_t W, uint64_t tiles, const uint32_t* counts, uint32_t* offsets,
                        uint64_t* nnz, uint32_t* chunk_tile, uint64_t chunks, uint64_t cap,
-                       hipStream_t s) {
-  hipLaunchKernelGGL(k_scan, dim3(W), dim3(kScanThreads), 0, s, tiles, counts, offsets, nnz,
-                     chunk_tile, chunks, cap);
+                       uint2* btot, uint32_t* spans, uint32_t* nspan, hipStream_t s) {
+  const uint32_t nb = tiles > 0 ? scan_blocks(tiles) : 1;
+  if (nb > 1) {
+    hipLaunchKernelGGL(k_scan_sum, dim3(nb, W), dim3(kScanThreads), 0, s, tiles, counts, btot);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL(k_scan, dim3(nb, W), dim3(kScanThreads), 0, s, tiles, counts, offsets, nnz,
+                     chunk_tile, chunks, cap, btot, spans, nspan);
   return hipGetLastError();
 }
 
@@ -490,10 +574,14 @@ hipError_t launch_fill_zero(float* p, uint64_t count, hipStream_t s) {
 
 hipError_t launch_expand(uint32_t W, const float* grad, uint64_t ld, uint64_t tiles,
                          const uint64_t* bitmaps, uint64_t words, const uint32_t* offsets,
-                         uint32_t* idx, float* val, uint64_t cap, hipStream_t s) {
+                         const uint32_t* spans, const uint32_t* nspan, uint32_t* idx, float* val,
+                         uint64_t cap, hipStream_t s) {
   if (tiles == 0 || cap == 0) return hipSuccess;
-  hipLaunchKernelGGL(k_expand, dim3((uint32_t)((tiles + 1) / 2), W), dim3(kExpandThreads), 0, s, grad, ld,
-                     tiles, bitmaps, words, offsets, idx, val, cap);
+  const uint64_t nsp = (tiles + 1) / 2;
+  uint64_t g = (kExpandGroups + W - 1) / W;
+  if (g > nsp) g = nsp;
+  hipLaunchKernelGGL(k_expand, dim3((uint32_t)g, W), dim3(kExpandThreads), 0, s, grad, ld, tiles,
+                     bitmaps, words, offsets, spans, nspan, idx, val, cap);
   return hipGetLastError();
 }
 

@@ -15,6 +15,7 @@
 namespace s2r {
 
 constexpr int kWave = 64;
+constexpr uint32_t kXcds = 8;  // accelerator complex dies of an MI355X
 
 // Kernel-argument copy of the hash constants.  Shifts are precomputed on the host so
 // kernels need no branches on K or L: top b bits of a 32-bit word = (uint64)hi >> (32-b),
@@ -191,6 +192,17 @@ __device__ __forceinline__ void lds_add_f32_many(float* tile, const uint32_t* ce
       got[r] = atomicCAS(&t[cell[r]], old[r], __float_as_uint(__uint_as_float(old[r]) + v[r]));
     }
   }
+}
+
+// Workgroups are dispatched to the 8 XCDs round-robin by linear id, and each XCD has its own
+// L2.  This maps the linear id so that XCD x runs the x-th eighth of the (x-fastest) work
+// items in order: neighbouring items, which share cache lines at their edges, then run on one
+// XCD at about the same time.  Identity when the grid is not a multiple of 8.
+__device__ __forceinline__ uint32_t xcd_grouped_item() {
+  const uint32_t lin = blockIdx.x + blockIdx.y * gridDim.x;
+  const uint32_t total = gridDim.x * gridDim.y;
+  if (total % kXcds != 0) return lin;
+  return (lin % kXcds) * (total / kXcds) + lin / kXcds;
 }
 
 // For each of U positions e[u]: the largest c in [0, nb) with off[c] <= e[u] (off

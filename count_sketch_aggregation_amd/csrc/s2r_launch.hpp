@@ -17,6 +17,7 @@ constexpr int kTileWords = kTile / 64;              // 64 bitmap words per tile
 constexpr int kStreamWaveSpan = kTile / (kStreamThreads / 64);  // elements per wave
 
 constexpr int kExpandThreads = 256;
+constexpr uint64_t kExpandGroups = 4096;             // expand workgroups per launch, all workers
 constexpr int kScatterThreads = 256;
 constexpr int kChunk = 8192;                        // list entries per chunk
 constexpr int kBinThreads = 512;                    // 16 entries per thread
@@ -29,6 +30,7 @@ constexpr int kSegBatch = 1024;                     // chunk segments flattened 
 constexpr size_t kAccLdsBytes = 64 * 1024;          // LDS of one partition tile
 
 constexpr int kScanThreads = 1024;
+constexpr uint32_t kScanPass = kScanThreads * 16;  // tiles per scan block
 
 // Workspace layout of s2r_encode (every section 256-byte aligned).
 struct EncodeLayout {
@@ -36,7 +38,7 @@ struct EncodeLayout {
   uint64_t chunks;       // list chunks per worker (bounded by min(cap, n))
   uint64_t partitions;   // 2^(L-K) on the partitioned path, 0 otherwise
   bool partitioned;
-  size_t off_counts, off_offsets, off_bins, off_prefix, total;
+  size_t off_counts, off_offsets, off_btot, off_spans, off_nspan, off_bins, off_prefix, total;
 };
 EncodeLayout encode_layout(const s2r_params& p, uint32_t W, uint64_t n, uint64_t cap);
 bool use_partitioned(const s2r_params& p);
@@ -45,13 +47,17 @@ HashArgs make_hash_args(const s2r_params& p);
 
 hipError_t launch_stream(uint32_t W, const float* grad, uint64_t n, uint64_t ld,
                          uint64_t tiles, uint64_t* bitmaps, uint32_t* counts, hipStream_t s);
+// tiles are scanned in blocks of kScanPass; more than one block needs W * scan_blocks(tiles)
+// uint2 block totals.  spans (W * ceil(tiles / 2) uint32) and nspan (W uint32) may be null.
+uint32_t scan_blocks(uint64_t tiles);
 hipError_t launch_scan(uint32_t W, uint64_t tiles, const uint32_t* counts, uint32_t* offsets,
                        uint64_t* nnz, uint32_t* chunk_tile, uint64_t chunks, uint64_t cap,
-                       hipStream_t s);
+                       uint2* btot, uint32_t* spans, uint32_t* nspan, hipStream_t s);
 hipError_t launch_fill_zero(float* p, uint64_t count, hipStream_t s);
 hipError_t launch_expand(uint32_t W, const float* grad, uint64_t ld, uint64_t tiles,
                          const uint64_t* bitmaps, uint64_t words, const uint32_t* offsets,
-                         uint32_t* idx, float* val, uint64_t cap, hipStream_t s);
+                         const uint32_t* spans, const uint32_t* nspan, uint32_t* idx, float* val,
+                         uint64_t cap, hipStream_t s);
 hipError_t launch_scatter(const HashArgs& h, uint32_t W, uint64_t tiles, const uint32_t* offsets,
                           const uint32_t* idx, const float* val, uint64_t cap, uint64_t chunks,
                           float* sketches, uint64_t w, hipStream_t s);
@@ -71,7 +77,7 @@ hipError_t launch_reduce(uint32_t W, uint64_t cells, uint64_t words, const uint6
 struct DecodeLayout {
   uint64_t tiles, chunks, partitions;
   bool partitioned;
-  size_t off_tcount, off_toff, off_total, off_chunk_tile, off_bidx, off_slot, off_gval,
+  size_t off_tcount, off_toff, off_btot, off_total, off_chunk_tile, off_bidx, off_slot, off_gval,
       off_prefix, total;
 };
 DecodeLayout decode_layout(const s2r_params& p, uint64_t n, uint64_t max_set);
