@@ -10,7 +10,8 @@ dominant phase reaches on its algorithmic bytes:
   reduce  (W + 1) * (4 d w + 8 words)       read W sketches/bitmaps, write one of each
   decode  8 words + min(4 d w, 4 d U) + 4N  read bitmap and sketch cells, write g_hat
 
-(words = ceil(N/64), U = set bits of the merged bitmap).  List writes and any extra
+(words = bitmap words, ceil(N/64) at the default per-element granularity; U = elements
+queried by the decode, the set bits of the merged bitmap).  List writes and any extra
 traffic of the implementation are not credited.
 
 Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--workload embedding]
@@ -40,7 +41,7 @@ def log(msg: str) -> None:
     print(msg, file=sys.stderr, flush=True)
 
 
-def build_inputs(wl, dev, hash_family: str):
+def build_inputs(wl, dev, hash_family: str, log2_block: int = 0):
     import numpy as np
     import torch
 
@@ -48,7 +49,7 @@ def build_inputs(wl, dev, hash_family: str):
     import workloads as WL
 
     K = wl.log2_w if hash_family == "independent" else s2r.s2r_default_log2_part(wl.d, wl.log2_w)
-    p = s2r.s2r_params_from_seed(wl.hash_seed, wl.d, wl.log2_w, K)
+    p = s2r.s2r_params_from_seed(wl.hash_seed, wl.d, wl.log2_w, K, log2_block=log2_block)
     ld = (wl.N + 3) // 4 * 4
     grad = torch.zeros((wl.W, ld), dtype=torch.float32, device=dev)
     nnz_max = 0
@@ -163,6 +164,8 @@ def main() -> int:
                     help="tiny | embedding | resnet50_blocktopk | transformer_mixed | large")
     ap.add_argument("--hash", dest="hash_family", default="partitioned",
                     choices=["partitioned", "independent"])
+    ap.add_argument("--block", type=int, default=0, metavar="LOG2_B",
+                    help="bitmap granularity: one bit per 2^LOG2_B elements (default 0: per element)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-reference", action="store_true",
                     help="run the 1 GiB copy that calibrates the traffic counters, then exit")
@@ -188,14 +191,14 @@ def main() -> int:
     wl = names[args.workload]
     dev = torch.device("cuda:0")
     log(f"workload {wl.name}: W={wl.W} N={wl.N} d={wl.d} w=2^{wl.log2_w} hash={args.hash_family}")
-    p, grad, ld, cap, sparse = build_inputs(wl, dev, args.hash_family)
+    p, grad, ld, cap, sparse = build_inputs(wl, dev, args.hash_family, args.block)
     buf = s2r.alloc_encode_buffers(p, wl.W, wl.N, cap, dev)
-    words = s2r.s2r_bitmap_words(wl.N)
+    words = s2r.s2r_block_bitmap_words(wl.N, args.block)
     bm = torch.empty(max(words, 1), dtype=torch.int64, device=dev)
     sk = torch.empty((wl.d, 1 << wl.log2_w), dtype=torch.float32, device=dev)
     out = torch.empty(wl.N, dtype=torch.float32, device=dev)
-    # the merged bitmap has at most sum_k nnz_k set bits
-    max_set = min(wl.N, sum(x[0].size for x in sparse))
+    # the merged query set holds at most every worker's touched blocks
+    max_set = min(wl.N, sum(np.unique(x[0] >> args.block).size << args.block for x in sparse))
     dws = s2r.alloc_decode_workspace(p, wl.N, max_set, dev)
     stream = torch.cuda.current_stream()
 
@@ -218,7 +221,11 @@ def main() -> int:
     torch.cuda.synchronize()
     nnz = buf["nnz"].cpu().numpy()
     assert all(int(x) <= cap for x in nnz), "list capacity exceeded"
-    U = int(np.unpackbits(bm.cpu().numpy().view(np.uint8), bitorder="little")[:wl.N].sum())
+    # U = elements queried by the decode (every element of every set block)
+    B = 1 << args.block
+    nblocks = (wl.N + B - 1) // B
+    setb = np.flatnonzero(np.unpackbits(bm.cpu().numpy().view(np.uint8), bitorder="little")[:nblocks])
+    U = int(setb.size) * B - ((nblocks * B - wl.N) if setb.size and setb[-1] == nblocks - 1 else 0)
 
     events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
     torch.cuda.synchronize()
@@ -264,7 +271,8 @@ def main() -> int:
         "dtype": "f32",
         "data": "synthetic",
         "config": {"workload": wl.name, "W": wl.W, "N": wl.N, "d": wl.d, "w": 1 << wl.log2_w,
-                   "log2_part": p.log2_part, "hash": args.hash_family, "nnz_per_worker": int(nnz.max()),
+                   "log2_part": p.log2_part, "log2_block": args.block, "hash": args.hash_family,
+                   "nnz_per_worker": int(nnz.max()),
                    "set_bits_merged": U},
         "roofline": {"bound": "hbm", "kernel": f"s2r_{dom}", "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),

@@ -35,7 +35,7 @@ class s2r_params(ctypes.Structure):
         ("d", ctypes.c_uint32),
         ("log2_w", ctypes.c_uint32),
         ("log2_part", ctypes.c_uint32),
-        ("reserved", ctypes.c_uint32),
+        ("log2_block", ctypes.c_uint32),
         ("pA", ctypes.c_uint64),
         ("pB", ctypes.c_uint64),
         ("hA", ctypes.c_uint64 * MAX_ROWS),
@@ -52,7 +52,7 @@ class s2r_params(ctypes.Structure):
         d = self.d
         return {
             "d": d, "log2_w": self.log2_w, "log2_part": self.log2_part,
-            "pA": self.pA, "pB": self.pB,
+            "log2_block": self.log2_block, "pA": self.pA, "pB": self.pB,
             "hA": list(self.hA)[:d], "hB": list(self.hB)[:d],
             "sA": list(self.sA)[:d], "sB": list(self.sB)[:d],
         }
@@ -79,6 +79,8 @@ def lib() -> ctypes.CDLL:
         L.s2r_default_log2_part.restype = u32
         L.s2r_bitmap_words.argtypes = [u64]
         L.s2r_bitmap_words.restype = u64
+        L.s2r_block_bitmap_words.argtypes = [u64, u32]
+        L.s2r_block_bitmap_words.restype = u64
         L.s2r_encode_workspace_bytes.argtypes = [P(s2r_params), u32, u64, u64]
         L.s2r_encode_workspace_bytes.restype = sz
         L.s2r_encode.argtypes = [P(s2r_params), u32, vp, u64, u64, vp, vp, vp, vp, u64, vp, vp, sz,
@@ -127,15 +129,18 @@ def _stream(stream) -> int | None:
 # entry points (same names as the C ABI)
 
 
-def s2r_params_from_seed(seed: int, d: int, log2_w: int, log2_part: int | None = None) -> s2r_params:
+def s2r_params_from_seed(seed: int, d: int, log2_w: int, log2_part: int | None = None,
+                         log2_block: int = 0) -> s2r_params:
     """Hash constants from a seed (SplitMix64).  log2_part defaults to the largest partition
     that fits the LDS accumulator (s2r_default_log2_part); log2_part == log2_w gives
-    independent rows."""
+    independent rows.  log2_block sets the bitmap granularity (one bit per 2^log2_block
+    elements; 0 = per element)."""
     if log2_part is None:
         log2_part = s2r_default_log2_part(d, log2_w)
     p = s2r_params()
     _check(lib().s2r_params_from_seed(seed, d, log2_w, log2_part, ctypes.byref(p)),
            "s2r_params_from_seed")
+    p.log2_block = log2_block
     return p
 
 
@@ -145,6 +150,10 @@ def s2r_default_log2_part(d: int, log2_w: int) -> int:
 
 def s2r_bitmap_words(n: int) -> int:
     return int(lib().s2r_bitmap_words(n))
+
+
+def s2r_block_bitmap_words(n: int, log2_block: int) -> int:
+    return int(lib().s2r_block_bitmap_words(n, log2_block))
 
 
 def s2r_encode_workspace_bytes(p: s2r_params, W: int, n: int, cap: int) -> int:
@@ -199,7 +208,7 @@ def alloc_decode_workspace(p: s2r_params, n: int, max_set: int, device="cuda"):
 def alloc_encode_buffers(p: s2r_params, W: int, n: int, cap: int, device="cuda") -> dict:
     """torch tensors for every s2r_encode output plus its workspace."""
     import torch
-    words = s2r_bitmap_words(n)
+    words = s2r_block_bitmap_words(n, p.log2_block)
     ws = s2r_encode_workspace_bytes(p, W, n, cap)
     if ws == 0:
         raise S2RError(S2R_ERR_DIM, "s2r_encode_workspace_bytes")
@@ -215,6 +224,7 @@ def alloc_encode_buffers(p: s2r_params, W: int, n: int, cap: int, device="cuda")
 
 __all__ = [
     "s2r_params", "S2RError", "s2r_params_from_seed", "s2r_default_log2_part", "s2r_bitmap_words",
+    "s2r_block_bitmap_words",
     "s2r_encode_workspace_bytes", "s2r_encode", "s2r_reduce", "s2r_decode_workspace_bytes",
     "s2r_decode", "s2r_hash",
     "alloc_encode_buffers", "status_string", "lib",

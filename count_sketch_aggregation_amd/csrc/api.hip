@@ -19,7 +19,7 @@ static inline uint64_t splitmix64_step(uint64_t& state) {
 
 static bool params_ok(const s2r_params* p) {
   return p && p->d >= 1 && p->d <= S2R_MAX_ROWS && p->log2_w <= 31 && p->log2_part <= p->log2_w &&
-         p->reserved == 0;
+         p->log2_block <= S2R_MAX_LOG2_BLOCK;
 }
 
 HashArgs make_hash_args(const s2r_params& p) {
@@ -27,6 +27,7 @@ HashArgs make_hash_args(const s2r_params& p) {
   memset(&h, 0, sizeof(h));
   h.d = p.d;
   h.K = p.log2_part;
+  h.lb = p.log2_block;
   h.shift_part = 32u - (p.log2_w - p.log2_part);
   h.shift_row = 32u - p.log2_part;
   h.pA = p.pA;
@@ -66,6 +67,8 @@ EncodeLayout encode_layout(const s2r_params& p, uint32_t W, uint64_t n, uint64_t
   off = align256(off + (size_t)W * ((L.tiles + 1) / 2) * 4);
   L.off_nspan = off;
   off = align256(off + (size_t)W * 4);
+  L.off_ebm = off;  // element bitmaps when the output bitmap is block-granular
+  if (p.log2_block > 0) off = align256(off + (size_t)W * ((n + 63) / 64) * 8);
   L.off_bins = L.off_prefix = off;
   if (L.partitioned) {
     const size_t slots = (size_t)W * L.chunks * kChunk;
@@ -113,6 +116,12 @@ uint32_t s2r_default_log2_part(uint32_t d, uint32_t log2_w) {
 
 uint64_t s2r_bitmap_words(uint64_t n) { return (n + 63) / 64; }
 
+uint64_t s2r_block_bitmap_words(uint64_t n, uint32_t log2_block) {
+  if (log2_block > 63) return 0;
+  const uint64_t blocks = (n >> log2_block) + ((n & ((1ull << log2_block) - 1)) ? 1 : 0);
+  return (blocks + 63) / 64;
+}
+
 size_t s2r_encode_workspace_bytes(const s2r_params* p, uint32_t W, uint64_t n, uint64_t cap) {
   if (!params_ok(p) || W == 0 || n >= (1ull << 32)) return 0;
   return encode_layout(*p, W, n, cap).total;
@@ -150,14 +159,18 @@ s2r_status s2r_encode(const s2r_params* p, uint32_t W, const float* grad, uint64
   const uint64_t words = s2r_bitmap_words(n);
   const HashArgs h = make_hash_args(*p);
 
+  // block-granular output: the element bitmaps the list step needs stay in the workspace
+  uint64_t* ebm = p->log2_block ? reinterpret_cast<uint64_t*>(ws + L.off_ebm) : bitmaps;
   if (!L.partitioned) S2R_TRY(launch_fill_zero(sketches, (uint64_t)W * dw, s));
-  S2R_TRY(launch_stream(W, grad, n, ld, L.tiles, bitmaps, counts, s));
+  S2R_TRY(launch_stream(W, grad, n, ld, L.tiles, ebm, counts, s));
+  if (p->log2_block)
+    S2R_TRY(launch_blockbits(W, ebm, words, n, p->log2_block,
+                             s2r_block_bitmap_words(n, p->log2_block), bitmaps, s));
   uint32_t* spans = reinterpret_cast<uint32_t*>(ws + L.off_spans);
   uint32_t* nspan = reinterpret_cast<uint32_t*>(ws + L.off_nspan);
   S2R_TRY(launch_scan(W, L.tiles, counts, offsets, nnz, nullptr, 0, cap,
                       reinterpret_cast<uint2*>(ws + L.off_btot), spans, nspan, s));
-  S2R_TRY(launch_expand(W, grad, ld, L.tiles, bitmaps, words, offsets, spans, nspan, idx, val, cap,
-                        s));
+  S2R_TRY(launch_expand(W, grad, ld, L.tiles, ebm, words, offsets, spans, nspan, idx, val, cap, s));
   if (L.partitioned) {
     uint2* bins = reinterpret_cast<uint2*>(ws + L.off_bins);
     uint32_t* prefix = reinterpret_cast<uint32_t*>(ws + L.off_prefix);
@@ -181,8 +194,8 @@ s2r_status s2r_reduce(const s2r_params* p, uint32_t W, uint64_t n, const uint64_
       !aligned(bitmap_out, 8))
     return S2R_ERR_ALIGN;
   const uint64_t cells = (uint64_t)p->d << p->log2_w;
-  S2R_TRY(launch_reduce(W, cells, s2r_bitmap_words(n), bitmaps, sketches, bitmap_out, sketch_out,
-                        static_cast<hipStream_t>(stream)));
+  S2R_TRY(launch_reduce(W, cells, s2r_block_bitmap_words(n, p->log2_block), bitmaps, sketches,
+                        bitmap_out, sketch_out, static_cast<hipStream_t>(stream)));
   return S2R_OK;
 }
 

@@ -47,22 +47,40 @@ constexpr uint32_t kDMedianMaxSplits = 8;
 constexpr int kDBinWordsPerThread = 4;
 constexpr int kDBinBatchWords = kDBinThreads * kDBinWordsPerThread;  // 2048 words per round
 
-// bitmap word q with the bits at or beyond n cleared
+// Element word q (elements 64q .. 64q+63) of the query set, bits at or beyond n cleared.
+// nwords = ceil(n / 64).  With a block-granular bitmap (lb = log2 B > 0) the word is built
+// from the block bits: all ones or zeros for B >= 64, else each of its 64/B block bits
+// spread over B element bits.
 __device__ __forceinline__ uint64_t masked_word(const uint64_t* __restrict__ bitmap,
-                                                uint64_t nwords, uint64_t n, uint64_t q) {
+                                                uint64_t nwords, uint64_t n, uint64_t q,
+                                                uint32_t lb) {
   if (q >= nwords) return 0ull;
-  uint64_t wv = bitmap[q];
   const uint64_t first = q * 64;
+  uint64_t wv;
+  if (lb == 0) {
+    wv = bitmap[q];
+  } else if (lb >= 6) {
+    const uint64_t b = first >> lb;
+    wv = ((bitmap[b >> 6] >> (b & 63)) & 1ull) ? ~0ull : 0ull;
+  } else {
+    const uint32_t B = 1u << lb, per = 64u >> lb;  // B <= 32, per <= 32
+    const uint64_t b0 = first >> lb;               // a multiple of per: one bitmap word
+    const uint64_t bits = (bitmap[b0 >> 6] >> (b0 & 63)) & ((1ull << per) - 1ull);
+    const uint64_t ones = (1ull << B) - 1ull;
+    wv = 0ull;
+    for (uint32_t t = 0; t < per; ++t)
+      if ((bits >> t) & 1ull) wv |= ones << (t * B);
+  }
   if (n - first < 64) wv &= (1ull << (n - first)) - 1ull;
   return wv;
 }
 
 // ---------------------------------------------------------------------------------------
 __global__ __launch_bounds__(kDecWords) void k_dcount(const uint64_t* __restrict__ bitmap,
-                                                      uint64_t n, uint64_t nwords,
+                                                      uint64_t n, uint64_t nwords, uint32_t lb,
                                                       uint32_t* __restrict__ tcount) {
   const uint64_t q = (uint64_t)blockIdx.x * kDecWords + threadIdx.x;
-  const uint32_t c = wave_sum((uint32_t)__popcll(masked_word(bitmap, nwords, n, q)));
+  const uint32_t c = wave_sum((uint32_t)__popcll(masked_word(bitmap, nwords, n, q, lb)));
   __shared__ uint32_t part[kDecWords / kWave];
   if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = c;
   __syncthreads();
@@ -111,7 +129,7 @@ __global__ __launch_bounds__(kDBinThreads) void k_dbin(HashArgs h, uint64_t n,
     uint32_t sum = 0;
 #pragma unroll
     for (int u = 0; u < kDBinWordsPerThread; ++u) {
-      wv[u] = masked_word(bitmap, nwords, n, q0 + (uint64_t)tid * kDBinWordsPerThread + u);
+      wv[u] = masked_word(bitmap, nwords, n, q0 + (uint64_t)tid * kDBinWordsPerThread + u, h.lb);
       sum += (uint32_t)__popcll(wv[u]);
     }
     const uint32_t inc = wave_inclusive_sum(sum);
@@ -328,7 +346,8 @@ __global__ __launch_bounds__(kDecThreads) void k_dwrite(HashArgs h, uint64_t n, 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const uint64_t base = (uint64_t)blockIdx.x * kDecTile;
   uint64_t wv = 0;
-  if (tid < kDecWords) wv = masked_word(bitmap, nwords, n, (uint64_t)blockIdx.x * kDecWords + tid);
+  if (tid < kDecWords)
+    wv = masked_word(bitmap, nwords, n, (uint64_t)blockIdx.x * kDecWords + tid, h.lb);
   const uint32_t pc = (uint32_t)__popcll(wv);
   const uint32_t inc = wave_inclusive_sum(pc);
   if (tid < kDecWords) {
@@ -472,7 +491,7 @@ hipError_t launch_decode(const HashArgs& h, const s2r_params& p, uint64_t n,
     ws.chunks = L.chunks;
     ws.max_set = L.chunks * kChunk < max_set ? L.chunks * kChunk : max_set;
     if (ws.max_set > n) ws.max_set = n;
-    hipLaunchKernelGGL(k_dcount, dim3((uint32_t)L.tiles), dim3(kDecWords), 0, s, bitmap, n, nwords,
+    hipLaunchKernelGGL(k_dcount, dim3((uint32_t)L.tiles), dim3(kDecWords), 0, s, bitmap, n, nwords, h.lb,
                        tcount);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;

@@ -528,6 +528,38 @@ __global__ __launch_bounds__(kAccThreads) void k_accumulate(
   }
 }
 
+// ---------------------------------------------------------------------------------------
+// k_blockbits (block-granular bitmaps): grid (ceil(bwords / 4), W), 256 threads.  Wave v
+// builds output word q = 4 blockIdx.x + v: lane l tests block b = 64 q + l, the OR of the
+// element bits of elements [b B, b B + B) (whole words for B >= 64, a B-bit field of one
+// word otherwise; element bits at or beyond n are already 0), and a ballot forms the word.
+__global__ __launch_bounds__(256) void k_blockbits(const uint64_t* __restrict__ ebm,
+                                                   uint64_t ewords, uint64_t n, uint32_t lb,
+                                                   uint64_t bwords, uint64_t* __restrict__ bbm) {
+  const uint32_t k = blockIdx.y;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const uint64_t q = (uint64_t)blockIdx.x * 4 + wave;
+  if (q >= bwords) return;  // whole wave
+  const uint64_t first = (q * 64 + lane) << lb;
+  const uint64_t* e = ebm + (uint64_t)k * ewords;
+  bool any = false;
+  if (first < n) {
+    if (lb >= 6) {
+      const uint64_t w0 = first >> 6;
+      uint64_t w1 = w0 + (1ull << (lb - 6));
+      if (w1 > ewords) w1 = ewords;
+      uint64_t acc = 0;
+      for (uint64_t x = w0; x < w1; ++x) acc |= e[x];
+      any = acc != 0ull;
+    } else {
+      const uint64_t field = (1ull << (1u << lb)) - 1ull;  // B <= 32 bits
+      any = ((e[first >> 6] >> (first & 63)) & field) != 0ull;
+    }
+  }
+  const uint64_t word = __ballot(any);
+  if (lane == 0) bbm[(uint64_t)k * bwords + q] = word;
+}
+
 __global__ void k_fill_zero(float* __restrict__ p, uint64_t count) {
   const uint64_t stride = (uint64_t)gridDim.x * blockDim.x;
   for (uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; i < count; i += stride)
@@ -569,6 +601,14 @@ hipError_t launch_fill_zero(float* p, uint64_t count, hipStream_t s) {
   uint64_t blocks = (count + 255) / 256;
   if (blocks > 8192) blocks = 8192;
   hipLaunchKernelGGL(k_fill_zero, dim3((uint32_t)blocks), dim3(256), 0, s, p, count);
+  return hipGetLastError();
+}
+
+hipError_t launch_blockbits(uint32_t W, const uint64_t* ebm, uint64_t ewords, uint64_t n,
+                            uint32_t log2_block, uint64_t bwords, uint64_t* bbm, hipStream_t s) {
+  if (bwords == 0) return hipSuccess;
+  hipLaunchKernelGGL(k_blockbits, dim3((uint32_t)((bwords + 3) / 4), W), dim3(256), 0, s, ebm, ewords,
+                     n, log2_block, bwords, bbm);
   return hipGetLastError();
 }
 

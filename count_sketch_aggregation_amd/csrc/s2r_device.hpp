@@ -25,6 +25,7 @@ struct HashArgs {
   uint32_t shift_part;  // 32 - (L - K)
   uint32_t shift_row;   // 32 - K
   uint32_t K;
+  uint32_t lb;          // log2 of the bitmap block size
   uint64_t pA, pB;
   uint64_t hA[S2R_MAX_ROWS], hB[S2R_MAX_ROWS];
   uint64_t sA[S2R_MAX_ROWS], sB[S2R_MAX_ROWS];

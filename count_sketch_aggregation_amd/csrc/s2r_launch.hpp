@@ -38,7 +38,8 @@ struct EncodeLayout {
   uint64_t chunks;       // list chunks per worker (bounded by min(cap, n))
   uint64_t partitions;   // 2^(L-K) on the partitioned path, 0 otherwise
   bool partitioned;
-  size_t off_counts, off_offsets, off_btot, off_spans, off_nspan, off_bins, off_prefix, total;
+  size_t off_counts, off_offsets, off_btot, off_spans, off_nspan, off_ebm, off_bins, off_prefix,
+      total;
 };
 EncodeLayout encode_layout(const s2r_params& p, uint32_t W, uint64_t n, uint64_t cap);
 bool use_partitioned(const s2r_params& p);
@@ -54,6 +55,9 @@ hipError_t launch_scan(uint32_t W, uint64_t tiles, const uint32_t* counts, uint3
                        uint64_t* nnz, uint32_t* chunk_tile, uint64_t chunks, uint64_t cap,
                        uint2* btot, uint32_t* spans, uint32_t* nspan, hipStream_t s);
 hipError_t launch_fill_zero(float* p, uint64_t count, hipStream_t s);
+// block-granular bitmaps [W][bwords] from element bitmaps [W][ewords]
+hipError_t launch_blockbits(uint32_t W, const uint64_t* ebm, uint64_t ewords, uint64_t n,
+                            uint32_t log2_block, uint64_t bwords, uint64_t* bbm, hipStream_t s);
 hipError_t launch_expand(uint32_t W, const float* grad, uint64_t ld, uint64_t tiles,
                          const uint64_t* bitmaps, uint64_t words, const uint32_t* offsets,
                          const uint32_t* spans, const uint32_t* nspan, uint32_t* idx, float* val,

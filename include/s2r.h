@@ -24,8 +24,10 @@
  *     argument check happens on the host before anything is enqueued, so a call that
  *     returns an error has enqueued nothing.  S2R_ERR_HIP means a launch failed.
  *   - Indices are the element positions 0..n-1 of a worker's gradient, so n < 2^32.
- *   - Bitmap layout: ceil(n/64) uint64 words per bitmap, bit i = bit (i % 64) of word
- *     i / 64 (least significant bit first); bits >= n are 0 on output.
+ *   - Bitmap layout: one bit per block of B = 2^log2_block consecutive elements (B = 1:
+ *     one bit per element).  s2r_block_bitmap_words(n, log2_block) uint64 words per
+ *     bitmap; bit b (block b, elements b*B .. b*B+B-1) = bit (b % 64) of word b / 64, least
+ *     significant bit first; bits of blocks at or beyond ceil(n/B) are 0 on output.
  *   - Sketch layout: fp32 [d][w] row-major per worker, w = 2^log2_w.
  *   - "Non-zero" means (bits(x) & 0x7fffffff) != 0: +0 and -0 are zero, subnormals are
  *     not.  Non-finite gradient values are outside the contract.
@@ -41,6 +43,7 @@ extern "C" {
 #endif
 
 #define S2R_MAX_ROWS 16
+#define S2R_MAX_LOG2_BLOCK 16
 
 typedef enum {
   S2R_OK = 0,
@@ -71,14 +74,19 @@ typedef struct {
   uint32_t d;         /* rows (the pages' r), 1..S2R_MAX_ROWS                         */
   uint32_t log2_w;    /* L: w = 2^L buckets per row (the pages' c, also m), 0..31        */
   uint32_t log2_part; /* K: 0..L, see above                                            */
-  uint32_t reserved;  /* must be 0                                                     */
+  uint32_t log2_block; /* bitmap granularity B = 2^log2_block elements per bit, 0..16;
+                          0 (the s2r_params_from_seed default) = one bit per element.
+                          Section 3.1 sizes the bitmap by embedding rows or gradient
+                          blocks: a block's bit is set if any of its elements is non-zero,
+                          and decoding queries every element of every set block.       */
   uint64_t pA, pB;
   uint64_t hA[S2R_MAX_ROWS], hB[S2R_MAX_ROWS];
   uint64_t sA[S2R_MAX_ROWS], sB[S2R_MAX_ROWS];
 } s2r_params;
 
 /* Fill *out from a 64-bit seed: SplitMix64 (Steele, Lea & Flood 2014) seeded with `seed`
- * yields pA, pB, then hA[j], hB[j], sA[j], sB[j] for j = 0..d-1.  Pure host code.
+ * yields pA, pB, then hA[j], hB[j], sA[j], sB[j] for j = 0..d-1; log2_block = 0 (set it
+ * afterwards for a block-granular bitmap).  Pure host code.
  * Errors: S2R_ERR_NULL (out), S2R_ERR_DIM (d, log2_w or log2_part out of range). */
 s2r_status s2r_params_from_seed(uint64_t seed, uint32_t d, uint32_t log2_w, uint32_t log2_part,
                                 s2r_params* out);
@@ -87,8 +95,12 @@ s2r_status s2r_params_from_seed(uint64_t seed, uint32_t d, uint32_t log2_w, uint
  * budget of the partitioned path; pure host code. */
 uint32_t s2r_default_log2_part(uint32_t d, uint32_t log2_w);
 
-/* ceil(n / 64): uint64 words per bitmap. */
+/* ceil(n / 64): uint64 words of an element-granular bitmap. */
 uint64_t s2r_bitmap_words(uint64_t n);
+
+/* ceil(ceil(n / 2^log2_block) / 64): uint64 words of a bitmap of n elements at granularity
+ * 2^log2_block (the size of every bitmap argument below, with log2_block from the params). */
+uint64_t s2r_block_bitmap_words(uint64_t n, uint32_t log2_block);
 
 /* Bytes of device workspace s2r_encode needs for W workers of n elements with list
  * capacity `cap` per worker (0 if the arguments are invalid). */
@@ -97,7 +109,7 @@ size_t s2r_encode_workspace_bytes(const s2r_params* p, uint32_t W, uint64_t n, u
 /* Compression of W workers' gradients in one call (Section 3.1; Algorithm 1, steps before
  * the AllReduce).
  *   grad      [W][ld] fp32, row k = worker k; 16-byte aligned, ld % 4 == 0, ld >= n.
- *   bitmaps   [W][s2r_bitmap_words(n)] uint64 out.
+ *   bitmaps   [W][s2r_block_bitmap_words(n, p->log2_block)] uint64 out.
  *   sketches  [W][d][w] fp32 out (fully overwritten; need not be initialised).
  *   idx, val  [W][cap] out: worker k's non-zero indices in ascending order and their
  *             exact fp32 values (the compacted Sparse(g_k)); may be NULL only if cap == 0.
@@ -120,8 +132,8 @@ s2r_status s2r_encode(const s2r_params* p, uint32_t W, const float* grad, uint64
 /* Aggregation (Section 3.1; the AllReduce of Algorithm 1) of W workers on one GPU:
  *   sketch_out[c] = sum_{k=0..W-1} sketches[k][c]   (fp32, added in order k = 0, 1, ...)
  *   bitmap_out[q] = OR_k bitmaps[k][q]
- * sketches [W][d][w] and bitmaps [W][s2r_bitmap_words(n)] in, sketch_out [d][w] and
- * bitmap_out [words] out.  sketch_out may equal `sketches` and bitmap_out may equal
+ * sketches [W][d][w] and bitmaps [W][words] in, sketch_out [d][w] and bitmap_out [words]
+ * out, words = s2r_block_bitmap_words(n, p->log2_block).  sketch_out may equal `sketches` and bitmap_out may equal
  * `bitmaps` (in place into worker 0's slot); other overlaps are not allowed.
  * Errors: S2R_ERR_NULL, S2R_ERR_DIM, S2R_ERR_ALIGN (sketch pointers not 4-byte aligned or
  * bitmap pointers not 8-byte aligned), S2R_ERR_HIP. */
@@ -135,10 +147,12 @@ s2r_status s2r_reduce(const s2r_params* p, uint32_t W, uint64_t n, const uint64_
 size_t s2r_decode_workspace_bytes(const s2r_params* p, uint64_t n, uint64_t max_set);
 
 /* Decompression (Section 3.1; the query loop of Algorithm 1):
- *   out[i] = median_j s_j(i) * sketch[j][h_j(i)]  if bit i of bitmap is set,
+ *   out[i] = median_j s_j(i) * sketch[j][h_j(i)]  if the bit of i's block is set,
  *   out[i] = +0.0                                 otherwise,           for i < n.
  * For even d the median is the mean of the two middle values, rounded once to fp32.
- * bitmap [s2r_bitmap_words(n)] uint64 (bits >= n are ignored), sketch [d][w] fp32,
+ * "Set bits" below count the elements i < n of set blocks.
+ * bitmap [s2r_block_bitmap_words(n, p->log2_block)] uint64 (bits of blocks at or beyond
+ * ceil(n/B) are ignored), sketch [d][w] fp32,
  * out [n] fp32, 16-byte aligned.  Must use the same params as the encode that produced
  * the sketch.  out may not overlap the inputs.
  * Paths: with workspace == NULL (or ws_bytes == 0) every set bit gathers its d cells from

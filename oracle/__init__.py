@@ -32,7 +32,7 @@ class OrcParams(ctypes.Structure):
         ("d", ctypes.c_uint32),
         ("log2_w", ctypes.c_uint32),
         ("log2_part", ctypes.c_uint32),
-        ("pad", ctypes.c_uint32),
+        ("log2_block", ctypes.c_uint32),
         ("pA", ctypes.c_uint64),
         ("pB", ctypes.c_uint64),
         ("hA", ctypes.c_uint64 * MAX_ROWS),
@@ -49,7 +49,7 @@ class OrcParams(ctypes.Structure):
         d = self.d
         return {
             "d": d, "log2_w": self.log2_w, "log2_part": self.log2_part,
-            "pA": self.pA, "pB": self.pB,
+            "log2_block": self.log2_block, "pA": self.pA, "pB": self.pB,
             "hA": list(self.hA)[:d], "hB": list(self.hB)[:d],
             "sA": list(self.sA)[:d], "sB": list(self.sB)[:d],
         }
@@ -88,6 +88,8 @@ def _bind(L: ctypes.CDLL) -> ctypes.CDLL:
     L.orc_reduce.restype = None
     L.orc_decode.argtypes = [P(OrcParams), u64, vp, vp, vp, vp, vp, vp, u64]
     L.orc_decode.restype = u64
+    L.orc_bitmap_words.argtypes = [P(OrcParams), u64]
+    L.orc_bitmap_words.restype = u64
     return L
 
 
@@ -136,19 +138,24 @@ def splitmix64(seed: int, count: int) -> list[int]:
     return [lib().orc_splitmix64_next(ctypes.byref(st)) for _ in range(count)]
 
 
-def params_from_seed(seed: int, d: int, log2_w: int, log2_part: int | None = None) -> OrcParams:
+def params_from_seed(seed: int, d: int, log2_w: int, log2_part: int | None = None,
+                     log2_block: int = 0) -> OrcParams:
+    """Hash constants from SplitMix64; log2_block sets the bitmap granularity (one bit per
+    2^log2_block elements)."""
     if log2_part is None:
         log2_part = log2_w
     p = OrcParams()
     rc = lib().orc_params_from_seed(seed, d, log2_w, log2_part, ctypes.byref(p))
     if rc != 0:
         raise ValueError(f"oracle: bad params d={d} log2_w={log2_w} log2_part={log2_part}")
+    p.log2_block = log2_block
     return p
 
 
-def params_from_constants(d, log2_w, log2_part, pA, pB, hA, hB, sA, sB) -> OrcParams:
+def params_from_constants(d, log2_w, log2_part, pA, pB, hA, hB, sA, sB,
+                          log2_block: int = 0) -> OrcParams:
     p = OrcParams()
-    p.d, p.log2_w, p.log2_part = d, log2_w, log2_part
+    p.d, p.log2_w, p.log2_part, p.log2_block = d, log2_w, log2_part, log2_block
     p.pA, p.pB = pA, pB
     for j in range(d):
         p.hA[j], p.hB[j], p.sA[j], p.sB[j] = hA[j], hB[j], sA[j], sB[j]
@@ -173,7 +180,13 @@ def hash_keys(p: OrcParams, keys: np.ndarray):
 
 
 def words(n: int) -> int:
+    """uint64 words of an element-granular bitmap of n bits."""
     return (n + 63) // 64
+
+
+def bitmap_words(p: OrcParams, n: int) -> int:
+    """uint64 words of the bitmap for n elements at p's granularity."""
+    return int(lib().orc_bitmap_words(ctypes.byref(p), n))
 
 
 def encode_dense(p: OrcParams, g: np.ndarray, cap: int | None = None):
@@ -181,7 +194,7 @@ def encode_dense(p: OrcParams, g: np.ndarray, cap: int | None = None):
     g = np.ascontiguousarray(g, dtype=np.float32)
     n = g.size
     cap = n if cap is None else cap
-    bm = np.empty(words(n), dtype=np.uint64)
+    bm = np.empty(bitmap_words(p, n), dtype=np.uint64)
     S = np.empty((p.d, p.w), dtype=np.float64)
     A = np.empty((p.d, p.w), dtype=np.float64)
     idx = np.empty(max(cap, 1), dtype=np.uint32)
@@ -200,7 +213,7 @@ def encode_sparse(p: OrcParams, idx: np.ndarray, val: np.ndarray, n: int):
     """Compression from Sparse(g) (index, value) pairs.  Returns dict(bitmap, S, A)."""
     idx = np.ascontiguousarray(idx, dtype=np.uint32)
     val = np.ascontiguousarray(val, dtype=np.float32)
-    bm = np.empty(words(n), dtype=np.uint64)
+    bm = np.empty(bitmap_words(p, n), dtype=np.uint64)
     S = np.empty((p.d, p.w), dtype=np.float64)
     A = np.empty((p.d, p.w), dtype=np.float64)
     rc = lib().orc_encode_sparse(ctypes.byref(p), _ptr(idx), _ptr(val), idx.size, n,
@@ -227,13 +240,19 @@ def reduce(bitmaps: np.ndarray, S: np.ndarray, A: np.ndarray):
 
 
 def decode(p: OrcParams, n: int, bitmap: np.ndarray, S: np.ndarray, A: np.ndarray | None = None):
-    """Sparse decode: (idx u32, val f64, tol f64) over the set bits < n, ascending."""
+    """Sparse decode: (idx u32, val f64, tol f64) over the elements < n whose block bit is
+    set, ascending."""
     bitmap = np.ascontiguousarray(bitmap, dtype=np.uint64)
     S = np.ascontiguousarray(S, dtype=np.float64)
     A = np.abs(S) if A is None else np.ascontiguousarray(A, dtype=np.float64)
-    nb = bitmap[: words(n)]
-    # the number of set bits below n bounds the output
-    cap = int(np.unpackbits(nb.view(np.uint8), bitorder="little")[:n].sum()) if n else 0
+    B = 1 << p.log2_block
+    nblocks = (n + B - 1) // B
+    nb = bitmap[: bitmap_words(p, n)]
+    # the elements of the set blocks below n bound the output
+    cap = 0
+    if n:
+        setb = np.flatnonzero(np.unpackbits(nb.view(np.uint8), bitorder="little")[:nblocks])
+        cap = int(setb.size) * B - (B * nblocks - n if nblocks - 1 in setb else 0)
     out_idx = np.empty(max(cap, 1), dtype=np.uint32)
     out_val = np.empty(max(cap, 1), dtype=np.float64)
     out_tol = np.empty(max(cap, 1), dtype=np.float64)

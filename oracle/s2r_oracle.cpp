@@ -15,7 +15,11 @@
 //     s_j(i) * S[j, h_j(i)].
 //
 // Readings taken where the pages leave a step open (each also listed in the design notes):
-//   * one bitmap bit per gradient element (block size 1);
+//   * one bitmap bit per block of 2^log2_block consecutive elements (the pages give the
+//     bitmap one entry per embedding row or gradient block); log2_block = 0 is one bit per
+//     element.
+//     A block's bit is set when any of its elements is non-zero, and decoding queries every
+//     element of every set block;
 //   * "non-zero" is the bit test (bits(x) & 0x7fffffff) != 0: +0 and -0 are zero;
 //   * hashes are multiply-add-shift (Dietzfelbinger 1996) on the element index with
 //     64-bit constants drawn from SplitMix64 (Steele, Lea & Flood 2014);
@@ -44,7 +48,7 @@ struct orc_params {
   uint32_t d;          // rows (the pages' r)
   uint32_t log2_w;     // L: w = 2^L buckets per row (the pages' c, also m)
   uint32_t log2_part;  // K: low bucket bits hashed per row; the high L-K bits are shared
-  uint32_t pad;
+  uint32_t log2_block;  // bitmap granularity: one bit per 2^log2_block elements
   uint64_t pA, pB;                 // shared partition hash constants
   uint64_t hA[ORC_MAX_ROWS], hB[ORC_MAX_ROWS];  // per-row bucket hash constants
   uint64_t sA[ORC_MAX_ROWS], sB[ORC_MAX_ROWS];  // per-row sign hash constants
@@ -132,23 +136,34 @@ static void insert(const orc_params* p, uint32_t i, float g, double* S, double* 
   }
 }
 
+// Bitmap granularity (Section 3.1, "Compressing Sparse Gradient": one bitmap entry per
+// embedding row or gradient block): element i belongs to block i >> log2_block.
+static uint64_t block_of(const orc_params* p, uint64_t i) { return i >> p->log2_block; }
+
+// ceil(ceil(n / 2^log2_block) / 64) words: bit b = bit (b%64) of word b/64.
+uint64_t orc_bitmap_words(const orc_params* p, uint64_t n) {
+  const uint64_t blocks = (n + (1ull << p->log2_block) - 1) >> p->log2_block;
+  return (blocks + 63) / 64;
+}
+
 // Compression of one worker's dense gradient g[0..n) (Section 3.1, Algorithm 1):
-// initialise bitmap and table, set bit i of the bitmap for every non-zero, list the
+// initialise bitmap and table, set the bit of the block of every non-zero, list the
 // non-zeros in ascending index order, and insert each into every row of the sketch.
-// bitmap: ceil(n/64) words, bit i = bit (i%64) of word i/64.  S, A: d*w doubles.
+// bitmap: orc_bitmap_words(p, n) words.  S, A: d*w doubles.
 // idx/val receive at most `cap` entries; *nnz receives the exact count.
 int orc_encode_dense(const orc_params* p, const float* g, uint64_t n, uint64_t* bitmap,
                      double* S, double* A, uint32_t* idx, float* val, uint64_t cap,
                      uint64_t* nnz) {
   if (n >= (1ull << 32)) return 2;
-  uint64_t words = (n + 63) / 64, cells = (uint64_t)p->d << p->log2_w;
+  uint64_t words = orc_bitmap_words(p, n), cells = (uint64_t)p->d << p->log2_w;
   std::memset(bitmap, 0, words * 8);
   std::memset(S, 0, cells * 8);
   std::memset(A, 0, cells * 8);
   uint64_t count = 0;
   for (uint64_t i = 0; i < n; ++i) {
     if (!is_nonzero(g[i])) continue;
-    bitmap[i / 64] |= 1ull << (i % 64);
+    const uint64_t b = block_of(p, i);
+    bitmap[b / 64] |= 1ull << (b % 64);
     if (count < cap) {
       idx[count] = (uint32_t)i;
       val[count] = g[i];
@@ -165,14 +180,15 @@ int orc_encode_dense(const orc_params* p, const float* g, uint64_t n, uint64_t* 
 int orc_encode_sparse(const orc_params* p, const uint32_t* idx, const float* val,
                       uint64_t k, uint64_t n, uint64_t* bitmap, double* S, double* A) {
   if (n >= (1ull << 32)) return 2;
-  uint64_t words = (n + 63) / 64, cells = (uint64_t)p->d << p->log2_w;
+  uint64_t words = orc_bitmap_words(p, n), cells = (uint64_t)p->d << p->log2_w;
   std::memset(bitmap, 0, words * 8);
   std::memset(S, 0, cells * 8);
   std::memset(A, 0, cells * 8);
   for (uint64_t t = 0; t < k; ++t) {
     if (idx[t] >= n) return 3;
     if (!is_nonzero(val[t])) continue;
-    bitmap[idx[t] / 64] |= 1ull << (idx[t] % 64);
+    const uint64_t b = block_of(p, idx[t]);
+    bitmap[b / 64] |= 1ull << (b % 64);
     insert(p, idx[t], val[t], S, A);
   }
   return 0;
@@ -200,8 +216,8 @@ void orc_reduce(uint32_t W, uint64_t cells, uint64_t words, const uint64_t* bitm
 }
 
 // Decompression (Section 3.1, "Decompressing Sparse Gradient"; Algorithm 1 query loop):
-// recover the indices from the bitmap (bits >= n ignored) and, for each, take the median
-// over rows of s_j(i) * S[j, h_j(i)].  Output is sparse: ascending indices with value and
+// recover the indices from the bitmap -- every element i < n whose block bit is set -- and,
+// for each, take the median over rows of s_j(i) * S[j, h_j(i)].  Output is sparse: ascending indices with value and
 // tolerance tol(i) = 1e-5 * max_j A[j, h_j(i)] + 1e-12.  Returns the number of set bits;
 // at most `cap` entries are written.
 uint64_t orc_decode(const orc_params* p, uint64_t n, const uint64_t* bitmap, const double* S,
@@ -212,7 +228,8 @@ uint64_t orc_decode(const orc_params* p, uint64_t n, const uint64_t* bitmap, con
   std::vector<double> est(d);
   uint64_t count = 0;
   for (uint64_t i = 0; i < n; ++i) {
-    if (!((bitmap[i / 64] >> (i % 64)) & 1ull)) continue;
+    const uint64_t b = block_of(p, i);
+    if (!((bitmap[b / 64] >> (b % 64)) & 1ull)) continue;
     double amax = 0.0;
     for (uint32_t j = 0; j < d; ++j) {
       uint64_t cell = (uint64_t)j * w + orc_bucket(p, j, (uint32_t)i);

@@ -31,12 +31,12 @@ def say(msg: str) -> None:
     sys.stdout.flush()
 
 
-def params_pair(seed: int, d: int, L: int, K: int | None = None):
+def params_pair(seed: int, d: int, L: int, K: int | None = None, log2_block: int = 0):
     """(library params, oracle params) derived independently from one seed."""
     if K is None:
         K = s2r.s2r_default_log2_part(d, L)
-    p = s2r.s2r_params_from_seed(seed, d, L, K)
-    op = oracle.params_from_seed(seed, d, L, K)
+    p = s2r.s2r_params_from_seed(seed, d, L, K, log2_block=log2_block)
+    op = oracle.params_from_seed(seed, d, L, K, log2_block=log2_block)
     assert p.as_dict() == op.as_dict()
     return p, op
 
@@ -60,7 +60,7 @@ def run_encode(p, grads: np.ndarray, n: int, cap: int | None = None):
     s2r.s2r_encode(p, W, g, n, ld, buf["bitmaps"], buf["sketches"], buf["idx"], buf["val"], cap,
                    buf["nnz"], buf["workspace"])
     torch.cuda.synchronize()
-    words = s2r.s2r_bitmap_words(n)
+    words = s2r.s2r_block_bitmap_words(n, p.log2_block)
     return {
         "bitmaps": _u64(buf["bitmaps"])[:, :words] if words else np.zeros((W, 0), np.uint64),
         "sketches": buf["sketches"].cpu().numpy(),
@@ -174,3 +174,10 @@ def assert_decode_matches(gpu: np.ndarray, want: np.ndarray, tol: np.ndarray, se
 def bits_of(bitmap: np.ndarray, n: int) -> np.ndarray:
     return np.unpackbits(np.ascontiguousarray(bitmap).view(np.uint8), bitorder="little")[:n] \
         .astype(bool)
+
+
+def set_elements(bitmap: np.ndarray, n: int, log2_block: int) -> np.ndarray:
+    """Elements i < n whose block bit is set (the elements a decode queries)."""
+    B = 1 << log2_block
+    blocks = bits_of(bitmap, (n + B - 1) // B)
+    return np.repeat(blocks, B)[:n]

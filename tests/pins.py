@@ -15,6 +15,9 @@ Each ``pin_*`` function raises AssertionError when the oracle (whichever build t
   * the query as the median over rows of (A_j A_j^T g)(i), taken with numpy.median
     (Section 3.1, "Decompressing Sparse Gradient"; Algorithm 1);
   * exact recovery when a majority of an item's buckets hold no other item;
+  * block-granular bitmaps (one bit per embedding row or gradient block, Section 3.1): the
+    bit of a block is the OR of its elements' non-zero tests, the sketch does not depend
+    on the granularity, and every element of a set block is queried;
   * unbiasedness of the single-row estimate over random hash constants (Theorem 1).
 
 The test modules run every pin against the real oracle and against altered copies of it.
@@ -297,9 +300,62 @@ def pin_unbiased_single_row():
     assert np.abs(errs[:, sup]).mean() > 0.1
 
 
+def _block_bits(g, B):
+    """numpy: one flag per block of B elements (last block ragged), True if any is non-zero."""
+    n = g.size
+    nb = (n + B - 1) // B
+    pad = np.zeros(nb * B, dtype=np.float32)
+    pad[:n] = g
+    return (pad.reshape(nb, B) != 0).any(axis=1)
+
+
+def pin_block_bitmap():
+    """Block bit = OR of the block's non-zero tests (ragged last block included); pad bits 0;
+    list and sketch unchanged by the granularity (zeros add nothing, Section 3.1)."""
+    for (n, lb, seed) in [(200, 2, 31), (333, 3, 32), (1000, 6, 33), (130, 7, 34), (5000, 9, 35)]:
+        B = 1 << lb
+        rng = np.random.Generator(np.random.PCG64(seed))
+        g = np.zeros(n, dtype=np.float32)
+        pos = rng.choice(n, size=max(1, n // 25), replace=False)
+        g[pos] = rng.standard_normal(pos.size).astype(np.float32)
+        g[n - 1] = 1.5   # the ragged last block is set
+        g[min(B, n - 1) - 1] = -0.0  # a negative zero sets nothing
+        p = O.params_from_seed(seed, 3, 6, 3, log2_block=lb)
+        e = O.encode_dense(p, g)
+        want = _block_bits(g, B)
+        bits = np.unpackbits(e["bitmap"].view(np.uint8), bitorder="little")
+        assert e["bitmap"].size == (want.size + 63) // 64
+        assert np.array_equal(bits[: want.size].astype(bool), want)
+        assert not bits[want.size:].any()
+        nz = np.flatnonzero(g != 0)
+        assert e["nnz"] == nz.size and np.array_equal(e["idx"], nz.astype(np.uint32))
+        mats = _mapping_matrices(p, n)
+        for j in range(p.d):
+            assert np.array_equal(e["S"][j], mats[j].T @ g.astype(np.float64))
+
+
+def pin_block_query():
+    """Every element of a set block -- zeros inside it too -- decodes to
+    median_j (A_j A_j^T g)(i); elements of clear blocks decode to 0 (Section 3.1)."""
+    n = 90
+    for (d, lb) in [(1, 1), (3, 2), (4, 3), (5, 4)]:
+        B = 1 << lb
+        p = O.params_from_seed(700 + d, d, 4, 2, log2_block=lb)
+        g = _int_grad(n, 0.08, 40 + d)
+        e = O.encode_dense(p, g)
+        out, tol = O.decode_dense(p, n, e["bitmap"], e["S"], e["A"])
+        mats = _mapping_matrices(p, n)
+        est = np.stack([mats[j] @ (mats[j].T @ g.astype(np.float64)) for j in range(d)])
+        inset = np.repeat(_block_bits(g, B), B)[:n]
+        assert inset.sum() > (g != 0).sum()  # some zeros lie inside set blocks
+        want = np.where(inset, np.median(est, axis=0), 0.0)
+        assert np.array_equal(out, want), (d, lb)
+        assert np.array_equal(tol > 0, inset)
+
+
 ALL_PINS = [
     pin_splitmix64, pin_params_draw_order, pin_hash_closed_forms, pin_hash_statistics,
     pin_bitmap_and_list, pin_sketch_projection, pin_zeros_do_not_matter, pin_linearity,
     pin_signed_permutation, pin_reduce, pin_median_query, pin_exact_recovery,
-    pin_unbiased_single_row,
+    pin_unbiased_single_row, pin_block_bitmap, pin_block_query,
 ]

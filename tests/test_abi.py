@@ -91,7 +91,7 @@ def test_encode_argument_errors(s2r):
     need = s2r.s2r_encode_workspace_bytes(p, 2, 1000, 1000)
     assert _encode(s2r, p, ws_bytes=need - 1) == s2r.S2R_ERR_WORKSPACE
     bad = s2r.s2r_params_from_seed(3, 3, 10, 10)
-    bad.reserved = 1
+    bad.log2_block = 17                                            # beyond S2R_MAX_LOG2_BLOCK
     assert _encode(s2r, bad) == s2r.S2R_ERR_DIM
     bad = s2r.s2r_params_from_seed(3, 3, 10, 10)
     bad.log2_part = 11
@@ -124,3 +124,22 @@ def test_binding_refuses_without_library(s2r, tmp_path, monkeypatch):
     monkeypatch.setattr(s2r, "_lib", None)
     with pytest.raises(ImportError):
         s2r.lib()
+
+
+def test_block_bitmap_words(s2r):
+    """ceil(ceil(n / 2^lb) / 64), computed by the library on the host."""
+    for n in (0, 1, 63, 64, 65, 4095, 4096, 4097, 137_084_928, 25_557_032, 2**32 - 1):
+        for lb in (0, 1, 5, 6, 8, 9, 12, 16):
+            B = 1 << lb
+            assert s2r.s2r_block_bitmap_words(n, lb) == ((n + B - 1) // B + 63) // 64, (n, lb)
+    assert s2r.s2r_block_bitmap_words(1000, 0) == s2r.s2r_bitmap_words(1000)
+
+
+def test_block_workspace_grows(s2r):
+    """A block-granular encode keeps the element bitmaps in its workspace."""
+    p = s2r.s2r_params_from_seed(3, 3, 10, 10)
+    q = s2r.s2r_params_from_seed(3, 3, 10, 10, log2_block=9)
+    a = s2r.s2r_encode_workspace_bytes(p, 2, 100_000, 1000)
+    b = s2r.s2r_encode_workspace_bytes(q, 2, 100_000, 1000)
+    assert b >= a + 2 * s2r.s2r_bitmap_words(100_000) * 8
+

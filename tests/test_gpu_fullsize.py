@@ -9,6 +9,8 @@ Every output is compared, not a sample:
   * merged bitmap: bit-exact;
   * decoded values at every set bit within tol(i), every clear bit exactly +0.0.
 The oracle compresses each worker from Sparse(g_k), the input form of Algorithm 1.
+The block-granular cases use the workloads' own row or block size as the bitmap block
+(embedding rows of 512, ResNet-50 blocks of 256, Transformer blocks of 512).
 """
 import gc
 
@@ -26,12 +28,12 @@ gp = pytest.importorskip("gpu_path")
 
 
 @pytest.mark.timeout(900)
-@pytest.mark.parametrize("cid", [1, 2, 3, 4])
-def test_fullsize_pipeline(cid):
+@pytest.mark.parametrize("cid,lb", [(1, 0), (2, 0), (3, 0), (4, 0), (1, 9), (2, 8), (3, 9)])
+def test_fullsize_pipeline(cid, lb):
     wl = WL.workload(cid)
     dev = gp.DEV
-    gp.say(f"fullsize {wl.name}: W={wl.W} N={wl.N} d={wl.d} w=2^{wl.log2_w}")
-    p, op = gp.params_pair(wl.hash_seed, wl.d, wl.log2_w)
+    gp.say(f"fullsize {wl.name}: W={wl.W} N={wl.N} d={wl.d} w=2^{wl.log2_w} B=2^{lb}")
+    p, op = gp.params_pair(wl.hash_seed, wl.d, wl.log2_w, log2_block=lb)
     ld = (wl.N + 3) // 4 * 4
     grad = torch.zeros((wl.W, ld), dtype=torch.float32, device=dev)
     sparse = []
@@ -41,9 +43,10 @@ def test_fullsize_pipeline(cid):
                             torch.from_numpy(val).to(dev))
         sparse.append((idx, val))
     cap = max(x[0].size for x in sparse)
-    max_set = min(wl.N, sum(x[0].size for x in sparse))
+    # the merged query set holds at most every worker's touched blocks
+    max_set = min(wl.N, sum(np.unique(x[0] >> lb).size << lb for x in sparse))
     buf = s2r.alloc_encode_buffers(p, wl.W, wl.N, cap, dev)
-    words = s2r.s2r_bitmap_words(wl.N)
+    words = s2r.s2r_block_bitmap_words(wl.N, lb)
     bm = torch.empty(words, dtype=torch.int64, device=dev)
     sk = torch.empty((wl.d, wl.w), dtype=torch.float32, device=dev)
     out = torch.full((wl.N,), float("nan"), dtype=torch.float32, device=dev)
@@ -85,6 +88,7 @@ def test_fullsize_pipeline(cid):
     got = out.cpu().numpy()
     setmask = np.zeros(wl.N, dtype=bool)
     setmask[oi] = True
+    assert np.array_equal(setmask, gp.set_elements(obm, wl.N, lb))
     assert np.all(got[~setmask].view(np.uint32) == 0), "clear bits must decode to +0.0"
     g = got[oi].astype(np.float64)
     bad = ~(np.abs(g - ov) <= ot)

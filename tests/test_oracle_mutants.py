@@ -23,8 +23,13 @@ MUTANTS = {
                         "uint64_t low64 = (uint64_t)full - c;\n  return (low64 >> (64 - bits)) + (c >> (64 - bits)) & ((1ull << bits) - 1);"),
     "partition_not_shifted": ("return (uint32_t)((part << K) | low);", "return (uint32_t)(part | low);"),
     "sign_uses_bucket_constant": ("mas_top(p->sA[j], p->sB[j], i, 1)", "mas_top(p->hA[j], p->sB[j], i, 1)"),
-    "bitmap_bit_off_by_one": ("bitmap[i / 64] |= 1ull << (i % 64);\n    if (count < cap)",
-                              "bitmap[i / 64] |= 1ull << ((i + 1) % 64);\n    if (count < cap)"),
+    "bitmap_bit_off_by_one": ("bitmap[b / 64] |= 1ull << (b % 64);\n    if (count < cap)",
+                              "bitmap[b / 64] |= 1ull << ((b + 1) % 64);\n    if (count < cap)"),
+    "block_bit_from_element_index": ("const uint64_t b = block_of(p, i);\n    bitmap[b / 64]",
+                                     "const uint64_t b = i;\n    bitmap[b / 64]"),
+    "block_rounds_up": ("return i >> p->log2_block; }", "return (i + 1) >> p->log2_block; }"),
+    "query_element_bits_only": ("const uint64_t b = block_of(p, i);\n    if (!((bitmap",
+                                "const uint64_t b = i;\n    if (!((bitmap"),
     "negative_zero_counts": ("return (u & 0x7FFFFFFFu) != 0;", "return u != 0;"),
     "median_odd_takes_max": ("(d % 2) ? est[(d - 1) / 2]", "(d % 2) ? est[d - 1]"),
     "median_even_takes_lower": ("0.5 * (est[d / 2 - 1] + est[d / 2])", "est[d / 2 - 1]"),
