@@ -88,6 +88,8 @@ def _bind(L: ctypes.CDLL) -> ctypes.CDLL:
     L.orc_reduce.restype = None
     L.orc_decode.argtypes = [P(OrcParams), u64, vp, vp, vp, vp, vp, vp, u64]
     L.orc_decode.restype = u64
+    L.orc_topk_ef.argtypes = [vp, vp, u64, u64, u64, vp, vp, vp]
+    L.orc_topk_ef.restype = ctypes.c_int
     L.orc_bitmap_words.argtypes = [P(OrcParams), u64]
     L.orc_bitmap_words.restype = u64
     return L
@@ -270,3 +272,23 @@ def decode_dense(p: OrcParams, n: int, bitmap, S, A=None):
     out[i] = v
     tol[i] = t
     return out, tol
+
+
+def topk_ef(grad: np.ndarray, residual: np.ndarray | None, block: int, K: int):
+    """Block-wise Top-K with error feedback on one worker's gradient.  Returns
+    dict(out, residual (None without error feedback), selected (uint64 bitmap of kept blocks),
+    norm2 (fp64 squared block norms))."""
+    grad = np.ascontiguousarray(grad, dtype=np.float32)
+    n = grad.size
+    nb = -(-n // block)
+    res = None if residual is None else np.array(residual, dtype=np.float32, copy=True)
+    out = np.empty(max(n, 1), dtype=np.float32)
+    sel = np.empty(max((nb + 63) // 64, 1), dtype=np.uint64)
+    norm2 = np.empty(max(nb, 1), dtype=np.float64)
+    rc = lib().orc_topk_ef(_ptr(grad), None if res is None else _ptr(res), n, block, K, _ptr(out),
+                           _ptr(sel), _ptr(norm2))
+    if rc:
+        raise ValueError(f"oracle topk_ef failed rc={rc}")
+    return {"out": out[:n], "residual": res, "selected": sel[: (nb + 63) // 64],
+            "norm2": norm2[:nb]}
+

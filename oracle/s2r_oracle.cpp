@@ -248,4 +248,41 @@ uint64_t orc_decode(const orc_params* p, uint64_t n, const uint64_t* bitmap, con
   return count;
 }
 
+// ---------------------------------------------------------------------------------
+// Block-wise Top-K sparsification with error feedback, the step that produces the sparse
+// gradients the method compresses (Section 2.2: l2 norm of every block, the K largest
+// blocks are kept; Appendix A.2: the error sequence e_{t+1} = g_t - C(g_t) with
+// g_t = gradient_t + e_t).  Readings: the residual is taken against the Top-K output
+// itself, e_{t+1} = g_t - sparse(g_t); blocks are ordered by squared norm, larger first,
+// then by lower block id; the squared norm is the plain fp64 sum of the squares of the
+// block's fp32 elements in index order, and g_t = gradient_t + e_t is one fp32 addition.
+//   grad [n], residual [n] (in/out; NULL = no error feedback), out [n] = sparse(g),
+//   sel [ceil(nb/64)] bitmap of the kept blocks, norm2 [nb]; nb = ceil(n / block).
+int orc_topk_ef(const float* grad, float* residual, uint64_t n, uint64_t block, uint64_t K,
+                float* out, uint64_t* sel, double* norm2) {
+  if (block == 0) return 1;
+  const uint64_t nb = (n + block - 1) / block;
+  std::vector<float> g(n);
+  for (uint64_t i = 0; i < n; ++i) g[i] = residual ? grad[i] + residual[i] : grad[i];
+  for (uint64_t q = 0; q < nb; ++q) {
+    double s = 0.0;
+    for (uint64_t i = q * block; i < n && i < (q + 1) * block; ++i) s += (double)g[i] * (double)g[i];
+    norm2[q] = s;
+  }
+  std::vector<uint64_t> order(nb);
+  for (uint64_t q = 0; q < nb; ++q) order[q] = q;
+  std::sort(order.begin(), order.end(), [&](uint64_t a, uint64_t b) {
+    return norm2[a] > norm2[b] || (norm2[a] == norm2[b] && a < b);
+  });
+  std::memset(sel, 0, ((nb + 63) / 64) * 8);
+  for (uint64_t r = 0; r < K && r < nb; ++r) sel[order[r] / 64] |= 1ull << (order[r] % 64);
+  for (uint64_t i = 0; i < n; ++i) {
+    const uint64_t q = i / block;
+    const bool kept = (sel[q / 64] >> (q % 64)) & 1ull;
+    out[i] = kept ? g[i] : 0.0f;
+    if (residual) residual[i] = kept ? 0.0f : g[i];
+  }
+  return 0;
+}
+
 }  // extern "C"

@@ -18,6 +18,9 @@ Each ``pin_*`` function raises AssertionError when the oracle (whichever build t
   * block-granular bitmaps (one bit per embedding row or gradient block, Section 3.1): the
     bit of a block is the OR of its elements' non-zero tests, the sketch does not depend
     on the granularity, and every element of a set block is queried;
+  * block-wise Top-K with error feedback (Section 2.2; Appendix A.2): numpy's block norms
+    and ordering, out + residual = g, the kept mass bound of Theorem 2's proof, and the
+    telescoping sum of the error sequence;
   * unbiasedness of the single-row estimate over random hash constants (Theorem 1).
 
 The test modules run every pin against the real oracle and against altered copies of it.
@@ -353,9 +356,88 @@ def pin_block_query():
         assert np.array_equal(tol > 0, inset)
 
 
+def _topk_numpy(g, block, K):
+    """numpy: squared block norms (fp64), kept blocks by (norm desc, id asc), out, residual."""
+    n = g.size
+    nb = -(-n // block)
+    pad = np.zeros(nb * block, dtype=np.float64)
+    pad[:n] = g.astype(np.float64)
+    norm2 = (pad.reshape(nb, block) ** 2).sum(axis=1)
+    order = np.lexsort((np.arange(nb), -norm2))
+    kept = np.zeros(nb, dtype=bool)
+    kept[order[:K]] = True
+    em = np.repeat(kept, block)[:n]
+    return norm2, kept, np.where(em, g, np.float32(0)), np.where(em, np.float32(0), g)
+
+
+def pin_topk_numpy():
+    """Integer-valued data (every square and sum exact): norms, kept set with planted ties
+    (identical blocks, zero blocks), out and residual equal numpy's (Section 2.2)."""
+    for (n, block, seed) in [(1000, 10, 1), (1001, 16, 2), (257, 256, 3), (5000, 64, 4), (7, 3, 5)]:
+        rng = np.random.Generator(np.random.PCG64(seed))
+        nb = -(-n // block)
+        grad = rng.integers(-8, 9, size=n).astype(np.float32)
+        grad[rng.random(n) < 0.5] = 0
+        if nb >= 4:  # a tie between two identical blocks and a run of zero blocks
+            grad[block:2 * block] = grad[:block]
+            grad[2 * block:min(n, 4 * block)] = 0
+        res = rng.integers(-2, 3, size=n).astype(np.float32)
+        for K in sorted({0, 1, nb // 3, nb // 2, nb - 1, nb, nb + 5}):
+            if K < 0:
+                continue
+            o = O.topk_ef(grad, res, block, K)
+            g = grad + res
+            norm2, kept, out, resid = _topk_numpy(g, block, K)
+            assert np.array_equal(o["norm2"], norm2), (n, block, K)
+            bits = np.unpackbits(o["selected"].view(np.uint8), bitorder="little")
+            assert np.array_equal(bits[:nb].astype(bool), kept), (n, block, K)
+            assert not bits[nb:].any()
+            assert np.array_equal(o["out"], out) and np.array_equal(o["residual"], resid)
+            o2 = O.topk_ef(grad, None, block, K)  # no error feedback: g = grad
+            _, kept2, out2, _ = _topk_numpy(grad, block, K)
+            assert o2["residual"] is None and np.array_equal(o2["out"], out2)
+
+
+def pin_topk_identities():
+    """Float data: out + residual = g exactly with disjoint supports; the kept squared mass
+    is at least K/b of the total (the bound in the proof of Theorem 2)."""
+    rng = np.random.Generator(np.random.PCG64(21))
+    n, block = 20_000, 100
+    nb = n // block
+    grad = (rng.standard_normal(n) * rng.exponential(1.0, size=n)).astype(np.float32)
+    res = (rng.standard_normal(n) * 0.1).astype(np.float32)
+    g = grad + res
+    for K in (1, 7, 50, 199):
+        o = O.topk_ef(grad, res, block, K)
+        assert np.array_equal(o["out"] + o["residual"], g)
+        assert not np.any((o["out"] != 0) & (o["residual"] != 0))
+        kept_mass = float((o["out"].astype(np.float64) ** 2).sum())
+        assert kept_mass >= K / nb * float((g.astype(np.float64) ** 2).sum()) * (1 - 1e-12)
+        assert np.allclose(o["norm2"], _topk_numpy(g, block, K)[0], rtol=1e-12, atol=0)
+
+
+def pin_topk_error_feedback():
+    """Over T steps with the residual carried, sum_t out_t + e_T = sum_t gradient_t exactly
+    (integer data): the error sequence loses nothing (Appendix A.2)."""
+    rng = np.random.Generator(np.random.PCG64(31))
+    n, block, K, T = 3000, 30, 9, 12
+    e = np.zeros(n, dtype=np.float32)
+    sent = np.zeros(n, dtype=np.float64)
+    total = np.zeros(n, dtype=np.float64)
+    for t in range(T):
+        grad = rng.integers(-5, 6, size=n).astype(np.float32)
+        o = O.topk_ef(grad, e, block, K)
+        e = o["residual"]
+        sent += o["out"]
+        total += grad
+        assert int((o["out"] != 0).sum()) <= K * block
+    assert np.array_equal(sent + e, total)
+
+
 ALL_PINS = [
     pin_splitmix64, pin_params_draw_order, pin_hash_closed_forms, pin_hash_statistics,
     pin_bitmap_and_list, pin_sketch_projection, pin_zeros_do_not_matter, pin_linearity,
     pin_signed_permutation, pin_reduce, pin_median_query, pin_exact_recovery,
-    pin_unbiased_single_row, pin_block_bitmap, pin_block_query,
+    pin_unbiased_single_row, pin_block_bitmap, pin_block_query, pin_topk_numpy,
+    pin_topk_identities, pin_topk_error_feedback,
 ]

@@ -28,6 +28,13 @@ MUTANTS = {
     "block_bit_from_element_index": ("const uint64_t b = block_of(p, i);\n    bitmap[b / 64]",
                                      "const uint64_t b = i;\n    bitmap[b / 64]"),
     "block_rounds_up": ("return i >> p->log2_block; }", "return (i + 1) >> p->log2_block; }"),
+    "topk_tie_prefers_higher_id": ("(norm2[a] == norm2[b] && a < b)", "(norm2[a] == norm2[b] && a > b)"),
+    "topk_norm_of_abs": ("s += (double)g[i] * (double)g[i];", "s += std::fabs((double)g[i]);"),
+    "topk_kept_residual_not_zeroed": ("residual[i] = kept ? 0.0f : g[i];", "residual[i] = g[i];"),
+    "topk_ignores_residual_input": ("g[i] = residual ? grad[i] + residual[i] : grad[i];",
+                                    "g[i] = grad[i];"),
+    "topk_keeps_one_less": ("for (uint64_t r = 0; r < K && r < nb; ++r)",
+                            "for (uint64_t r = 1; r < K && r < nb; ++r)"),
     "query_element_bits_only": ("const uint64_t b = block_of(p, i);\n    if (!((bitmap",
                                 "const uint64_t b = i;\n    if (!((bitmap"),
     "negative_zero_counts": ("return (u & 0x7FFFFFFFu) != 0;", "return u != 0;"),
