@@ -155,6 +155,86 @@ def copy_reference() -> int:
     return 0
 
 
+def topk_stage(args) -> int:
+    """Block-wise Top-K with error feedback on the ResNet-50 workload's dense gradients
+    (W=16, N=25,557,032, blocks of 256, K = 1% of the blocks), residual carried across steps.
+    Algorithmic bytes: 16 per element (read gradient and residual, write output and
+    residual)."""
+    import numpy as np
+    import torch
+
+    import count_sketch_aggregation_amd as s2r
+    import workloads as WL
+
+    if args.gpus != 1:
+        print("bench.py runs on one GPU only", file=sys.stderr)
+        return 2
+    cid, block = 2, 256
+    wl = WL.workload(cid)
+    nb = -(-wl.N // block)
+    K = -(-nb // 100)
+    dev = torch.device("cuda:0")
+    ld = (wl.N + 3) // 4 * 4
+    log(f"topk stage {wl.name}: W={wl.W} N={wl.N} block={block} K={K}")
+    grad = torch.zeros((wl.W, ld), dtype=torch.float32, device=dev)
+    for k in range(wl.W):
+        grad[k, :wl.N] = torch.from_numpy(WL.worker_dense(cid, k)).to(dev)
+    res = torch.zeros_like(grad)
+    out = torch.empty_like(grad)
+    sel = torch.empty((wl.W, (nb + 63) // 64), dtype=torch.int64, device=dev)
+    ws = torch.empty((s2r.s2r_topk_workspace_bytes(wl.W, wl.N, block),), dtype=torch.uint8,
+                     device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        s2r.s2r_topk_ef(wl.W, grad, res, wl.N, ld, block, K, out, sel, ws, stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    t0 = time.perf_counter()
+    ev[0].record(stream)
+    for _ in range(args.steps):
+        step()
+    ev[1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_ev = ev[0].elapsed_time(ev[1]) / args.steps
+    ms_per_step = wall * 1e3 / args.steps
+    alg = 16 * wl.W * wl.N
+    achieved = alg / (ms_ev * 1e-3) / 1e9
+    result = {
+        "metric": "G gradient-elements/s (block-wise Top-K with error feedback)",
+        "value": round(wl.W * wl.N / (ms_per_step * 1e-3) / 1e9, 3),
+        "unit": "G gradient-elements/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": "resnet50_blocktopk dense gradients", "W": wl.W, "N": wl.N,
+                   "block": block, "K": K, "error_feedback": True},
+        "roofline": {"bound": "hbm", "kernel": "s2r_topk_ef", "achieved": round(achieved, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None},
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+        g0 = WL.worker_dense(cid, 0)
+        r0 = np.zeros_like(g0)
+        t0 = time.perf_counter()
+        reps = 0
+        while time.perf_counter() - t0 < 10.0 or reps == 0:
+            o = oracle.topk_ef(g0, r0, block, K)
+            r0 = o["residual"]
+            reps += 1
+        el = time.perf_counter() - t0
+        result["cpu_baseline"] = {
+            "value": round(reps * wl.N / el / 1e9, 6), "unit": "G gradient-elements/s",
+            "cores": 1, "kind": "oracle",
+            "sample": f"{reps} error-feedback steps of worker 0 (N={wl.N}), {el:.1f} s"}
+    print(json.dumps(result), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -167,11 +247,16 @@ def main() -> int:
     ap.add_argument("--block", type=int, default=0, metavar="LOG2_B",
                     help="bitmap granularity: one bit per 2^LOG2_B elements (default 0: per element)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--stage", default="aggregate", choices=["aggregate", "topk"],
+                    help="aggregate: encode+reduce+decode (default); topk: the block-wise Top-K "
+                         "with error feedback that precedes it (ResNet-50 workload)")
     ap.add_argument("--copy-reference", action="store_true",
                     help="run the 1 GiB copy that calibrates the traffic counters, then exit")
     args = ap.parse_args()
     if args.copy_reference:
         return copy_reference()
+    if args.stage == "topk":
+        return topk_stage(args)
 
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the W data-parallel "

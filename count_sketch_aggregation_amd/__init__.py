@@ -94,6 +94,10 @@ def lib() -> ctypes.CDLL:
         L.s2r_decode.restype = st
         L.s2r_hash.argtypes = [P(s2r_params), vp, u64, vp, vp, vp]
         L.s2r_hash.restype = st
+        L.s2r_topk_workspace_bytes.argtypes = [u32, u64, u64]
+        L.s2r_topk_workspace_bytes.restype = sz
+        L.s2r_topk_ef.argtypes = [u32, vp, vp, u64, u64, u64, u64, vp, vp, vp, sz, vp]
+        L.s2r_topk_ef.restype = st
         L.s2r_status_string.argtypes = [st]
         L.s2r_status_string.restype = ctypes.c_char_p
         _lib = L
@@ -194,6 +198,21 @@ def s2r_hash(p: s2r_params, keys, m: int, buckets, signs, stream=None) -> None:
                           _stream(stream)), "s2r_hash")
 
 
+def s2r_topk_workspace_bytes(W: int, n: int, block: int) -> int:
+    return int(lib().s2r_topk_workspace_bytes(W, n, block))
+
+
+def s2r_topk_ef(W: int, grad, residual, n: int, ld: int, block: int, K: int, out, selected,
+                workspace, ws_bytes: int | None = None, stream=None) -> None:
+    """Block-wise Top-K with error feedback (residual may be None: no error feedback;
+    selected may be None)."""
+    if ws_bytes is None:
+        ws_bytes = workspace.numel() * workspace.element_size()
+    _check(lib().s2r_topk_ef(W, _ptr(grad), _ptr(residual), n, ld, block, K, _ptr(out),
+                             _ptr(selected), _ptr(workspace), ws_bytes, _stream(stream)),
+           "s2r_topk_ef")
+
+
 # ---------------------------------------------------------------------------------------
 # allocation helper (torch supplies device memory; no arithmetic here)
 
@@ -226,6 +245,6 @@ __all__ = [
     "s2r_params", "S2RError", "s2r_params_from_seed", "s2r_default_log2_part", "s2r_bitmap_words",
     "s2r_block_bitmap_words",
     "s2r_encode_workspace_bytes", "s2r_encode", "s2r_reduce", "s2r_decode_workspace_bytes",
-    "s2r_decode", "s2r_hash",
+    "s2r_decode", "s2r_hash", "s2r_topk_workspace_bytes", "s2r_topk_ef",
     "alloc_encode_buffers", "status_string", "lib",
 ]

@@ -230,6 +230,26 @@ s2r_status s2r_hash(const s2r_params* p, const uint32_t* keys, uint64_t m, uint3
   return S2R_OK;
 }
 
+size_t s2r_topk_workspace_bytes(uint32_t W, uint64_t n, uint64_t block) {
+  if (W == 0 || block == 0 || n >= (1ull << 32)) return 0;
+  return topk_layout(W, n, block).total;
+}
+
+s2r_status s2r_topk_ef(uint32_t W, const float* grad, float* residual, uint64_t n, uint64_t ld,
+                       uint64_t block, uint64_t K, float* out, uint64_t* selected,
+                       void* workspace, size_t ws_bytes, void* stream) {
+  if (n > 0 && (!grad || !out || !workspace)) return S2R_ERR_NULL;
+  if (W == 0 || W > 65535 || block == 0 || n >= (1ull << 32) || ld < n) return S2R_ERR_DIM;
+  if (ld % 4 != 0 || !aligned(grad, 16) || !aligned(residual, 16) || !aligned(out, 16) ||
+      !aligned(selected, 8) || !aligned(workspace, 16))
+    return S2R_ERR_ALIGN;
+  if (n > 0 && ws_bytes < topk_layout(W, n, block).total) return S2R_ERR_WORKSPACE;
+  if (n > 0 && residual == grad) return S2R_ERR_DIM;
+  S2R_TRY(launch_topk(W, grad, residual, n, ld, block, K, out, selected, workspace,
+                      static_cast<hipStream_t>(stream)));
+  return S2R_OK;
+}
+
 const char* s2r_status_string(s2r_status s) {
   switch (s) {
     case S2R_OK: return "ok";

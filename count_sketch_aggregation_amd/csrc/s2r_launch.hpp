@@ -89,6 +89,16 @@ hipError_t launch_decode(const HashArgs& h, const s2r_params& p, uint64_t n,
                          const uint64_t* bitmap, const float* sketch, float* out,
                          uint64_t max_set, void* workspace, size_t ws_bytes, hipStream_t s);
 
+// Workspace of s2r_topk_ef: fp64 keys [W][nb] and a kept-block bitmap [W][sel_words].
+struct TopkLayout {
+  uint64_t nb, sel_words;
+  size_t off_keys, off_sel, total;
+};
+TopkLayout topk_layout(uint32_t W, uint64_t n, uint64_t block);
+hipError_t launch_topk(uint32_t W, const float* grad, float* residual, uint64_t n, uint64_t ld,
+                       uint64_t block, uint64_t K, float* out, uint64_t* selected,
+                       void* workspace, hipStream_t s);
+
 hipError_t launch_hash(const HashArgs& h, const uint32_t* keys, uint64_t m, uint32_t* buckets,
                        int8_t* signs, hipStream_t s);
 

@@ -15,6 +15,8 @@
  *                  Algorithm 1: for every set bit i, g_hat(i) = median over rows j of
  *                  s_j(i) * S[j, h_j(i)]; every clear bit decodes to +0.0.
  *   s2r_hash    -- the bucket and sign hashes of Algorithm 1 on arbitrary keys (test hook).
+ *   s2r_topk_ef -- Section 2.2 and Appendix A.2: block-wise Top-K sparsification with error
+ *                  feedback, which produces the sparse gradients that s2r_encode compresses.
  *
  * Conventions shared by every call:
  *   - Device arrays are caller-owned device memory (hipMalloc / torch tensors).  The
@@ -173,6 +175,35 @@ s2r_status s2r_decode(const s2r_params* p, uint64_t n, const uint64_t* bitmap,
  * Errors: S2R_ERR_NULL, S2R_ERR_DIM, S2R_ERR_HIP. */
 s2r_status s2r_hash(const s2r_params* p, const uint32_t* keys, uint64_t m, uint32_t* buckets,
                     int8_t* signs, void* stream);
+
+/* Bytes of device workspace s2r_topk_ef needs for W workers of n elements in blocks of
+ * `block` elements (0 if the arguments are invalid). */
+size_t s2r_topk_workspace_bytes(uint32_t W, uint64_t n, uint64_t block);
+
+/* Block-wise Top-K sparsification with error feedback, the step that produces the sparse
+ * gradients compressed above (Section 2.2: the l2 norm of every block, the K largest blocks
+ * are kept; Appendix A.2: the error sequence e_{t+1} = g_t - C(g_t), g_t = gradient_t + e_t,
+ * taken here against the Top-K output itself).  Per worker k, with nb = ceil(n / block)
+ * blocks (the last may be short):
+ *   g[i]        = grad[i] + residual[i]    (one fp32 addition; g = grad if residual == NULL)
+ *   norm2(q)    = sum over block q of g[i]^2, accumulated in fp64
+ *   kept blocks = the K largest norm2, ties to the lower block id (all blocks if K >= nb)
+ *   out[i]      = g[i] in kept blocks, +0.0 elsewhere        (= sparse(g))
+ *   residual[i] = 0 in kept blocks, g[i] elsewhere          (= g - sparse(g))
+ *   grad      [W][ld] fp32 in; residual [W][ld] fp32 in/out or NULL; out [W][ld] fp32 out
+ *             (elements n..ld-1 of a row are not touched); all 16-byte aligned, ld % 4 == 0.
+ *   selected  [W][ceil(nb / 64)] uint64 out, bit q = block q kept (bits >= nb are 0); may
+ *             be NULL.
+ *   workspace at least s2r_topk_workspace_bytes(W, n, block) bytes; contents irrelevant.
+ * The squared norms are fp64 sums in the kernel's own order (per-lane partial sums, then a
+ * butterfly across the wave), so a block whose norm ties another's only to within fp64
+ * rounding may be ordered either way.
+ * Aliasing: out may not overlap grad or residual; residual may not equal grad.
+ * Errors: S2R_ERR_NULL, S2R_ERR_DIM (W == 0, block == 0, n >= 2^32, ld < n), S2R_ERR_ALIGN,
+ * S2R_ERR_WORKSPACE, S2R_ERR_HIP. */
+s2r_status s2r_topk_ef(uint32_t W, const float* grad, float* residual, uint64_t n, uint64_t ld,
+                       uint64_t block, uint64_t K, float* out, uint64_t* selected,
+                       void* workspace, size_t ws_bytes, void* stream);
 
 /* Static string naming a status code. */
 const char* s2r_status_string(s2r_status s);

@@ -181,3 +181,59 @@ def set_elements(bitmap: np.ndarray, n: int, log2_block: int) -> np.ndarray:
     B = 1 << log2_block
     blocks = bits_of(bitmap, (n + B - 1) // B)
     return np.repeat(blocks, B)[:n]
+
+
+def run_topk(grads: np.ndarray, residual: np.ndarray | None, n: int, block: int, K: int):
+    """grads, residual: [W][ld] host arrays.  Returns (out, residual, selected) as numpy."""
+    W, ld = grads.shape
+    g = torch.from_numpy(np.ascontiguousarray(grads)).to(DEV)
+    r = None if residual is None else torch.from_numpy(np.ascontiguousarray(residual)).to(DEV)
+    out = torch.full((W, ld), float("nan"), dtype=torch.float32, device=DEV)
+    nb = -(-n // block)
+    sw = max((nb + 63) // 64, 1)
+    sel = torch.full((W, sw), -1, dtype=torch.int64, device=DEV)
+    ws = torch.empty((max(s2r.s2r_topk_workspace_bytes(W, n, block), 1),), dtype=torch.uint8,
+                     device=DEV)
+    ws.fill_(0xAB)
+    s2r.s2r_topk_ef(W, g, r, n, ld, block, K, out, sel, ws)
+    torch.cuda.synchronize()
+    return (out.cpu().numpy(), None if r is None else r.cpu().numpy(),
+            sel.cpu().numpy().view(np.uint64)[:, : (nb + 63) // 64])
+
+
+def assert_topk_matches(grads, residual, n, block, K, out, res_out, sel, what=""):
+    """Every worker against the oracle.  The kept set must equal the oracle's unless the
+    K-th and (K+1)-th squared norms tie to within fp64 rounding (1e-12 relative); then the
+    GPU's set must still be a valid Top-K of the oracle's norms.  Given the kept set, out and
+    the residual are bit-exact (the same fp32 addition g = grad + residual on both sides)."""
+    W = grads.shape[0]
+    nb = -(-n // block)
+    for k in range(W):
+        o = oracle.topk_ef(grads[k, :n], None if residual is None else residual[k, :n], block, K)
+        gbits = np.unpackbits(sel[k].view(np.uint8), bitorder="little")
+        assert not gbits[nb:].any(), f"{what} worker {k}: selection pad bits"
+        gkept = gbits[:nb].astype(bool)
+        okept = np.unpackbits(o["selected"].view(np.uint8), bitorder="little")[:nb].astype(bool)
+        assert int(gkept.sum()) == min(K, nb), f"{what} worker {k}: {gkept.sum()} kept"
+        if not np.array_equal(gkept, okept):
+            nrm = o["norm2"]
+            srt = np.sort(nrm)[::-1]
+            tie = srt[min(K, nb) - 1]
+            close = np.abs(nrm - tie) <= 1e-12 * max(tie, 1e-300)
+            diff = gkept != okept
+            assert np.all(close[diff]), f"{what} worker {k}: kept set differs beyond ties"
+            # recompute the expected output with the GPU's (valid) kept set
+            em = np.repeat(gkept, block)[:n]
+            g = grads[k, :n] + (0 if residual is None else residual[k, :n])
+            want_out = np.where(em, g, np.float32(0))
+            want_res = np.where(em, np.float32(0), g)
+        else:
+            want_out, want_res = o["out"], o["residual"]
+        assert np.array_equal(out[k, :n].view(np.uint32), want_out.astype(np.float32).view(np.uint32)), \
+            f"{what} worker {k}: out"
+        assert np.all(np.isnan(out[k, n:])), f"{what} worker {k}: wrote beyond n"
+        if residual is not None:
+            assert np.array_equal(res_out[k, :n].view(np.uint32),
+                                  want_res.astype(np.float32).view(np.uint32)), f"{what} worker {k}: residual"
+            assert np.array_equal(res_out[k, n:].view(np.uint32), residual[k, n:].view(np.uint32)), \
+                f"{what} worker {k}: residual beyond n"

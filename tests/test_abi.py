@@ -143,3 +143,31 @@ def test_block_workspace_grows(s2r):
     b = s2r.s2r_encode_workspace_bytes(q, 2, 100_000, 1000)
     assert b >= a + 2 * s2r.s2r_bitmap_words(100_000) * 8
 
+
+
+def test_topk_argument_errors(s2r):
+    """s2r_topk_ef rejects bad arguments on the host, before any enqueue."""
+    FAKE = 1 << 20
+    L = s2r.lib()
+    need = s2r.s2r_topk_workspace_bytes(2, 1000, 64)
+    assert need > 0 and s2r.s2r_topk_workspace_bytes(0, 1000, 64) == 0
+    assert s2r.s2r_topk_workspace_bytes(2, 1000, 0) == 0
+
+    def call(W=2, grad=FAKE, res=FAKE * 2, n=1000, ld=1000, block=64, K=3, out=FAKE * 3,
+             sel=FAKE * 4, ws=FAKE * 5, ws_bytes=None):
+        return L.s2r_topk_ef(W, grad, res, n, ld, block, K, out, sel, ws,
+                             need if ws_bytes is None else ws_bytes, None)
+
+    assert call(grad=None) == s2r.S2R_ERR_NULL
+    assert call(out=None) == s2r.S2R_ERR_NULL
+    assert call(ws=None) == s2r.S2R_ERR_NULL
+    assert call(W=0) == s2r.S2R_ERR_DIM
+    assert call(block=0) == s2r.S2R_ERR_DIM
+    assert call(ld=996) == s2r.S2R_ERR_DIM
+    assert call(n=2**32, ld=2**32) == s2r.S2R_ERR_DIM
+    assert call(res=FAKE) == s2r.S2R_ERR_DIM          # residual may not be the gradient
+    assert call(ld=1002) == s2r.S2R_ERR_ALIGN
+    assert call(grad=FAKE + 4) == s2r.S2R_ERR_ALIGN
+    assert call(out=FAKE * 3 + 8) == s2r.S2R_ERR_ALIGN
+    assert call(sel=FAKE * 4 + 4) == s2r.S2R_ERR_ALIGN
+    assert call(ws_bytes=need - 1) == s2r.S2R_ERR_WORKSPACE

@@ -95,3 +95,31 @@ def test_fullsize_pipeline(cid, lb):
     assert not bad.any(), f"{int(bad.sum())} decoded values outside tolerance, e.g. " \
         f"i={oi[bad][:5].tolist()} gpu={g[bad][:5]} oracle={ov[bad][:5]} tol={ot[bad][:5]}"
     gp.say(f"  ok: nnz/worker max {int(nnz.max())}, set bits {oi.size}")
+
+
+@pytest.mark.timeout(900)
+def test_fullsize_topk_resnet():
+    """Block-wise Top-K with error feedback at the ResNet-50 workload's size (W=16,
+    N=25,557,032, blocks of 256, K = 999), two steps with the residual carried: kept sets,
+    outputs and residuals against the oracle; the first step's kept blocks are exactly the
+    workload's own Top-1% blocks."""
+    wl = WL.workload(2)
+    block = 256
+    nb = -(-wl.N // block)
+    K = -(-nb // 100)
+    gp.say(f"fullsize topk {wl.name}: W={wl.W} N={wl.N} K={K}")
+    ld = (wl.N + 3) // 4 * 4
+    grads = np.zeros((wl.W, ld), dtype=np.float32)
+    for k in range(wl.W):
+        grads[k, :wl.N] = WL.worker_dense(2, k)
+    res = np.zeros_like(grads)
+    for step in range(2):
+        out, res_new, sel = gp.run_topk(grads, res, wl.N, block, K)
+        gp.say(f"  step {step}: gpu done")
+        gp.assert_topk_matches(grads, res, wl.N, block, K, out, res_new, sel, f"step {step}")
+        if step == 0:
+            for k in range(3):
+                idx, val = WL.worker_sparse(2, k)
+                nzi = np.flatnonzero(out[k, :wl.N])
+                assert np.array_equal(nzi, idx.astype(np.int64)), f"worker {k}: kept elements"
+        res = res_new

@@ -200,6 +200,14 @@ def worker_sparse(cid: int, k: int):
     raise ValueError(cid)
 
 
+def worker_dense(cid: int, k: int) -> np.ndarray:
+    """Worker k's dense gradient before block-wise Top-K, for the block-sparsified workload
+    (cid 2: N(0,1) over all N elements, the same draws worker_sparse(2, k) keeps 1% of)."""
+    if cid != 2:
+        raise ValueError("dense pre-sparsification gradients exist for the ResNet-50 workload")
+    return normal(rng_for(cid, k), WORKLOADS[cid].N, 1.0)
+
+
 # ----------------------------------------------------------------------------------------
 # small generators for edge cases and parity at oracle-friendly sizes
 
