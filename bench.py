@@ -65,6 +65,30 @@ def build_inputs(wl, dev, hash_family: str, log2_block: int = 0):
     return p, grad, ld, cap, sparse
 
 
+def estimation_error(wl, sparse, out_dev) -> dict:
+    """Relative l2 error of the decoded aggregate against the exact sum of the workers'
+    gradients, sum_k g_k, formed in fp64 with numpy from the same seeded (index, value) lists:
+    ||g_hat - sum_k g_k|| / ||sum_k g_k||, over all N elements, and over the union of the
+    workers' non-zeros.  Measured after the timed region."""
+    import numpy as np
+
+    idx_all = np.concatenate([x[0] for x in sparse]).astype(np.int64)
+    val_all = np.concatenate([x[1] for x in sparse]).astype(np.float64)
+    sup, inv = np.unique(idx_all, return_inverse=True)
+    gsum = np.zeros(sup.size, dtype=np.float64)
+    np.add.at(gsum, inv, val_all)
+    ghat = out_dev.cpu().numpy().astype(np.float64)
+    on_sup = ghat[sup] - gsum
+    err2_sup = float(np.dot(on_sup, on_sup))
+    off = ghat.copy()
+    off[sup] = 0.0
+    err2_all = err2_sup + float(np.dot(off, off))
+    ref2 = float(np.dot(gsum, gsum))
+    return {"rel_l2_all": round((err2_all / ref2) ** 0.5, 6) if ref2 else None,
+            "rel_l2_support": round((err2_sup / ref2) ** 0.5, 6) if ref2 else None,
+            "union_nnz": int(sup.size)}
+
+
 def library_source_sha256() -> str:
     """sha256 over the library's sources (kernels, launchers, C header), by file name."""
     import glob
@@ -247,6 +271,8 @@ def main() -> int:
     ap.add_argument("--block", type=int, default=0, metavar="LOG2_B",
                     help="bitmap granularity: one bit per 2^LOG2_B elements (default 0: per element)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-error", action="store_true",
+                    help="skip the estimation-error report (relative l2 error vs the exact sum)")
     ap.add_argument("--stage", default="aggregate", choices=["aggregate", "topk"],
                     help="aggregate: encode+reduce+decode (default); topk: the block-wise Top-K "
                          "with error feedback that precedes it (ResNet-50 workload)")
@@ -366,6 +392,9 @@ def main() -> int:
         "step_hbm_frac": round(step_alg / HBM_PEAK_GBS, 4),
         "phases": phases,
     }
+    if not args.no_error:
+        log("estimation error vs the exact sum ...")
+        result["estimation_error"] = estimation_error(wl, sparse, out)
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle) ...")
         result["cpu_baseline"] = cpu_baseline(wl, sparse, p.as_dict())

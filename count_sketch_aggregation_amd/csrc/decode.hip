@@ -96,7 +96,7 @@ struct DecodeWs {
   uint16_t* slot;             // [chunks][kChunk] rank -> slot in that order
   float* gval;                // [chunks][kChunk] median of the item at each slot (k_dmedian),
                               // then of each rank (k_dunsort)
-  uint32_t* prefix;           // [P + 1][chunks] partition starts per chunk
+  uint32_t* prefix;           // [chunks][P + 1] partition starts per chunk
   uint64_t chunks;            // capacity in chunks (max_set rounded up)
   uint64_t max_set;
 };
@@ -185,9 +185,9 @@ __global__ __launch_bounds__(kDBinThreads) void k_dbin(HashArgs h, uint64_t n,
     }
     __syncthreads();
   }
-  uint32_t* pf = ws.prefix + c;
-  for (uint32_t p = tid; p < P; p += kDBinThreads) pf[(uint64_t)p * ws.chunks] = hist[p];
-  if (tid == 0) pf[(uint64_t)P * ws.chunks] = cnt;
+  uint32_t* pf = ws.prefix + (uint64_t)c * (P + 1);  // one contiguous row per chunk
+  for (uint32_t p = tid; p < P; p += kDBinThreads) pf[p] = hist[p];
+  if (tid == 0) pf[P] = cnt;
   uint16_t* sl = ws.slot + start;
 #pragma unroll
   for (int r = 0; r < R; ++r) {
@@ -244,7 +244,7 @@ __global__ __launch_bounds__(kAccThreads) void k_dmedian(HashArgs h, uint64_t ti
       tile[c] = sk[(uint64_t)j * w + q];
     }
   }
-  const uint32_t* pf = ws.prefix + (uint64_t)p * ws.chunks;
+  const uint32_t* pf = ws.prefix + p;  // column p of the chunk-major offsets
   constexpr int PER = kSegBatch / kAccThreads;
   for (uint32_t cb = c_lo; cb < c_hi; cb += kSegBatch) {
     const uint32_t nb = c_hi - cb < (uint32_t)kSegBatch ? c_hi - cb : (uint32_t)kSegBatch;
@@ -255,7 +255,8 @@ __global__ __launch_bounds__(kAccThreads) void k_dmedian(HashArgs h, uint64_t ti
       const uint32_t c = tid * PER + u;
       len[u] = 0;
       if (c < nb) {
-        const uint32_t lo = pf[cb + c], hi = pf[ws.chunks + cb + c];
+        const uint64_t row = (uint64_t)(cb + c) * (P + 1);
+        const uint32_t lo = pf[row], hi = pf[row + 1];
         seg_src[c] = (cb + c) * (uint32_t)kChunk + lo;
         len[u] = hi - lo;
       }

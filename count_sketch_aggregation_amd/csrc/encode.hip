@@ -359,7 +359,8 @@ __device__ __forceinline__ void block_exclusive_scan(uint32_t* hist, uint32_t P,
 // chunk in LDS and writes it out with coalesced 128-bit stores:
 //   bins[k][c * kChunk + X[p] ...]        the chunk's (index, value bits) pairs grouped by
 //                                         partition, interleaved so a segment is one run
-//   prefix[k][p][c] = X[p], p = 0..P       the start of partition p inside chunk c
+//   prefix[k][c][p] = X[p], p = 0..P       the start of partition p inside chunk c (one
+//                                          contiguous row per chunk, so the stores coalesce)
 __global__ __launch_bounds__(kBinThreads) void k_bin(
     HashArgs h, uint64_t tiles, const uint32_t* __restrict__ offsets,
     const uint32_t* __restrict__ idx, const float* __restrict__ val, uint64_t cap,
@@ -399,9 +400,9 @@ __global__ __launch_bounds__(kBinThreads) void k_bin(
   }
   __syncthreads();
   block_exclusive_scan<kBinThreads>(hist, P, wtot);
-  uint32_t* pf = prefix + (uint64_t)k * (P + 1) * chunks + c;
-  for (uint32_t p = tid; p < P; p += kBinThreads) pf[(uint64_t)p * chunks] = hist[p];
-  if (tid == 0) pf[(uint64_t)P * chunks] = cnt;
+  uint32_t* pf = prefix + ((uint64_t)k * chunks + c) * (P + 1);
+  for (uint32_t p = tid; p < P; p += kBinThreads) pf[p] = hist[p];
+  if (tid == 0) pf[P] = cnt;
 #pragma unroll
   for (int r = 0; r < R; ++r) {
     const uint32_t s = tid + kBinThreads * r;
@@ -441,7 +442,9 @@ __global__ __launch_bounds__(kAccThreads) void k_accumulate(
   const uint64_t total = offsets[(uint64_t)k * (tiles + 1) + tiles];
   const uint64_t lim = total < cap ? total : cap;
   const uint32_t nch = (uint32_t)((lim + kChunk - 1) / kChunk);
-  const uint32_t* pf = prefix + ((uint64_t)k * (partitions + 1) + p) * chunks;
+  // column p of the worker's chunk-major offsets: strided, but the XCD grouping runs the
+  // partitions that share each cache line on one XCD at about the same time
+  const uint32_t* pf = prefix + (uint64_t)k * chunks * (partitions + 1) + p;
   const uint64_t kbase = (uint64_t)k * chunks * kChunk;
   constexpr int PER = kSegBatch / kAccThreads;
   for (uint32_t cb = 0; cb < nch; cb += kSegBatch) {
@@ -453,7 +456,8 @@ __global__ __launch_bounds__(kAccThreads) void k_accumulate(
       const uint32_t c = tid * PER + u;
       len[u] = 0;
       if (c < nb) {
-        const uint32_t lo = pf[cb + c], hi = pf[chunks + cb + c];
+        const uint64_t row = (uint64_t)(cb + c) * (partitions + 1);
+        const uint32_t lo = pf[row], hi = pf[row + 1];
         seg_src[c] = (cb + c) * (uint32_t)kChunk + lo;
         len[u] = hi - lo;
       }
