@@ -13,9 +13,10 @@
 //                into the residual, so the last pass reads one array instead of two;
 //   k_tk_select  one workgroup per worker: radix select over the keys (eight 8-bit digits,
 //                most significant first; non-negative fp64 bit patterns order as their
-//                values) finds the K-th largest key T and how many keys equal to T are
-//                taken; kept = key > T, plus the lowest-id keys equal to T when fewer than
-//                all of them fit; writes the kept-block bitmap;
+//                values; the surviving candidates move to LDS once they fit) finds the K-th
+//                largest key T and how many keys equal to T are taken; kept = key > T, plus
+//                the lowest-id keys equal to T when fewer than all of them fit; writes the
+//                kept-block bitmap;
 //   k_tk_apply   every element: out = g in kept blocks and 0 elsewhere; the residual of
 //                kept blocks becomes 0 (the rest already holds g).
 // HBM traffic with error feedback: 12 B per element in the first pass (read gradient and
@@ -88,15 +89,22 @@ __global__ __launch_bounds__(kTkNormThreads) void k_tk_norm(const float* __restr
 
 // ---------------------------------------------------------------------------------------
 // k_tk_select: grid W, 1024 threads.  Per-wave 256-bin histograms in LDS (64 lanes hitting
-// one bin serialise within a wave only), summed before each digit is chosen.
+// one bin serialise within a wave only), summed before each digit is chosen.  Passes over
+// global keys keep kTkLoads loads in flight per thread.  As soon as the keys that match the
+// digits chosen so far fit in LDS (kTkCand), the next pass also gathers them there, and the
+// remaining passes read only those.
+constexpr int kTkCand = 6000;  // candidate keys staged in LDS (47 KiB; with the histograms under 64 KiB)
+constexpr int kTkLoads = 8;
 __global__ __launch_bounds__(kTkSelThreads) void k_tk_select(const uint64_t* __restrict__ keys,
                                                              uint64_t nb, uint64_t K,
                                                              uint64_t* __restrict__ sel,
                                                              uint64_t sel_words) {
   constexpr int NW = kTkSelThreads / kWave;
   __shared__ uint32_t hist[NW][256];
+  __shared__ uint64_t cand[kTkCand];
   __shared__ uint64_t s_prefix;
   __shared__ uint64_t s_rem, s_eq;
+  __shared__ uint32_t s_ncand;
   __shared__ uint32_t wsum[NW];
   const uint32_t k = blockIdx.x;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -109,18 +117,44 @@ __global__ __launch_bounds__(kTkSelThreads) void k_tk_select(const uint64_t* __r
     if (tid == 0) {
       s_prefix = 0;
       s_rem = K;
+      s_eq = nb;  // keys matching the (empty) prefix
+      s_ncand = 0;
     }
+    bool in_lds = false;
+    uint32_t ncand = 0;
     for (int shift = 56; shift >= 0; shift -= 8) {
       for (int b = tid; b < NW * 256; b += kTkSelThreads) (&hist[0][0])[b] = 0u;
       __syncthreads();
       const uint64_t prefix = s_prefix;
-      for (uint64_t i = tid; i < nb; i += kTkSelThreads) {
-        const uint64_t x = key[i];
-        // the digits above `shift` must match the prefix chosen so far
-        const bool match = shift == 56 || ((x ^ prefix) >> (shift + 8)) == 0;
-        if (match) atomicAdd(&hist[wave][(x >> shift) & 255u], 1u);
+      // keys whose digits above `shift` equal the prefix chosen so far
+      const uint64_t hi_mask = shift == 56 ? 0ull : ~0ull << (shift + 8);
+      if (in_lds) {
+        for (uint32_t i = tid; i < ncand; i += kTkSelThreads) {
+          const uint64_t x = cand[i];
+          if (((x ^ prefix) & hi_mask) == 0) atomicAdd(&hist[wave][(x >> shift) & 255u], 1u);
+        }
+      } else {
+        const bool gather = s_eq <= (uint64_t)kTkCand;
+        for (uint64_t i0 = tid; i0 < nb; i0 += (uint64_t)kTkSelThreads * kTkLoads) {
+          uint64_t x[kTkLoads];
+#pragma unroll
+          for (int u = 0; u < kTkLoads; ++u) {
+            const uint64_t i = i0 + (uint64_t)u * kTkSelThreads;
+            x[u] = i < nb ? key[i] : 0ull;
+          }
+#pragma unroll
+          for (int u = 0; u < kTkLoads; ++u) {
+            const uint64_t i = i0 + (uint64_t)u * kTkSelThreads;
+            if (i < nb && ((x[u] ^ prefix) & hi_mask) == 0) {
+              atomicAdd(&hist[wave][(x[u] >> shift) & 255u], 1u);
+              if (gather) cand[atomicAdd(&s_ncand, 1u)] = x[u];
+            }
+          }
+        }
+        if (gather) in_lds = true;  // uniform: s_eq was read by every thread
       }
       __syncthreads();
+      ncand = s_ncand;
       if (tid < 256) {
         uint32_t c = 0;
         for (int v = 0; v < NW; ++v) c += hist[v][tid];
@@ -148,11 +182,21 @@ __global__ __launch_bounds__(kTkSelThreads) void k_tk_select(const uint64_t* __r
 
   // kept-block bitmap, 64 keys per wave step
   if (all || none || take_eq == n_eq) {
-    for (uint64_t base = (uint64_t)wave * kWave; base < nb; base += kTkSelThreads) {
-      const uint64_t i = base + lane;
-      const bool kept = i < nb && (all || (!none && key[i] >= T));
-      const uint64_t word = __ballot(kept);
-      if (lane == 0) out[base / 64] = word;
+    constexpr int U = 4;
+    for (uint64_t b0 = (uint64_t)wave * kWave; b0 < nb; b0 += (uint64_t)kTkSelThreads * U) {
+      uint64_t x[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const uint64_t i = b0 + (uint64_t)u * kTkSelThreads + lane;
+        x[u] = (i < nb && !all && !none) ? key[i] : 0ull;
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const uint64_t base = b0 + (uint64_t)u * kTkSelThreads;
+        const bool kept = base + lane < nb && (all || (!none && x[u] >= T));
+        const uint64_t word = __ballot(kept);
+        if (lane == 0 && base < nb) out[base / 64] = word;
+      }
     }
   } else {
     // only some keys equal to T fit: they go to the lowest block ids, so the tie rank is a
