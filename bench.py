@@ -14,6 +14,13 @@ dominant phase reaches on its algorithmic bytes:
 queried by the decode, the set bits of the merged bitmap).  List writes and any extra
 traffic of the implementation are not credited.
 
+Besides `value` (K steps back to back, host-timed), the line reports the median and minimum
+of the per-step event times, the same for `--cold-reps` steps each timed alone after an
+untimed 512 MiB write that evicts L2 and the Infinity Cache, a plain streaming read of
+2 GiB measured on the same GPU (the achievable read ceiling) with the step's fraction of it,
+the estimation error of the decoded aggregate against the exact sum, and the CPU oracle's
+rate on a bounded sample of the same workload.
+
 Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--workload embedding]
 Prints ONE JSON line on stdout; progress goes to stderr.
 
@@ -271,6 +278,8 @@ def main() -> int:
     ap.add_argument("--block", type=int, default=0, metavar="LOG2_B",
                     help="bitmap granularity: one bit per 2^LOG2_B elements (default 0: per element)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cold-reps", type=int, default=20,
+                    help="extra steps timed alone after flushing the caches (0 to skip)")
     ap.add_argument("--no-error", action="store_true",
                     help="skip the estimation-error report (relative l2 error vs the exact sum)")
     ap.add_argument("--stage", default="aggregate", choices=["aggregate", "topk"],
@@ -363,6 +372,31 @@ def main() -> int:
     }
     phases = {k: {"ms": round(phase_ms[k], 4), "alg_bytes": b_alg[k],
                   "alg_GBs": round(b_alg[k] / (phase_ms[k] * 1e-3) / 1e9, 1)} for k in phase_ms}
+    step_ev = sorted(ev[0].elapsed_time(ev[3]) for ev in events)
+
+    # Cold-cache repetitions: before each, an untimed 512 MiB write evicts L2 and the
+    # Infinity Cache; each step is timed alone with events.  Then a plain streaming read of
+    # 2 GiB on the same GPU for the measured read ceiling.
+    flush = torch.empty(512 << 18, dtype=torch.float32, device=dev)
+    cold = []
+    for _ in range(args.cold_reps):
+        flush.fill_(1.0)
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+        step(ev)
+        torch.cuda.synchronize()
+        cold.append(ev[0].elapsed_time(ev[3]))
+    del flush
+    cold.sort()
+    big = torch.ones(512 << 20, dtype=torch.float32, device=dev)
+    big.sum()
+    r0, r1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    r0.record(stream)
+    for _ in range(5):
+        big.sum()
+    r1.record(stream)
+    torch.cuda.synchronize()
+    read_GBs = 5 * big.numel() * 4 / (r0.elapsed_time(r1) * 1e-3) / 1e9
+    del big
     dom = max(phase_ms, key=phase_ms.get)
     achieved = b_alg[dom] / (phase_ms[dom] * 1e-3) / 1e9
     step_alg = sum(b_alg.values()) / (ms_per_step * 1e-3) / 1e9
@@ -390,6 +424,11 @@ def main() -> int:
                      "traffic": measured_traffic(wl.name, dom)},
         "step_alg_GBs": round(step_alg, 1),
         "step_hbm_frac": round(step_alg / HBM_PEAK_GBS, 4),
+        "step_ms_events": {"median": round(step_ev[len(step_ev) // 2], 4), "min": round(step_ev[0], 4)},
+        "cold_cache_step_ms": ({"median": round(cold[len(cold) // 2], 4), "min": round(cold[0], 4),
+                                "reps": len(cold)} if cold else None),
+        "measured_read_GBs": round(read_GBs, 1),
+        "step_frac_of_measured_read": round(step_alg / read_GBs, 4),
         "phases": phases,
     }
     if not args.no_error:
