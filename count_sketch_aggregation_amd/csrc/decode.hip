@@ -447,7 +447,7 @@ DecodeLayout decode_layout(const s2r_params& p, uint64_t n, uint64_t max_set) {
   L.off_toff = off;
   off = align256(off + (L.tiles + 1) * 4);
   L.off_btot = off;
-  off = align256(off + (size_t)scan_blocks(L.tiles) * 8);
+  off = align256(off + (size_t)scan_blocks(L.tiles) * 16);
   L.off_total = off;
   off = align256(off + 8);
   L.off_chunk_tile = off;
@@ -497,7 +497,7 @@ hipError_t launch_decode(const HashArgs& h, const s2r_params& p, uint64_t n,
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     e = launch_scan(1, L.tiles, tcount, toff, reinterpret_cast<uint64_t*>(b + L.off_total),
-                    chunk_tile, L.chunks, ws.max_set, reinterpret_cast<uint2*>(b + L.off_btot),
+                    chunk_tile, L.chunks, ws.max_set, reinterpret_cast<uint4*>(b + L.off_btot),
                     nullptr, nullptr, s);
     if (e != hipSuccess) return e;
     if (L.chunks > 0) {

@@ -8,10 +8,15 @@
 //   k_stream      streams the gradient once with 128-bit loads, packs the non-zero tests
 //                 into element-ordered bitmap words through LDS; writes the bitmap and one
 //                 non-zero count per 4096-element tile.
-//   k_scan        per worker: exclusive prefix of the tile counts (list offsets) and nnz.
-//   k_expand      per tile: expands the bitmap words into ascending (index, value) pairs at
-//                 their list offsets, re-reading only the 16-byte gradient groups that hold
-//                 a set bit.
+//   k_scan_sum, k_scan
+//                 per (16384-tile block, worker): exclusive prefix of the tile counts (list
+//                 offsets), nnz, and the lists of non-empty tile pairs, sparse and dense.
+//   k_blockbits   (block-granular bitmaps only) folds the element bitmap into block bits.
+//   k_expand_dense, k_expand_sparse
+//                 per non-empty tile pair: expands the bitmap words into ascending
+//                 (index, value) pairs at their list offsets, re-reading only the 16-byte
+//                 gradient groups that hold a set bit (a workgroup per dense pair, a wave
+//                 per sparse one).
 //   then either (d x w table larger than LDS, independent rows)
 //     k_scatter   reads 8192-entry list chunks and adds each pair into the d rows with
 //                 global fp32 atomics (after a zero fill), or (partitioned path)
@@ -99,39 +104,45 @@ __global__ __launch_bounds__(kStreamThreads) void k_stream(
 // thread for the block scan (read with a 1-in-16 padding so the 64 lanes hit distinct
 // banks), offsets written back through LDS with coalesced stores.  The block starts from the
 // totals of the blocks before it (btot, from k_scan_sum; none with one block).
-// Optionally (spans != nullptr) it also lists, in order, the spans (tile pairs) that hold a
-// non-zero, for k_expand, with their count in nspan.  And, for every chunk of kChunk
-// consecutive list positions below `limit`, it records the tile holding its first position.
+// Optionally (spans != nullptr) it also lists the spans (tile pairs) that hold a non-zero,
+// for k_expand: the sparse ones (at most kDenseSpan non-zeros) in order from the front of
+// the worker's list, the dense ones from its back, with the two counts in nspan[2k],
+// nspan[2k + 1].  And, for every chunk of kChunk consecutive list positions below `limit`,
+// it records the tile holding its first position.
 __device__ __forceinline__ uint32_t scan_pad(uint32_t i) { return i + (i >> 4); }
 
 __global__ __launch_bounds__(kScanThreads) void k_scan_sum(uint64_t tiles,
                                                            const uint32_t* __restrict__ counts,
-                                                           uint2* __restrict__ btot) {
-  __shared__ uint32_t wsum[2][kScanThreads / kWave];
+                                                           uint4* __restrict__ btot) {
+  __shared__ uint32_t wsum[3][kScanThreads / kWave];
   const uint32_t b = blockIdx.x, k = blockIdx.y;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const uint32_t* cnt = counts + (uint64_t)k * tiles;
   const uint64_t base = (uint64_t)b * kScanPass;
-  uint32_t sum = 0, ne = 0;
+  uint32_t sum = 0, ns = 0, nd = 0;
 #pragma unroll
   for (int u = 0; u < kScanPass / 2 / kScanThreads; ++u) {
     const uint64_t i = base + 2 * (uint64_t)(tid + kScanThreads * u);  // a span's first tile
     const uint32_t c = (i < tiles ? cnt[i] : 0u) + (i + 1 < tiles ? cnt[i + 1] : 0u);
     sum += c;
-    ne += c ? 1u : 0u;
+    ns += (c && c <= kDenseSpan) ? 1u : 0u;
+    nd += c > kDenseSpan ? 1u : 0u;
   }
   sum = wave_sum(sum);
-  ne = wave_sum(ne);
+  ns = wave_sum(ns);
+  nd = wave_sum(nd);
   if (lane == 0) {
     wsum[0][wave] = sum;
-    wsum[1][wave] = ne;
+    wsum[1][wave] = ns;
+    wsum[2][wave] = nd;
   }
   __syncthreads();
   if (tid == 0) {
-    uint2 t = {0u, 0u};
+    uint4 t = {0u, 0u, 0u, 0u};
     for (int v = 0; v < kScanThreads / kWave; ++v) {
       t.x += wsum[0][v];
       t.y += wsum[1][v];
+      t.z += wsum[2][v];
     }
     btot[(uint64_t)k * gridDim.x + b] = t;
   }
@@ -140,36 +151,42 @@ __global__ __launch_bounds__(kScanThreads) void k_scan_sum(uint64_t tiles,
 __global__ __launch_bounds__(kScanThreads) void k_scan(
     uint64_t tiles, const uint32_t* __restrict__ counts, uint32_t* __restrict__ offsets,
     uint64_t* __restrict__ nnz, uint32_t* __restrict__ chunk_tile, uint64_t chunks,
-    uint64_t limit, const uint2* __restrict__ btot, uint32_t* __restrict__ spans,
+    uint64_t limit, const uint4* __restrict__ btot, uint32_t* __restrict__ spans,
     uint32_t* __restrict__ nspan) {
   constexpr int PER = kScanPass / kScanThreads;  // 16 tiles = 8 spans per thread
+  constexpr int NW = kScanThreads / kWave;
   __shared__ uint32_t lc[kScanPass + kScanPass / 16];
-  __shared__ uint32_t wsum[2][kScanThreads / kWave];
+  __shared__ uint32_t wsum[3][NW];
   const uint32_t b = blockIdx.x, k = blockIdx.y, nb = gridDim.x;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const uint32_t* cnt = counts + (uint64_t)k * tiles;
   uint32_t* off = offsets + (uint64_t)k * (tiles + 1);
   uint32_t* ct = chunk_tile + (uint64_t)k * chunks;
-  uint32_t* sp = spans ? spans + (uint64_t)k * ((tiles + 1) / 2) : nullptr;
+  const uint64_t nsp = (tiles + 1) / 2;
+  uint32_t* sp = spans ? spans + (uint64_t)k * nsp : nullptr;
   const uint64_t base = (uint64_t)b * kScanPass;
-  uint32_t carry = 0, scarry = 0;
+  uint32_t carry = 0, scarry = 0, dcarry = 0;
   if (b > 0) {  // totals of the blocks before this one
-    uint32_t c = 0, e = 0;
+    uint32_t c = 0, e = 0, f = 0;
     for (uint32_t i = tid; i < b; i += kScanThreads) {
-      const uint2 t = btot[(uint64_t)k * nb + i];
+      const uint4 t = btot[(uint64_t)k * nb + i];
       c += t.x;
       e += t.y;
+      f += t.z;
     }
     c = wave_sum(c);
     e = wave_sum(e);
+    f = wave_sum(f);
     if (lane == 0) {
       wsum[0][wave] = c;
       wsum[1][wave] = e;
+      wsum[2][wave] = f;
     }
     __syncthreads();
-    for (int v = 0; v < kScanThreads / kWave; ++v) {
+    for (int v = 0; v < NW; ++v) {
       carry += wsum[0][v];
       scarry += wsum[1][v];
+      dcarry += wsum[2][v];
     }
     __syncthreads();  // wsum is reused below
   }
@@ -179,29 +196,38 @@ __global__ __launch_bounds__(kScanThreads) void k_scan(
     lc[scan_pad(i)] = base + i < tiles ? cnt[base + i] : 0u;
   }
   __syncthreads();
-  uint32_t v[PER], sum = 0, ne = 0;
+  uint32_t v[PER], sum = 0, ns = 0, nd = 0;
 #pragma unroll
   for (int u = 0; u < PER; ++u) {
     v[u] = lc[scan_pad(tid * PER + u)];
     sum += v[u];
-    if (u & 1) ne += (v[u - 1] | v[u]) ? 1u : 0u;
+    if (u & 1) {
+      const uint32_t c = v[u - 1] + v[u];
+      ns += (c && c <= kDenseSpan) ? 1u : 0u;
+      nd += c > kDenseSpan ? 1u : 0u;
+    }
   }
   const uint32_t inc = wave_inclusive_sum(sum);
-  const uint32_t sinc = wave_inclusive_sum(ne);
+  const uint32_t sinc = wave_inclusive_sum(ns);
+  const uint32_t dinc = wave_inclusive_sum(nd);
   if (lane == kWave - 1) {
     wsum[0][wave] = inc;
     wsum[1][wave] = sinc;
+    wsum[2][wave] = dinc;
   }
   __syncthreads();
   uint32_t run = carry + inc - sum, block_total = 0;
-  uint32_t srun = scarry + sinc - ne, block_spans = 0;
-  for (int w = 0; w < kScanThreads / kWave; ++w) {
+  uint32_t srun = scarry + sinc - ns, block_sparse = 0;
+  uint32_t drun = dcarry + dinc - nd, block_dense = 0;
+  for (int w = 0; w < NW; ++w) {
     if (w < wave) {
       run += wsum[0][w];
       srun += wsum[1][w];
+      drun += wsum[2][w];
     }
     block_total += wsum[0][w];
-    block_spans += wsum[1][w];
+    block_sparse += wsum[1][w];
+    block_dense += wsum[2][w];
   }
   const uint64_t t0 = base + (uint64_t)tid * PER;
 #pragma unroll
@@ -213,7 +239,12 @@ __global__ __launch_bounds__(kScanThreads) void k_scan(
            c0 < chunks && c0 * kChunk < (uint64_t)run + v[u] && c0 * kChunk < limit; ++c0)
         ct[c0] = (uint32_t)(t0 + u);
     }
-    if (sp && (u & 1) && (v[u - 1] | v[u])) sp[srun++] = (uint32_t)((t0 + u) >> 1);
+    if (sp && (u & 1)) {
+      const uint32_t c = v[u - 1] + v[u];
+      const uint32_t span = (uint32_t)((t0 + u) >> 1);
+      if (c > kDenseSpan) sp[nsp - 1 - drun++] = span;
+      else if (c) sp[srun++] = span;
+    }
     run += v[u];
   }
   __syncthreads();
@@ -225,21 +256,47 @@ __global__ __launch_bounds__(kScanThreads) void k_scan(
   if (b == nb - 1 && tid == 0) {
     off[tiles] = carry + block_total;
     nnz[k] = carry + block_total;
-    if (nspan) nspan[k] = scarry + block_spans;
+    if (nspan) {
+      nspan[2 * k] = scarry + block_sparse;
+      nspan[2 * k + 1] = dcarry + block_dense;
+    }
   }
 }
 
 // ---------------------------------------------------------------------------------------
-// k_expand: grid (G, W), 256 threads.  Workgroup g of worker k lists the non-empty spans
-// spans[g], spans[g + G], ... (tile pairs, 8192 elements, 128 words, from k_scan), so empty
-// regions cost no workgroups.  Per span, at list positions offsets[2 t] + (rank within the
-// span): the words and their popcount prefix go to LDS, each thread takes 8 groups of four
-// elements and, for the groups holding a set bit, re-reads only that 16-byte group of the
-// gradient (all 8 loads issued before use) and stores its pairs straight to their list
-// positions (the span's positions are contiguous).
+// k_expand_dense / k_expand_sparse: list the non-empty spans (tile pairs of 8192 elements and
+// 128 words, from k_scan), so empty regions cost nothing.  Each writes a span's pairs at list
+// positions offsets[2 t] + (rank within the span), re-reading only the 16-byte gradient
+// groups that hold a set bit.
+//   dense spans (more than kDenseSpan non-zeros), grid (G, W), 256 threads: a workgroup per
+//     span; the words and their popcount prefix go to LDS and each thread takes 8 groups of
+//     four elements, all 8 loads issued before use;
+//   sparse spans, grid (G, W), 256 threads: a wave per span, so four spans per workgroup are
+//     in flight with no workgroup barrier; lane l loads words 2l and 2l+1, a wave prefix sum
+//     of their popcounts gives every word's rank offset, both go to the wave's own LDS rows,
+//     and lane l takes the groups g = l + 64 m (m = 0..31), kExpandUnroll at a time (a round
+//     with no set group issues no load).
 constexpr int kExpandSpan = 2 * kTile;
-constexpr int kExpandWords = kExpandSpan / 64;
-__global__ __launch_bounds__(kExpandThreads) void k_expand(
+constexpr int kExpandWords = kExpandSpan / 64;  // 128
+constexpr int kExpandWaves = kExpandThreads / kWave;
+constexpr int kExpandUnroll = 4;
+
+// store the pairs of one group of four elements (nib = its set bits)
+__device__ __forceinline__ void expand_store(uint32_t* oi, float* ov, uint64_t cap, uint64_t pos,
+                                             uint32_t e0, uint32_t nib, const f32x4& v) {
+#pragma unroll
+  for (int c4 = 0; c4 < 4; ++c4) {
+    if (nib & (1u << c4)) {
+      if (pos < cap) {
+        oi[pos] = e0 + c4;
+        ov[pos] = v[c4];
+      }
+      ++pos;
+    }
+  }
+}
+
+__global__ __launch_bounds__(kExpandThreads) void k_expand_dense(
     const float* __restrict__ grad, uint64_t ld, uint64_t tiles,
     const uint64_t* __restrict__ bitmaps, uint64_t words, const uint32_t* __restrict__ offsets,
     const uint32_t* __restrict__ spans, const uint32_t* __restrict__ nspan,
@@ -249,13 +306,13 @@ __global__ __launch_bounds__(kExpandThreads) void k_expand(
   const uint32_t* off = offsets + (uint64_t)k * (tiles + 1);
   const uint64_t nsp = (tiles + 1) / 2;
   const uint32_t* sl = spans + (uint64_t)k * nsp;
-  const uint32_t ns = nspan[k];
+  const uint32_t nd = nspan[2 * k + 1];
   __shared__ uint64_t lwords[kExpandWords];
   __shared__ uint32_t lwoff[kExpandWords + 2];
   uint32_t* oi = idx + (uint64_t)k * cap;
   float* ov = val + (uint64_t)k * cap;
-  for (uint32_t si = blockIdx.x; si < ns; si += gridDim.x) {
-    const uint32_t t = sl[si];
+  for (uint32_t si = blockIdx.x; si < nd; si += gridDim.x) {
+    const uint32_t t = sl[nsp - 1 - si];
     const uint64_t o_t = off[2ull * t];
     if (o_t >= cap) continue;  // beyond the list capacity (uniform)
     if (tid < kExpandWords) {
@@ -284,22 +341,81 @@ __global__ __launch_bounds__(kExpandThreads) void k_expand(
       if (nib[m]) v[m] = *reinterpret_cast<const f32x4*>(row + 4 * gidx);
     }
 #pragma unroll
-    for (int m = 0; m < G; ++m) {
-      if (!nib[m]) continue;
-      const uint32_t e0 = t * (uint32_t)kExpandSpan + 4u * (uint32_t)(tid + kExpandThreads * m);
-      uint64_t pos = o_t + pos0[m];
-#pragma unroll
-      for (int c4 = 0; c4 < 4; ++c4) {
-        if (nib[m] & (1u << c4)) {
-          if (pos < cap) {
-            oi[pos] = e0 + c4;
-            ov[pos] = v[m][c4];
-          }
-          ++pos;
-        }
-      }
-    }
+    for (int m = 0; m < G; ++m)
+      if (nib[m])
+        expand_store(oi, ov, cap, o_t + pos0[m],
+                     t * (uint32_t)kExpandSpan + 4u * (uint32_t)(tid + kExpandThreads * m), nib[m],
+                     v[m]);
     __syncthreads();  // lwords and lwoff are rewritten for the next span
+  }
+}
+
+// LDS written by some lanes of a wave and read by others: order the two within the wave
+// (no workgroup barrier: the waves of a workgroup run different spans).
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+}
+
+__global__ __launch_bounds__(kExpandThreads) void k_expand_sparse(
+    const float* __restrict__ grad, uint64_t ld, uint64_t tiles,
+    const uint64_t* __restrict__ bitmaps, uint64_t words, const uint32_t* __restrict__ offsets,
+    const uint32_t* __restrict__ spans, const uint32_t* __restrict__ nspan,
+    uint32_t* __restrict__ idx, float* __restrict__ val, uint64_t cap) {
+  const uint32_t k = blockIdx.y;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const uint32_t* off = offsets + (uint64_t)k * (tiles + 1);
+  const uint64_t nsp = (tiles + 1) / 2;
+  const uint32_t* sl = spans + (uint64_t)k * nsp;
+  const uint32_t ns = nspan[2 * k];
+  __shared__ uint64_t lwords[kExpandWaves][kExpandWords];
+  __shared__ uint32_t lwoff[kExpandWaves][kExpandWords];
+  uint64_t* lw = lwords[wave];
+  uint32_t* lo = lwoff[wave];
+  uint32_t* oi = idx + (uint64_t)k * cap;
+  float* ov = val + (uint64_t)k * cap;
+  const uint32_t stride = gridDim.x * kExpandWaves;
+  for (uint32_t si = blockIdx.x * kExpandWaves + wave; si < ns; si += stride) {
+    const uint32_t t = sl[si];
+    const uint64_t o_t = off[2ull * t];
+    if (o_t >= cap) continue;  // beyond the list capacity (wave-uniform)
+    uint64_t wv[2];
+    uint32_t pc[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const uint64_t q = (uint64_t)t * kExpandWords + 2 * lane + j;
+      wv[j] = q < words ? bitmaps[(uint64_t)k * words + q] : 0ull;
+      pc[j] = (uint32_t)__popcll(wv[j]);
+    }
+    const uint32_t inc = wave_inclusive_sum(pc[0] + pc[1]);
+    wave_lds_sync();  // the previous span's reads of lw / lo are done
+    lw[2 * lane] = wv[0];
+    lw[2 * lane + 1] = wv[1];
+    lo[2 * lane] = inc - pc[0] - pc[1];
+    lo[2 * lane + 1] = inc - pc[1];
+    wave_lds_sync();
+    const float* row = grad + (uint64_t)k * ld + (uint64_t)t * kExpandSpan;
+    constexpr int UN = kExpandUnroll;
+#pragma unroll 1
+    for (int m0 = 0; m0 < kExpandSpan / 4 / kWave; m0 += UN) {
+      f32x4 v[UN];
+      uint32_t nib[UN], pos0[UN];
+#pragma unroll
+      for (int u = 0; u < UN; ++u) {
+        const int g = lane + kWave * (m0 + u);
+        const int q = g >> 4, sh = 4 * (g & 15);
+        const uint64_t w = lw[q];
+        nib[u] = (uint32_t)(w >> sh) & 0xFu;
+        pos0[u] = lo[q] + (uint32_t)__popcll(w & ((1ull << sh) - 1ull));
+        if (nib[u]) v[u] = *reinterpret_cast<const f32x4*>(row + 4 * g);
+      }
+#pragma unroll
+      for (int u = 0; u < UN; ++u)
+        if (nib[u])
+          expand_store(oi, ov, cap, o_t + pos0[u],
+                       t * (uint32_t)kExpandSpan + 4u * (uint32_t)(lane + kWave * (m0 + u)),
+                       nib[u], v[u]);
+    }
   }
 }
 
@@ -588,7 +704,7 @@ uint32_t scan_blocks(uint64_t tiles) {
 
 hipError_t launch_scan(uint32_t W, uint64_t tiles, const uint32_t* counts, uint32_t* offsets,
                        uint64_t* nnz, uint32_t* chunk_tile, uint64_t chunks, uint64_t cap,
-                       uint2* btot, uint32_t* spans, uint32_t* nspan, hipStream_t s) {
+                       uint4* btot, uint32_t* spans, uint32_t* nspan, hipStream_t s) {
   const uint32_t nb = tiles > 0 ? scan_blocks(tiles) : 1;
   if (nb > 1) {
     hipLaunchKernelGGL(k_scan_sum, dim3(nb, W), dim3(kScanThreads), 0, s, tiles, counts, btot);
@@ -624,8 +740,14 @@ hipError_t launch_expand(uint32_t W, const float* grad, uint64_t ld, uint64_t ti
   const uint64_t nsp = (tiles + 1) / 2;
   uint64_t g = (kExpandGroups + W - 1) / W;
   if (g > nsp) g = nsp;
-  hipLaunchKernelGGL(k_expand, dim3((uint32_t)g, W), dim3(kExpandThreads), 0, s, grad, ld, tiles,
-                     bitmaps, words, offsets, spans, nspan, idx, val, cap);
+  hipLaunchKernelGGL(k_expand_dense, dim3((uint32_t)g, W), dim3(kExpandThreads), 0, s, grad, ld,
+                     tiles, bitmaps, words, offsets, spans, nspan, idx, val, cap);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  uint64_t gs = (nsp + kExpandWaves - 1) / kExpandWaves;
+  if (gs > g) gs = g;
+  hipLaunchKernelGGL(k_expand_sparse, dim3((uint32_t)gs, W), dim3(kExpandThreads), 0, s, grad, ld,
+                     tiles, bitmaps, words, offsets, spans, nspan, idx, val, cap);
   return hipGetLastError();
 }
 

@@ -18,6 +18,8 @@ constexpr int kStreamWaveSpan = kTile / (kStreamThreads / 64);  // elements per 
 
 constexpr int kExpandThreads = 256;
 constexpr uint64_t kExpandGroups = 4096;             // expand workgroups per launch, all workers
+constexpr uint32_t kDenseSpan = 1024;                // non-zeros above which a span is expanded
+                                                     // by a whole workgroup, not one wave
 constexpr int kScatterThreads = 256;
 constexpr int kChunk = 8192;                        // list entries per chunk
 constexpr int kBinThreads = 512;                    // 16 entries per thread
@@ -49,11 +51,11 @@ HashArgs make_hash_args(const s2r_params& p);
 hipError_t launch_stream(uint32_t W, const float* grad, uint64_t n, uint64_t ld,
                          uint64_t tiles, uint64_t* bitmaps, uint32_t* counts, hipStream_t s);
 // tiles are scanned in blocks of kScanPass; more than one block needs W * scan_blocks(tiles)
-// uint2 block totals.  spans (W * ceil(tiles / 2) uint32) and nspan (W uint32) may be null.
+// uint4 block totals.  spans (W * ceil(tiles / 2) uint32) and nspan (2 W uint32) may be null.
 uint32_t scan_blocks(uint64_t tiles);
 hipError_t launch_scan(uint32_t W, uint64_t tiles, const uint32_t* counts, uint32_t* offsets,
                        uint64_t* nnz, uint32_t* chunk_tile, uint64_t chunks, uint64_t cap,
-                       uint2* btot, uint32_t* spans, uint32_t* nspan, hipStream_t s);
+                       uint4* btot, uint32_t* spans, uint32_t* nspan, hipStream_t s);
 hipError_t launch_fill_zero(float* p, uint64_t count, hipStream_t s);
 // block-granular bitmaps [W][bwords] from element bitmaps [W][ewords]
 hipError_t launch_blockbits(uint32_t W, const uint64_t* ebm, uint64_t ewords, uint64_t n,
