@@ -98,6 +98,8 @@ def lib() -> ctypes.CDLL:
         L.s2r_topk_workspace_bytes.restype = sz
         L.s2r_topk_ef.argtypes = [u32, vp, vp, u64, u64, u64, u64, vp, vp, vp, sz, vp]
         L.s2r_topk_ef.restype = st
+        L.s2r_diag_stream_read.argtypes = [vp, sz, vp, vp]
+        L.s2r_diag_stream_read.restype = st
         L.s2r_status_string.argtypes = [st]
         L.s2r_status_string.restype = ctypes.c_char_p
         _lib = L
@@ -211,6 +213,12 @@ def s2r_topk_ef(W: int, grad, residual, n: int, ld: int, block: int, K: int, out
     _check(lib().s2r_topk_ef(W, _ptr(grad), _ptr(residual), n, ld, block, K, _ptr(out),
                              _ptr(selected), _ptr(workspace), ws_bytes, _stream(stream)),
            "s2r_topk_ef")
+
+
+def s2r_diag_stream_read(buf, nbytes: int, sink, stream=None) -> None:
+    """Measurement helper (include/s2r_diag.h): stream `nbytes` of `buf` once."""
+    _check(lib().s2r_diag_stream_read(_ptr(buf), nbytes, _ptr(sink), _stream(stream)),
+           "s2r_diag_stream_read")
 
 
 # ---------------------------------------------------------------------------------------

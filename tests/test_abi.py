@@ -24,14 +24,19 @@ def s2r():
 
 
 def _declared():
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(s2r_[a-z0-9_]+)\s*\(", text)))
+    """Every function declared in include/*.h."""
+    import glob
+    names = set()
+    for h in glob.glob(os.path.join(ROOT, "include", "*.h")):
+        text = re.sub(r"/\*.*?\*/", "", open(h).read(), flags=re.S)
+        names |= set(re.findall(r"\b(s2r_[a-z0-9_]+)\s*\(", text))
+    return sorted(names)
 
 
 def test_header_symbols_exported(s2r):
     names = _declared()
-    assert {"s2r_encode", "s2r_reduce", "s2r_decode", "s2r_hash"} <= set(names)
+    assert {"s2r_encode", "s2r_reduce", "s2r_decode", "s2r_hash", "s2r_topk_ef",
+            "s2r_diag_stream_read"} <= set(names)
     L = ctypes.CDLL(s2r.LIB_PATH)
     for name in names:
         assert hasattr(L, name), f"{name} declared in s2r.h but not exported"
@@ -171,3 +176,13 @@ def test_topk_argument_errors(s2r):
     assert call(out=FAKE * 3 + 8) == s2r.S2R_ERR_ALIGN
     assert call(sel=FAKE * 4 + 4) == s2r.S2R_ERR_ALIGN
     assert call(ws_bytes=need - 1) == s2r.S2R_ERR_WORKSPACE
+
+
+def test_diag_argument_errors(s2r):
+    L = s2r.lib()
+    assert L.s2r_diag_stream_read(None, 16, 1 << 20, None) == s2r.S2R_ERR_NULL
+    assert L.s2r_diag_stream_read(1 << 20, 16, None, None) == s2r.S2R_ERR_NULL
+    assert L.s2r_diag_stream_read((1 << 20) + 4, 16, 1 << 21, None) == s2r.S2R_ERR_ALIGN
+    assert L.s2r_diag_stream_read(1 << 20, 20, 1 << 21, None) == s2r.S2R_ERR_ALIGN
+    assert L.s2r_diag_stream_read(1 << 20, 0, 1 << 21, None) == s2r.S2R_OK  # nothing to read
+
