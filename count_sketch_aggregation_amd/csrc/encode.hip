@@ -39,7 +39,7 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 // (min(bits << 1, 1) is 1 exactly when the magnitude bits are not all zero), a DPP swap
 // pairs adjacent lanes' nibbles into one byte, and the even lanes drop the bytes into LDS
 // in element order, so the tile's 128 bitmap words assemble in LDS with no scalar-unit work
-// and leave with one coalesced 1 KiB store.
+// and leave with one coalesced non-temporal 512-byte store.
 __device__ __forceinline__ uint32_t nz_bit(float x) { return min(__float_as_uint(x) << 1, 1u); }
 
 template <bool TAIL>
@@ -88,7 +88,8 @@ __global__ __launch_bounds__(kStreamThreads) void k_stream(
   __syncthreads();
   if (tid < kTileWords) {
     const uint64_t gw = (uint64_t)t * kTileWords + tid;
-    if (gw < words) bitmaps[(uint64_t)k * words + gw] = lwords[tid];
+    // non-temporal: ordinary stores mixed into this read stream cost the pass ~20% on MI355X
+    if (gw < words) __builtin_nontemporal_store(lwords[tid], &bitmaps[(uint64_t)k * words + gw]);
   }
   if (tid == 0) {
     uint32_t sum = 0;
@@ -535,7 +536,8 @@ __global__ __launch_bounds__(kBinThreads) void k_bin(
   if ((cnt & 1u) && tid == 0) out[cnt - 1] = spair[cnt - 1];
 }
 
-// k_accumulate (partitioned path): grid (P, W), 512 threads, items XCD-grouped.  The partition's d x 2^K
+// k_accumulate (partitioned path): grid (P, W), 512 threads, items XCD-grouped; the tile
+// leaves with non-temporal stores when nt is set.  The partition's d x 2^K
 // buckets live in LDS.  Its entries are spread over one short segment per list chunk; the
 // segments of up to kSegBatch chunks are flattened with a prefix sum so that consecutive
 // threads read consecutive entries, several per thread in flight.
@@ -543,7 +545,8 @@ template <int D>
 __global__ __launch_bounds__(kAccThreads) void k_accumulate(
     HashArgs h, uint64_t tiles, const uint32_t* __restrict__ offsets, uint64_t cap,
     uint64_t chunks, uint32_t partitions, const uint2* __restrict__ bins,
-    const uint32_t* __restrict__ prefix, float* __restrict__ sketches, uint64_t w, int vec4) {
+    const uint32_t* __restrict__ prefix, float* __restrict__ sketches, uint64_t w, int vec4,
+    int nt) {
   extern __shared__ __align__(16) float tile[];  // D * 2^K
   __shared__ uint32_t seg_src[kSegBatch];
   __shared__ uint32_t seg_off[kSegBatch + 1];
@@ -638,7 +641,9 @@ __global__ __launch_bounds__(kAccThreads) void k_accumulate(
     for (uint32_t c = tid; c < D * pw4; c += kAccThreads) {
       const uint32_t j = c / pw4, q = c - j * pw4;
       const f32x4 x = *reinterpret_cast<const f32x4*>(&tile[j * pw + 4 * q]);
-      *reinterpret_cast<f32x4*>(sk + (uint64_t)j * w + 4 * q) = x;
+      f32x4* dst = reinterpret_cast<f32x4*>(sk + (uint64_t)j * w + 4 * q);
+      if (nt) __builtin_nontemporal_store(x, dst);
+      else *dst = x;
     }
   } else {
     for (uint32_t c = tid; c < cells; c += kAccThreads) {
@@ -780,6 +785,9 @@ hipError_t launch_accumulate(const HashArgs& h, uint32_t W, uint64_t tiles,
                              float* sketches, uint64_t w, hipStream_t s) {
   const size_t lds = ((size_t)h.d << h.K) * sizeof(float);
   const int vec4 = (h.K >= 2 && (reinterpret_cast<uintptr_t>(sketches) % 16) == 0) ? 1 : 0;
+  // sketches larger than the Infinity Cache go out with non-temporal stores; smaller ones
+  // stay cached for the reduce that reads them next (both measured faster on MI355X)
+  const int nt = (uint64_t)W * ((uint64_t)h.d * w) * sizeof(float) > kCacheResidentBytes ? 1 : 0;
   hipError_t e = hipSuccess;
   S2R_DISPATCH_D(h.d, {
     e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_accumulate<D>),
@@ -787,7 +795,7 @@ hipError_t launch_accumulate(const HashArgs& h, uint32_t W, uint64_t tiles,
     if (e == hipSuccess)
       hipLaunchKernelGGL((k_accumulate<D>), dim3((uint32_t)partitions, W), dim3(kAccThreads), lds,
                          s, h, tiles, offsets, cap, chunks, (uint32_t)partitions, bins, prefix,
-                         sketches, w, vec4);
+                         sketches, w, vec4, nt);
   });
   if (e != hipSuccess) return e;
   return hipGetLastError();

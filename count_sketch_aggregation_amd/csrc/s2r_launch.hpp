@@ -30,6 +30,7 @@ constexpr int kAccThreads = 512;
 constexpr int acc_unroll(int d) { return d <= 5 ? 2 : 1; }
 constexpr int kSegBatch = 1024;                     // chunk segments flattened per batch
 constexpr size_t kAccLdsBytes = 64 * 1024;          // LDS of one partition tile
+constexpr uint64_t kCacheResidentBytes = 256ull << 20;  // MI355X Infinity Cache
 
 constexpr int kScanThreads = 1024;
 constexpr uint32_t kScanPass = kScanThreads * 16;  // tiles per scan block
