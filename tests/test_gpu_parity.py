@@ -238,3 +238,25 @@ def test_pipeline_tiny_config(K):
     out = gp.run_decode(p, wl.N, bm, S)
     want, tol = oracle.decode_dense(op, wl.N, obm, oS, oA)
     gp.assert_decode_matches(out, want, tol, gp.bits_of(obm, wl.N))
+
+
+def test_encode_span_classes():
+    """Tile pairs (8192 elements) with exactly 1024 non-zeros (listed one wave per pair), 1025
+    (a workgroup per pair), a full pair, and a pair whose non-zeros straddle its two tiles,
+    plus a ragged tail: every list entry in place."""
+    gp.say("encode span classes")
+    n = 8192 * 6 + 777
+    rng = np.random.Generator(np.random.PCG64(17))
+    g = np.zeros((2, n), dtype=np.float32)
+    for k in range(2):
+        for span, cnt in ((0, 1024), (1, 1025), (2, 8192), (4, 1)):
+            pos = rng.choice(8192, size=cnt, replace=False) + 8192 * span
+            g[k, pos] = rng.standard_normal(cnt).astype(np.float32) + 3.0
+        g[k, 8192 * 3 + 4090:8192 * 3 + 4102] = 1.5   # across the tile boundary inside pair 3
+        g[k, n - 5:] = -2.0                            # the ragged last pair
+    p, op = gp.params_pair(4242, 3, 14)
+    res = gp.run_encode(p, g, n)
+    gp.assert_encode_matches(op, g, n, res)
+    # and with a list capacity that cuts inside the dense pair
+    res = gp.run_encode(p, g, n, cap=1500)
+    gp.assert_encode_matches(op, g, n, res, cap=1500)
