@@ -246,8 +246,9 @@ def test_encode_span_classes():
     plus a ragged tail: every list entry in place."""
     gp.say("encode span classes")
     n = 8192 * 6 + 777
+    ld = (n + 3) // 4 * 4
     rng = np.random.Generator(np.random.PCG64(17))
-    g = np.zeros((2, n), dtype=np.float32)
+    g = np.zeros((2, ld), dtype=np.float32)
     for k in range(2):
         for span, cnt in ((0, 1024), (1, 1025), (2, 8192), (4, 1)):
             pos = rng.choice(8192, size=cnt, replace=False) + 8192 * span
