@@ -25,8 +25,11 @@
 //   k_dunsort  per rank chunk: moves the medians from slot order to rank order;
 //   k_dwrite   per tile: reads the medians of its set bits in rank order and writes the
 //              tile.
-// If U exceeds the workspace capacity the first three steps do nothing and k_dwrite falls
-// back to the direct gathers, decided on the device.
+// If U exceeds the workspace capacity, k_dbin, k_dmedian and k_dunsort do nothing and
+// k_dwrite falls back to the direct gathers, decided on the device.
+// With a block-granular bitmap (one bit per 2^lb elements) every kernel reads element words
+// built from the block bits (masked_word), so the set bits above are the elements of set
+// blocks.
 #include <string.h>
 
 #include "s2r_launch.hpp"

@@ -133,10 +133,10 @@ __device__ __forceinline__ uint64_t readlane64(uint64_t v, int l) {
 // visits only lanes whose word is non-empty and meets the range (a ballot), broadcasts that
 // word, and expands its 64 bits with one lane per bit (v_mbcnt gives each bit's rank), so the
 // cost follows the set bits in range, not the span of words.
-template <int WPT, typename T = uint32_t>
+template <int WPT>
 __device__ __forceinline__ void expand_owned_words(const uint64_t* wv, const uint64_t* rank,
                                                    uint64_t qbase, uint64_t start, uint64_t end,
-                                                   T* item, int lane) {
+                                                   uint32_t* item, int lane) {
 #pragma unroll
   for (int u = 0; u < WPT; ++u) {
     const uint64_t pc = (uint64_t)__popcll(wv[u]);
@@ -147,28 +147,9 @@ __device__ __forceinline__ void expand_owned_words(const uint64_t* wv, const uin
       const uint64_t w = readlane64(wv[u], l);
       const uint64_t r = readlane64(rank[u], l) + bits_below_lane(w);
       const uint64_t q = readlane64(qbase, l) + u;
-      if (((w >> lane) & 1ull) && r >= start && r < end) item[r - start] = (T)(q * 64 + lane);
+      if (((w >> lane) & 1ull) && r >= start && r < end) item[r - start] = (uint32_t)(q * 64 + lane);
     }
   }
-}
-
-// Bit position (0..63) of the k-th set bit of w, k < popcount(w): halve the window six
-// times by comparing k with the popcount of its low half.
-__device__ __forceinline__ uint32_t select_bit(uint64_t w, uint32_t k) {
-  const uint32_t lo = (uint32_t)w;
-  uint32_t c = __popc(lo);
-  uint32_t x = k >= c ? (uint32_t)(w >> 32) : lo;
-  uint32_t pos = k >= c ? 32u : 0u;
-  k = k >= c ? k - c : k;
-#pragma unroll
-  for (int half = 16; half >= 1; half >>= 1) {
-    c = __popc(x & ((1u << half) - 1u));
-    const bool up = k >= c;
-    k = up ? k - c : k;
-    pos += up ? (uint32_t)half : 0u;
-    x = up ? x >> half : x;
-  }
-  return pos;
 }
 
 // Adds v[r] into tile[cell[r]] (an LDS array) for R independent cells: all reads and the

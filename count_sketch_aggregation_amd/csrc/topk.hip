@@ -21,8 +21,6 @@
 //                kept blocks becomes 0 (the rest already holds g).
 // HBM traffic with error feedback: 12 B per element in the first pass (read gradient and
 // residual, write g) and 8 B in the last (read g, write out), plus 4 B per kept element.
-#include <string.h>
-
 #include "s2r_launch.hpp"
 
 namespace s2r {
