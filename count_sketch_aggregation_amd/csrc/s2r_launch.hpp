@@ -92,9 +92,10 @@ hipError_t launch_decode(const HashArgs& h, const s2r_params& p, uint64_t n,
                          const uint64_t* bitmap, const float* sketch, float* out,
                          uint64_t max_set, void* workspace, size_t ws_bytes, hipStream_t s);
 
-// Workspace of s2r_topk_ef: fp64 keys [W][nb] and a kept-block bitmap [W][sel_words].
+// Workspace of s2r_topk_ef: fp64 keys [W][key_stride] (nb rounded up to even) and a
+// kept-block bitmap [W][sel_words].
 struct TopkLayout {
-  uint64_t nb, sel_words;
+  uint64_t nb, key_stride, sel_words;
   size_t off_keys, off_sel, total;
 };
 TopkLayout topk_layout(uint32_t W, uint64_t n, uint64_t block);

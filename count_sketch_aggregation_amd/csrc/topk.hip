@@ -11,16 +11,19 @@
 //                (per-lane partial sums in index order, then a butterfly across the wave),
 //                stored as the block's 64-bit key; with error feedback g is written back
 //                into the residual, so the last pass reads one array instead of two;
-//   k_tk_select  one workgroup per worker: radix select over the keys (eight 8-bit digits,
-//                most significant first; non-negative fp64 bit patterns order as their
-//                values; the surviving candidates move to LDS once they fit) finds the K-th
-//                largest key T and how many keys equal to T are taken; kept = key > T, plus
-//                the lowest-id keys equal to T when fewer than all of them fit; writes the
-//                kept-block bitmap;
+//   k_tk_select  one workgroup per worker: radix select over the keys (up to eight digits,
+//                sign and exponent first; non-negative fp64 bit patterns order as their
+//                values; the surviving candidates move to LDS once they fit; it stops
+//                early once every key matching the digits chosen so far is taken) finds the
+//                K-th largest key T and how many keys equal to T are taken; kept = key > T,
+//                plus the lowest-id keys equal to T when fewer than all of them fit; writes
+//                the kept-block bitmap;
 //   k_tk_apply   every element: out = g in kept blocks and 0 elsewhere; the residual of
 //                kept blocks becomes 0 (the rest already holds g).
 // HBM traffic with error feedback: 12 B per element in the first pass (read gradient and
 // residual, write g) and 8 B in the last (read g, write out), plus 4 B per kept element.
+#include <atomic>
+
 #include "s2r_launch.hpp"
 
 namespace s2r {
@@ -36,6 +39,7 @@ __global__ __launch_bounds__(kTkNormThreads) void k_tk_norm(const float* __restr
                                                             float* __restrict__ residual,
                                                             uint64_t n, uint64_t ld,
                                                             uint64_t block, uint64_t nb,
+                                                            uint64_t key_stride,
                                                             uint64_t* __restrict__ keys,
                                                             int vec4) {
   const uint32_t k = blockIdx.y;
@@ -82,31 +86,76 @@ __global__ __launch_bounds__(kTkNormThreads) void k_tk_norm(const float* __restr
   }
 #pragma unroll
   for (int off = kWave / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, kWave);
-  if (lane == 0) keys[(uint64_t)k * nb + q] = (uint64_t)__double_as_longlong(acc);
+  if (lane == 0) keys[(uint64_t)k * key_stride + q] = (uint64_t)__double_as_longlong(acc);
 }
 
 // ---------------------------------------------------------------------------------------
-// k_tk_select: grid W, 1024 threads.  Per-wave 256-bin histograms in LDS (64 lanes hitting
-// one bin serialise within a wave only), summed before each digit is chosen.  Passes over
-// global keys keep kTkLoads loads in flight per thread.  As soon as the keys that match the
-// digits chosen so far fit in LDS (kTkCand), the next pass also gathers them there, and the
-// remaining passes read only those.
-constexpr int kTkCand = 6000;  // candidate keys staged in LDS (47 KiB; with the histograms under 64 KiB)
+// k_tk_select: grid W, 1024 threads.  Digits, most significant first: the 12 bits of sign and
+// exponent, six 8-bit digits of the mantissa, its last 4 bits.  The first digit splits the
+// keys by binade (a top 8-bit digit would not: it holds the sign and the exponent's high
+// bits, alike for every norm).  Histograms live in one 4096-entry LDS array: flat for the
+// first digit, as 16 per-wave 256-bin histograms after it, summed before each choice.  Lanes
+// of a wave that share the first live lane's digit add once together (the keys' leading
+// digits are mostly alike, and same-address LDS atomics of one instruction serialise).
+// Passes over global keys read two keys per 16-byte load, kTkLoads loads in flight per
+// thread.  As soon as the keys that match the digits chosen so far fit in LDS (cand_cap,
+// dynamic LDS), the next pass also gathers them there, and the remaining passes read only
+// those.  The digit is chosen by all threads at once (a suffix sum over 4-bin groups).
 constexpr int kTkLoads = 8;
+constexpr int kTkBitmapLoads = 16;
+constexpr int kTkHistWords = 4096;       // 2^12 bins of the first digit
+constexpr uint32_t kTkCandBig = 16384;   // 128 KiB of candidates where the device allows it
+constexpr uint32_t kTkCandSmall = 6000;  // else 47 KiB (with the histograms under 64 KiB)
+typedef unsigned long long u64x2 __attribute__((ext_vector_type(2)));
+
+// Digit p of a key: its lowest bit and its width.
+__device__ __forceinline__ int digit_shift(int p) { return p == 0 ? 52 : (p < 7 ? 52 - 8 * p : 0); }
+__device__ __forceinline__ int digit_bits(int p) { return p == 0 ? 12 : (p < 7 ? 8 : 4); }
+
+// Counts each lane with `on` set into h[digit]; the lanes holding the first live lane's digit
+// add together.
+__device__ __forceinline__ void hist_add(uint32_t* h, uint32_t digit, bool on, int lane) {
+  const uint64_t live = __ballot(on);
+  if (live == 0) return;
+  const int leader = __ffsll((unsigned long long)live) - 1;
+  const uint32_t d0 = (uint32_t)__builtin_amdgcn_readlane((int)digit, leader);
+  const uint64_t same = __ballot(on && digit == d0);
+  if (lane == leader) atomicAdd(&h[d0], (uint32_t)__popcll(same));
+  else if (on && digit != d0) atomicAdd(&h[digit], 1u);
+}
+
+// Appends v to list (count in *n) for each lane with `on` set: one atomic per wave.
+__device__ __forceinline__ void wave_append(uint64_t* list, uint32_t* n, uint64_t v, bool on,
+                                            int lane) {
+  const uint64_t m = __ballot(on);
+  if (m == 0) return;
+  const int leader = __ffsll((unsigned long long)m) - 1;
+  uint32_t base = 0;
+  if (lane == leader) base = atomicAdd(n, (uint32_t)__popcll(m));
+  base = (uint32_t)__builtin_amdgcn_readlane((int)base, leader);
+  if (on) list[base + bits_below_lane(m)] = v;
+}
+
 __global__ __launch_bounds__(kTkSelThreads) void k_tk_select(const uint64_t* __restrict__ keys,
-                                                             uint64_t nb, uint64_t K,
+                                                             uint64_t nb, uint64_t stride,
+                                                             uint64_t K,
                                                              uint64_t* __restrict__ sel,
-                                                             uint64_t sel_words) {
+                                                             uint64_t sel_words,
+                                                             uint32_t cand_cap) {
   constexpr int NW = kTkSelThreads / kWave;
-  __shared__ uint32_t hist[NW][256];
-  __shared__ uint64_t cand[kTkCand];
+  static_assert(kTkHistWords == NW * 256 && kTkHistWords == 4 * kTkSelThreads,
+                "the first digit's histogram is the per-wave histograms' storage, 4 bins a thread");
+  __shared__ uint32_t hist[kTkHistWords];
+  extern __shared__ uint64_t cand[];  // cand_cap keys
   __shared__ uint64_t s_prefix;
   __shared__ uint64_t s_rem, s_eq;
   __shared__ uint32_t s_ncand;
-  __shared__ uint32_t wsum[NW];
+  __shared__ uint64_t wsum[NW];
   const uint32_t k = blockIdx.x;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const uint64_t* key = keys + (uint64_t)k * nb;
+  const uint64_t* key = keys + (uint64_t)k * stride;  // stride even: 16-byte aligned rows
+  const u64x2* key2 = reinterpret_cast<const u64x2*>(key);
+  const uint64_t npairs = (nb + 1) / 2;
   uint64_t* out = sel + (uint64_t)k * sel_words;
 
   uint64_t T = 0, take_eq = 0, n_eq = 0;
@@ -120,32 +169,41 @@ __global__ __launch_bounds__(kTkSelThreads) void k_tk_select(const uint64_t* __r
     }
     bool in_lds = false;
     uint32_t ncand = 0;
-    for (int shift = 56; shift >= 0; shift -= 8) {
-      for (int b = tid; b < NW * 256; b += kTkSelThreads) (&hist[0][0])[b] = 0u;
+    for (int p = 0; p < 8; ++p) {
+      const int shift = digit_shift(p), bits = digit_bits(p);
+      const uint32_t dmask = (1u << bits) - 1u;
+#pragma unroll
+      for (int j = 0; j < kTkHistWords / kTkSelThreads; ++j) hist[tid + j * kTkSelThreads] = 0u;
       __syncthreads();
-      const uint64_t prefix = s_prefix;
-      // keys whose digits above `shift` equal the prefix chosen so far
-      const uint64_t hi_mask = shift == 56 ? 0ull : ~0ull << (shift + 8);
+      const uint64_t prefix = s_prefix, rem = s_rem;
+      // keys whose digits above this one equal the prefix chosen so far
+      const uint64_t hi_mask = shift + bits >= 64 ? 0ull : ~0ull << (shift + bits);
+      uint32_t* h = p == 0 ? hist : hist + wave * 256;
       if (in_lds) {
-        for (uint32_t i = tid; i < ncand; i += kTkSelThreads) {
-          const uint64_t x = cand[i];
-          if (((x ^ prefix) & hi_mask) == 0) atomicAdd(&hist[wave][(x >> shift) & 255u], 1u);
+        for (uint32_t i0 = 0; i0 < ncand; i0 += kTkSelThreads) {
+          const uint32_t i = i0 + tid;
+          const uint64_t x = i < ncand ? cand[i] : 0ull;
+          hist_add(h, (uint32_t)(x >> shift) & dmask, i < ncand && ((x ^ prefix) & hi_mask) == 0,
+                   lane);
         }
       } else {
-        const bool gather = s_eq <= (uint64_t)kTkCand;
-        for (uint64_t i0 = tid; i0 < nb; i0 += (uint64_t)kTkSelThreads * kTkLoads) {
-          uint64_t x[kTkLoads];
+        const bool gather = s_eq <= (uint64_t)cand_cap;
+        for (uint64_t p0 = 0; p0 < npairs; p0 += (uint64_t)kTkSelThreads * kTkLoads) {
+          u64x2 x[kTkLoads];
 #pragma unroll
           for (int u = 0; u < kTkLoads; ++u) {
-            const uint64_t i = i0 + (uint64_t)u * kTkSelThreads;
-            x[u] = i < nb ? key[i] : 0ull;
+            const uint64_t pi = p0 + (uint64_t)u * kTkSelThreads + tid;
+            if (pi < npairs) x[u] = key2[pi];
           }
 #pragma unroll
           for (int u = 0; u < kTkLoads; ++u) {
-            const uint64_t i = i0 + (uint64_t)u * kTkSelThreads;
-            if (i < nb && ((x[u] ^ prefix) & hi_mask) == 0) {
-              atomicAdd(&hist[wave][(x[u] >> shift) & 255u], 1u);
-              if (gather) cand[atomicAdd(&s_ncand, 1u)] = x[u];
+            const uint64_t pi = p0 + (uint64_t)u * kTkSelThreads + tid;
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+              const uint64_t xv = e ? x[u].y : x[u].x;
+              const bool on = 2 * pi + e < nb && ((xv ^ prefix) & hi_mask) == 0;
+              hist_add(h, (uint32_t)(xv >> shift) & dmask, on, lane);
+              if (gather) wave_append(cand, &s_ncand, xv, on, lane);
             }
           }
         }
@@ -153,25 +211,46 @@ __global__ __launch_bounds__(kTkSelThreads) void k_tk_select(const uint64_t* __r
       }
       __syncthreads();
       ncand = s_ncand;
-      if (tid < 256) {
+      if (p > 0 && tid < 256) {
         uint32_t c = 0;
-        for (int v = 0; v < NW; ++v) c += hist[v][tid];
-        hist[0][tid] = c;
+        for (int v = 0; v < NW; ++v) c += hist[v * 256 + tid];
+        hist[tid] = c;
       }
       __syncthreads();
-      if (tid == 0) {
-        // from the largest digit down: the digit where the running count reaches s_rem
-        uint64_t rem = s_rem, above = 0;
-        int b = 255;
-        for (; b > 0; --b) {
-          if (above + hist[0][b] >= rem) break;
-          above += hist[0][b];
+      // The digit taken is the largest b whose count from the top (bins >= b) reaches rem.
+      // Thread t holds bins 4t..4t+3; with suf(t) the count of the bins of threads >= t, the
+      // one thread with suf(t) >= rem > suf(t + 1) holds it.
+      const int nbins = 1 << bits;
+      uint64_t c[4] = {0, 0, 0, 0}, tot = 0;
+      if (4 * tid < nbins) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) tot += (c[j] = hist[4 * tid + j]);
+      }
+      uint64_t suf = tot;
+#pragma unroll
+      for (int off = 1; off < kWave; off <<= 1) {
+        const uint64_t t = __shfl_down(suf, off, kWave);
+        if (lane + off < kWave) suf += t;
+      }
+      if (lane == 0) wsum[wave] = suf;
+      __syncthreads();
+      for (int v = wave + 1; v < NW; ++v) suf += wsum[v];
+      uint64_t above = suf - tot;  // suf(t + 1)
+      if (suf >= rem && above < rem) {
+#pragma unroll
+        for (int j = 3; j >= 0; --j) {
+          if (above + c[j] >= rem) {
+            s_rem = rem - above;
+            s_prefix = prefix | ((uint64_t)(4 * tid + j) << shift);
+            s_eq = c[j];
+            break;
+          }
+          above += c[j];
         }
-        s_rem = rem - above;
-        s_prefix = prefix | ((uint64_t)b << shift);
-        s_eq = hist[0][b];
       }
       __syncthreads();
+      // every key matching the prefix is taken: the keys kept are those >= the prefix
+      if (s_rem == s_eq) break;
     }
     T = s_prefix;
     take_eq = s_rem;  // 1 <= take_eq <= n_eq
@@ -180,7 +259,7 @@ __global__ __launch_bounds__(kTkSelThreads) void k_tk_select(const uint64_t* __r
 
   // kept-block bitmap, 64 keys per wave step
   if (all || none || take_eq == n_eq) {
-    constexpr int U = 4;
+    constexpr int U = kTkBitmapLoads;
     for (uint64_t b0 = (uint64_t)wave * kWave; b0 < nb; b0 += (uint64_t)kTkSelThreads * U) {
       uint64_t x[U];
 #pragma unroll
@@ -205,7 +284,7 @@ __global__ __launch_bounds__(kTkSelThreads) void k_tk_select(const uint64_t* __r
       const uint64_t x = i < nb ? key[i] : 0ull;
       const bool tie = i < nb && x == T;
       const uint64_t tb = __ballot(tie);
-      if (lane == 0) wsum[wave] = (uint32_t)__popcll(tb);
+      if (lane == 0) wsum[wave] = (uint64_t)__popcll(tb);
       __syncthreads();
       uint64_t before = carry, total = 0;
       for (int v = 0; v < NW; ++v) {
@@ -284,13 +363,37 @@ __global__ __launch_bounds__(kTkApplyThreads) void k_tk_apply(const float* __res
 // ---------------------------------------------------------------------------------------
 // host side
 
+// Dynamic LDS beyond the default per-launch limit is allowed once per device; where the
+// device refuses, the select kernel stages fewer candidates.
+static uint32_t select_cand_cap() {
+  constexpr int kMaxDevices = 64;
+  static std::atomic<uint32_t> cap[kMaxDevices];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    (void)hipGetLastError();
+    return kTkCandSmall;
+  }
+  uint32_t c = cap[dev].load(std::memory_order_relaxed);
+  if (c != 0) return c;
+  c = kTkCandBig;
+  if (hipFuncSetAttribute(reinterpret_cast<const void*>(&k_tk_select),
+                          hipFuncAttributeMaxDynamicSharedMemorySize,
+                          (int)(kTkCandBig * sizeof(uint64_t))) != hipSuccess) {
+    (void)hipGetLastError();
+    c = kTkCandSmall;
+  }
+  cap[dev].store(c, std::memory_order_relaxed);
+  return c;
+}
+
 TopkLayout topk_layout(uint32_t W, uint64_t n, uint64_t block) {
   TopkLayout L;
   L.nb = block ? (n + block - 1) / block : 0;
+  L.key_stride = (L.nb + 1) & ~(uint64_t)1;
   L.sel_words = (L.nb + 63) / 64;
   size_t off = 0;
   L.off_keys = off;
-  off += ((size_t)W * L.nb * 8 + 255) & ~(size_t)255;
+  off += ((size_t)W * L.key_stride * 8 + 255) & ~(size_t)255;
   L.off_sel = off;
   off += ((size_t)W * L.sel_words * 8 + 255) & ~(size_t)255;
   L.total = off > 0 ? off : 256;
@@ -308,11 +411,12 @@ hipError_t launch_topk(uint32_t W, const float* grad, float* residual, uint64_t 
   const int vec4 = (block % 4 == 0) && (ld % 4 == 0);
   const uint64_t ngroups = (L.nb + kTkNormThreads / kWave - 1) / (kTkNormThreads / kWave);
   hipLaunchKernelGGL(k_tk_norm, dim3((uint32_t)ngroups, W), dim3(kTkNormThreads), 0, s, grad,
-                     residual, n, ld, block, L.nb, keys, vec4);
+                     residual, n, ld, block, L.nb, L.key_stride, keys, vec4);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_tk_select, dim3(W), dim3(kTkSelThreads), 0, s, keys, L.nb, K, sel,
-                     L.sel_words);
+  const uint32_t cap = select_cand_cap();
+  hipLaunchKernelGGL(k_tk_select, dim3(W), dim3(kTkSelThreads), cap * sizeof(uint64_t), s, keys,
+                     L.nb, L.key_stride, K, sel, L.sel_words, cap);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   const uint64_t per = 4ull * kTkApplyThreads * kTkApplyIters;
