@@ -54,21 +54,27 @@ constexpr int kDBinBatchWords = kDBinThreads * kDBinWordsPerThread;  // 2048 wor
 // nwords = ceil(n / 64).  With a block-granular bitmap (lb = log2 B > 0) the word is built
 // from the block bits: all ones or zeros for B >= 64, else each of its 64/B block bits
 // spread over B element bits.
-__device__ __forceinline__ uint64_t masked_word(const uint64_t* __restrict__ bitmap,
-                                                uint64_t nwords, uint64_t n, uint64_t q,
-                                                uint32_t lb) {
+// The bitmap word that element word q (< nwords) is built from: q itself, or the word
+// holding q's block bits.
+__device__ __forceinline__ uint64_t masked_src(uint64_t q, uint32_t lb) {
+  return lb == 0 ? q : ((q * 64) >> lb) >> 6;
+}
+
+// Element word q built from raw = bitmap[masked_src(q, lb)]; 0 for q >= nwords.
+__device__ __forceinline__ uint64_t masked_from(uint64_t raw, uint64_t nwords, uint64_t n,
+                                                uint64_t q, uint32_t lb) {
   if (q >= nwords) return 0ull;
   const uint64_t first = q * 64;
   uint64_t wv;
   if (lb == 0) {
-    wv = bitmap[q];
+    wv = raw;
   } else if (lb >= 6) {
     const uint64_t b = first >> lb;
-    wv = ((bitmap[b >> 6] >> (b & 63)) & 1ull) ? ~0ull : 0ull;
+    wv = ((raw >> (b & 63)) & 1ull) ? ~0ull : 0ull;
   } else {
     const uint32_t B = 1u << lb, per = 64u >> lb;  // B <= 32, per <= 32
     const uint64_t b0 = first >> lb;               // a multiple of per: one bitmap word
-    const uint64_t bits = (bitmap[b0 >> 6] >> (b0 & 63)) & ((1ull << per) - 1ull);
+    const uint64_t bits = (raw >> (b0 & 63)) & ((1ull << per) - 1ull);
     const uint64_t ones = (1ull << B) - 1ull;
     wv = 0ull;
     for (uint32_t t = 0; t < per; ++t)
@@ -76,6 +82,15 @@ __device__ __forceinline__ uint64_t masked_word(const uint64_t* __restrict__ bit
   }
   if (n - first < 64) wv &= (1ull << (n - first)) - 1ull;
   return wv;
+}
+
+// Element word q (0 for q >= nwords; nwords > 0): the load is unconditional, at a clamped
+// index, so that several of them issue back to back.
+__device__ __forceinline__ uint64_t masked_word(const uint64_t* __restrict__ bitmap,
+                                                uint64_t nwords, uint64_t n, uint64_t q,
+                                                uint32_t lb) {
+  const uint64_t raw = bitmap[masked_src(q < nwords ? q : nwords - 1, lb)];
+  return masked_from(raw, nwords, n, q, lb);
 }
 
 // ---------------------------------------------------------------------------------------
@@ -115,6 +130,7 @@ __global__ __launch_bounds__(kDBinThreads) void k_dbin(HashArgs h, uint64_t n,
   const uint32_t c = blockIdx.x;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const uint64_t U = ws.toff[tiles];
+  const uint32_t t0 = ws.chunk_tile[c];  // loaded with U (c < chunks); meaningful if start < U
   if (U > ws.max_set) return;  // over capacity: k_dwrite decodes directly
   const uint64_t start = (uint64_t)c * kChunk;
   if (start >= U) return;
@@ -124,15 +140,19 @@ __global__ __launch_bounds__(kDBinThreads) void k_dbin(HashArgs h, uint64_t n,
   // 1. expand ranks [start, end) into litem, 2048 bitmap words per round: each thread holds
   //    4 words and their ranks, and the waves expand only the non-empty words that meet
   //    the chunk (expand_owned_words)
-  const uint32_t t0 = ws.chunk_tile[c];
   uint64_t q0 = (uint64_t)t0 * kDecWords;
   uint64_t rank0 = ws.toff[t0];
   while (rank0 < end && q0 < nwords) {
     uint64_t wv[kDBinWordsPerThread];
     uint32_t sum = 0;
 #pragma unroll
+    for (int u = 0; u < kDBinWordsPerThread; ++u) {  // all loads first, then the masking
+      const uint64_t q = q0 + (uint64_t)tid * kDBinWordsPerThread + u;
+      wv[u] = bitmap[masked_src(q < nwords ? q : nwords - 1, h.lb)];
+    }
+#pragma unroll
     for (int u = 0; u < kDBinWordsPerThread; ++u) {
-      wv[u] = masked_word(bitmap, nwords, n, q0 + (uint64_t)tid * kDBinWordsPerThread + u, h.lb);
+      wv[u] = masked_from(wv[u], nwords, n, q0 + (uint64_t)tid * kDBinWordsPerThread + u, h.lb);
       sum += (uint32_t)__popcll(wv[u]);
     }
     const uint32_t inc = wave_inclusive_sum(sum);

@@ -9,7 +9,7 @@
 //                 into element-ordered bitmap words through LDS; writes the bitmap and one
 //                 non-zero count per 4096-element tile.
 //   k_scan_sum, k_scan
-//                 per (16384-tile block, worker): exclusive prefix of the tile counts (list
+//                 per (4096-tile block, worker): exclusive prefix of the tile counts (list
 //                 offsets), nnz, and the lists of non-empty tile pairs, sparse and dense.
 //   k_blockbits   (block-granular bitmaps only) folds the element bitmap into block bits.
 //   k_expand_dense, k_expand_sparse
@@ -101,9 +101,9 @@ __global__ __launch_bounds__(kStreamThreads) void k_stream(
 
 // ---------------------------------------------------------------------------------------
 // k_scan: grid (blocks, W), 1024 threads; block b of worker k scans tiles
-// [b * kScanPass, (b + 1) * kScanPass): coalesced loads into LDS, one contiguous run of 16 per
-// thread for the block scan (read with a 1-in-16 padding so the 64 lanes hit distinct
-// banks), offsets written back through LDS with coalesced stores.  The block starts from the
+// [b * kScanPass, (b + 1) * kScanPass): coalesced loads into LDS, one contiguous run of
+// kScanPass / 1024 per thread for the block scan (read with a 1-in-16 padding), offsets
+// written back through LDS with coalesced stores.  The block starts from the
 // totals of the blocks before it (btot, from k_scan_sum; none with one block).
 // Optionally (spans != nullptr) it also lists the spans (tile pairs) that hold a non-zero,
 // for k_expand: the sparse ones (at most kDenseSpan non-zeros) in order from the front of
@@ -111,6 +111,13 @@ __global__ __launch_bounds__(kStreamThreads) void k_stream(
 // nspan[2k + 1].  And, for every chunk of kChunk consecutive list positions below `limit`,
 // it records the tile holding its first position.
 __device__ __forceinline__ uint32_t scan_pad(uint32_t i) { return i + (i >> 4); }
+
+// p[i] for i < n, else 0 (n > 0): an unconditional load of a clamped index, so that a
+// thread's loads issue back to back rather than as one guarded round trip each.
+__device__ __forceinline__ uint32_t load_or_zero(const uint32_t* p, uint64_t i, uint64_t n) {
+  const uint32_t v = p[i < n ? i : n - 1];
+  return i < n ? v : 0u;
+}
 
 __global__ __launch_bounds__(kScanThreads) void k_scan_sum(uint64_t tiles,
                                                            const uint32_t* __restrict__ counts,
@@ -120,11 +127,18 @@ __global__ __launch_bounds__(kScanThreads) void k_scan_sum(uint64_t tiles,
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const uint32_t* cnt = counts + (uint64_t)k * tiles;
   const uint64_t base = (uint64_t)b * kScanPass;
+  constexpr int U = kScanPass / 2 / kScanThreads;
+  uint32_t x[2 * U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const uint64_t i = base + 2 * (uint64_t)(tid + kScanThreads * u);  // a span's first tile
+    x[2 * u] = load_or_zero(cnt, i, tiles);
+    x[2 * u + 1] = load_or_zero(cnt, i + 1, tiles);
+  }
   uint32_t sum = 0, ns = 0, nd = 0;
 #pragma unroll
-  for (int u = 0; u < kScanPass / 2 / kScanThreads; ++u) {
-    const uint64_t i = base + 2 * (uint64_t)(tid + kScanThreads * u);  // a span's first tile
-    const uint32_t c = (i < tiles ? cnt[i] : 0u) + (i + 1 < tiles ? cnt[i + 1] : 0u);
+  for (int u = 0; u < U; ++u) {
+    const uint32_t c = x[2 * u] + x[2 * u + 1];
     sum += c;
     ns += (c && c <= kDenseSpan) ? 1u : 0u;
     nd += c > kDenseSpan ? 1u : 0u;
@@ -154,7 +168,8 @@ __global__ __launch_bounds__(kScanThreads) void k_scan(
     uint64_t* __restrict__ nnz, uint32_t* __restrict__ chunk_tile, uint64_t chunks,
     uint64_t limit, const uint4* __restrict__ btot, uint32_t* __restrict__ spans,
     uint32_t* __restrict__ nspan) {
-  constexpr int PER = kScanPass / kScanThreads;  // 16 tiles = 8 spans per thread
+  constexpr int PER = kScanPass / kScanThreads;  // tiles per thread, whole spans
+  static_assert(PER % 2 == 0, "a thread's run holds whole spans");
   constexpr int NW = kScanThreads / kWave;
   __shared__ uint32_t lc[kScanPass + kScanPass / 16];
   __shared__ uint32_t wsum[3][NW];
@@ -191,10 +206,12 @@ __global__ __launch_bounds__(kScanThreads) void k_scan(
     }
     __syncthreads();  // wsum is reused below
   }
+  {
+    uint32_t x[PER];
 #pragma unroll
-  for (int u = 0; u < PER; ++u) {
-    const uint32_t i = tid + kScanThreads * u;
-    lc[scan_pad(i)] = base + i < tiles ? cnt[base + i] : 0u;
+    for (int u = 0; u < PER; ++u) x[u] = load_or_zero(cnt, base + tid + kScanThreads * u, tiles);
+#pragma unroll
+    for (int u = 0; u < PER; ++u) lc[scan_pad(tid + kScanThreads * u)] = x[u];
   }
   __syncthreads();
   uint32_t v[PER], sum = 0, ns = 0, nd = 0;
@@ -569,16 +586,21 @@ __global__ __launch_bounds__(kAccThreads) void k_accumulate(
   for (uint32_t cb = 0; cb < nch; cb += kSegBatch) {
     const uint32_t nb = nch - cb < (uint32_t)kSegBatch ? nch - cb : (uint32_t)kSegBatch;
     __syncthreads();  // the previous batch is consumed (and the tile is zeroed)
-    uint32_t len[PER], sum = 0;
+    uint32_t lo[PER], hi[PER], len[PER], sum = 0;
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {  // clamped, unconditional loads: all in flight at once
+      const uint32_t c = tid * PER + u < nb ? tid * PER + u : nb - 1;
+      const uint64_t row = (uint64_t)(cb + c) * (partitions + 1);
+      lo[u] = pf[row];
+      hi[u] = pf[row + 1];
+    }
 #pragma unroll
     for (int u = 0; u < PER; ++u) {
       const uint32_t c = tid * PER + u;
       len[u] = 0;
       if (c < nb) {
-        const uint64_t row = (uint64_t)(cb + c) * (partitions + 1);
-        const uint32_t lo = pf[row], hi = pf[row + 1];
-        seg_src[c] = (cb + c) * (uint32_t)kChunk + lo;
-        len[u] = hi - lo;
+        seg_src[c] = (cb + c) * (uint32_t)kChunk + lo[u];
+        len[u] = hi[u] - lo[u];
       }
       sum += len[u];
     }

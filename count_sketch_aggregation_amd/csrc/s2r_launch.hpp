@@ -33,7 +33,9 @@ constexpr size_t kAccLdsBytes = 64 * 1024;          // LDS of one partition tile
 constexpr uint64_t kCacheResidentBytes = 256ull << 20;  // MI355X Infinity Cache
 
 constexpr int kScanThreads = 1024;
-constexpr uint32_t kScanPass = kScanThreads * 16;  // tiles per scan block
+// tiles per scan block: small enough that the blocks spread over many CUs (one CU writes
+// its offsets and span lists slowly), four per thread so the loads all fly together
+constexpr uint32_t kScanPass = kScanThreads * 4;
 
 // Workspace layout of s2r_encode (every section 256-byte aligned).
 struct EncodeLayout {
