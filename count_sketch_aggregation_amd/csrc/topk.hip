@@ -302,13 +302,38 @@ __global__ __launch_bounds__(kTkSelThreads) void k_tk_select(const uint64_t* __r
 }
 
 // ---------------------------------------------------------------------------------------
-// k_tk_apply: grid (ceil(n / (4 * 256 * kTkApplyIters)), W).  Each thread takes float4
-// groups; the group's first element fixes its block by one division, the others follow.
+// k_tk_apply: grid (ceil(n / (4 * 256 * kTkApplyIters)), W).  Each thread takes
+// kTkApplyIters float4 groups, 1024 elements apart.  A group's first element gives its block
+// by a multiply-high division (below); the others follow by counting.  Away from the row's
+// end every load of the thread (data and kept-block words) is issued before any is used.
 constexpr int kTkApplyIters = 4;
+
+// Unsigned division by a divisor fixed for the launch, exact for every 32-bit dividend:
+// the round-up multiplier method of Granlund & Montgomery, "Division by invariant integers
+// using multiplication" (1994), Section 4.  With l = ceil(log2 d),
+// m = floor(2^32 (2^l - d) / d) + 1 and t = mulhi(m, x): x / d = (t + ((x - t) >> s1)) >> s2,
+// s1 = min(l, 1), s2 = max(l - 1, 0).
+struct DivU32 {
+  uint32_t d, m, s1, s2;
+};
+__device__ __forceinline__ uint32_t div_u32(const DivU32& v, uint32_t x) {
+  const uint32_t t = __umulhi(v.m, x);
+  return (t + ((x - t) >> v.s1)) >> v.s2;
+}
+static DivU32 make_div_u32(uint32_t d) {  // d >= 1
+  DivU32 v;
+  uint32_t l = 0;
+  while (l < 32 && (1ull << l) < d) ++l;
+  v.d = d;
+  v.m = (uint32_t)((((1ull << 32) * ((1ull << l) - d)) / d) + 1);
+  v.s1 = l < 1 ? l : 1;
+  v.s2 = l > 0 ? l - 1 : 0;
+  return v;
+}
+
 __global__ __launch_bounds__(kTkApplyThreads) void k_tk_apply(const float* __restrict__ grad,
                                                               float* __restrict__ residual,
-                                                              uint64_t n, uint64_t ld,
-                                                              uint64_t block,
+                                                              uint64_t n, uint64_t ld, DivU32 dv,
                                                               const uint64_t* __restrict__ sel,
                                                               uint64_t sel_words,
                                                               float* __restrict__ out) {
@@ -318,43 +343,69 @@ __global__ __launch_bounds__(kTkApplyThreads) void k_tk_apply(const float* __res
   const float* src = residual ? residual + (uint64_t)k * ld : grad + (uint64_t)k * ld;
   float* rs = residual ? residual + (uint64_t)k * ld : nullptr;
   float* o = out + (uint64_t)k * ld;
+  const uint32_t d = dv.d;  // the block size, or n when the block holds the whole row
+  constexpr uint64_t kStep = 4ull * kTkApplyThreads;
+  const uint64_t e0 = 4 * ((uint64_t)blockIdx.x * kTkApplyThreads * kTkApplyIters + threadIdx.x);
+  if (e0 + kStep * (kTkApplyIters - 1) + 4 <= n) {
+    // every group whole and inside the row (ld % 4 == 0: aligned float4 groups)
+    f32x4 g[kTkApplyIters];
+    uint64_t w0[kTkApplyIters], w1[kTkApplyIters];
+    uint32_t q[kTkApplyIters], r[kTkApplyIters];
 #pragma unroll
-  for (int it = 0; it < kTkApplyIters; ++it) {
-    const uint64_t e = 4 * ((uint64_t)blockIdx.x * kTkApplyThreads * kTkApplyIters +
-                            (uint64_t)it * kTkApplyThreads + threadIdx.x);
-    if (e >= n) break;
-    uint64_t q = e / block;
-    uint64_t r = e - q * block;
-    bool kept[4];
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      kept[c] = e + c < n && ((sk[q >> 6] >> (q & 63)) & 1ull);
-      if (++r == block) {
-        r = 0;
-        ++q;
-      }
+    for (int it = 0; it < kTkApplyIters; ++it) {
+      const uint32_t e = (uint32_t)(e0 + kStep * it);
+      q[it] = div_u32(dv, e);
+      r[it] = e - q[it] * d;
+      const uint32_t q3 = div_u32(dv, e + 3);  // block of the group's last element
+      w0[it] = sk[q[it] >> 6];
+      w1[it] = sk[q3 >> 6];  // the group's blocks span at most these two words
+      g[it] = *reinterpret_cast<const f32x4*>(src + e);
     }
-    if (e + 4 <= n) {  // ld % 4 == 0 and e % 4 == 0: the group is aligned and inside the row
-      const f32x4 g = *reinterpret_cast<const f32x4*>(src + e);
+#pragma unroll
+    for (int it = 0; it < kTkApplyIters; ++it) {
+      const uint64_t e = e0 + kStep * it;
+      bool kept[4];
+      uint32_t qc = q[it], rc = r[it];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const uint64_t w = (qc >> 6) == (q[it] >> 6) ? w0[it] : w1[it];
+        kept[c] = (w >> (qc & 63)) & 1ull;
+        if (++rc == d) {
+          rc = 0;
+          ++qc;
+        }
+      }
       f32x4 v;
-      v.x = kept[0] ? g.x : 0.f;
-      v.y = kept[1] ? g.y : 0.f;
-      v.z = kept[2] ? g.z : 0.f;
-      v.w = kept[3] ? g.w : 0.f;
+      v.x = kept[0] ? g[it].x : 0.f;
+      v.y = kept[1] ? g[it].y : 0.f;
+      v.z = kept[2] ? g[it].z : 0.f;
+      v.w = kept[3] ? g[it].w : 0.f;
       *reinterpret_cast<f32x4*>(o + e) = v;
       if (rs && (kept[0] | kept[1] | kept[2] | kept[3])) {
         f32x4 z;
-        z.x = kept[0] ? 0.f : g.x;
-        z.y = kept[1] ? 0.f : g.y;
-        z.z = kept[2] ? 0.f : g.z;
-        z.w = kept[3] ? 0.f : g.w;
+        z.x = kept[0] ? 0.f : g[it].x;
+        z.y = kept[1] ? 0.f : g[it].y;
+        z.z = kept[2] ? 0.f : g[it].z;
+        z.w = kept[3] ? 0.f : g[it].w;
         *reinterpret_cast<f32x4*>(rs + e) = z;
       }
-    } else {
-      for (int c = 0; c < 4 && e + c < n; ++c) {
-        const float g = src[e + c];
-        o[e + c] = kept[c] ? g : 0.f;
-        if (rs && kept[c]) rs[e + c] = 0.f;
+    }
+    return;
+  }
+  // the row's end: group by group, element by element past n
+  for (int it = 0; it < kTkApplyIters; ++it) {
+    const uint64_t e = e0 + kStep * it;
+    if (e >= n) break;
+    uint32_t qc = div_u32(dv, (uint32_t)e);
+    uint32_t rc = (uint32_t)e - qc * d;
+    for (int c = 0; c < 4 && e + c < n; ++c) {
+      const bool kept = (sk[qc >> 6] >> (qc & 63)) & 1ull;
+      const float gv = src[e + c];
+      o[e + c] = kept ? gv : 0.f;
+      if (rs && kept) rs[e + c] = 0.f;
+      if (++rc == d) {
+        rc = 0;
+        ++qc;
       }
     }
   }
@@ -420,8 +471,10 @@ hipError_t launch_topk(uint32_t W, const float* grad, float* residual, uint64_t 
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   const uint64_t per = 4ull * kTkApplyThreads * kTkApplyIters;
+  // blocks beyond n hold the whole row: dividing by n gives the same block ids (all 0)
+  const DivU32 dv = make_div_u32((uint32_t)(block < n ? block : n));
   hipLaunchKernelGGL(k_tk_apply, dim3((uint32_t)((n + per - 1) / per), W), dim3(kTkApplyThreads), 0,
-                     s, grad, residual, n, ld, block, sel, L.sel_words, out);
+                     s, grad, residual, n, ld, dv, sel, L.sel_words, out);
   return hipGetLastError();
 }
 

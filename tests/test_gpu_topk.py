@@ -41,6 +41,9 @@ CASES = [
     ("K_more", 2, 10_000, 10_000, 64, 10_000, False),
     ("n_small", 3, 5, 8, 2, 2, True),
     ("many_blocks", 2, 2_000_000, 2_000_000, 16, 12_500, True),
+    ("block3", 2, 30_001, 30_004, 3, 2_000, True),
+    ("block1000", 2, 250_000, 250_000, 1000, 25, True),
+    ("block_beyond_n", 2, 100_000, 100_000, 1 << 31, 1, True),
 ]
 
 
