@@ -94,11 +94,14 @@ hipError_t launch_decode(const HashArgs& h, const s2r_params& p, uint64_t n,
                          const uint64_t* bitmap, const float* sketch, float* out,
                          uint64_t max_set, void* workspace, size_t ws_bytes, hipStream_t s);
 
-// Workspace of s2r_topk_ef: fp64 keys [W][key_stride] (nb rounded up to even) and a
-// kept-block bitmap [W][sel_words].
+// Workspace of s2r_topk_ef: fp64 keys [W][key_stride] (nb rounded up to even), a kept-block
+// bitmap [W][sel_words] (used when the caller passes none), the select's per-worker scratch
+// (global digit histograms and candidate count), gathered candidates [W][16384] and the
+// per-worker select outcome.
 struct TopkLayout {
   uint64_t nb, key_stride, sel_words;
-  size_t off_keys, off_sel, total;
+  uint32_t scratch_words;
+  size_t off_keys, off_sel, off_scratch, off_gcand, off_outcome, total;
 };
 TopkLayout topk_layout(uint32_t W, uint64_t n, uint64_t block);
 hipError_t launch_topk(uint32_t W, const float* grad, float* residual, uint64_t n, uint64_t ld,

@@ -41,9 +41,14 @@ __global__ __launch_bounds__(kTkNormThreads) void k_tk_norm(const float* __restr
                                                             uint64_t block, uint64_t nb,
                                                             uint64_t key_stride,
                                                             uint64_t* __restrict__ keys,
-                                                            int vec4) {
+                                                            int vec4,
+                                                            uint32_t* __restrict__ zero,
+                                                            uint32_t zero_words) {
   const uint32_t k = blockIdx.y;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  if (blockIdx.x == 0)  // the worker's select histograms and candidate count start at zero
+    for (uint32_t i = threadIdx.x; i < zero_words; i += kTkNormThreads)
+      zero[(uint64_t)k * zero_words + i] = 0u;
   const uint64_t q = (uint64_t)blockIdx.x * (kTkNormThreads / kWave) + wave;
   if (q >= nb) return;  // whole wave
   const uint64_t first = q * block;
@@ -90,30 +95,49 @@ __global__ __launch_bounds__(kTkNormThreads) void k_tk_norm(const float* __restr
 }
 
 // ---------------------------------------------------------------------------------------
-// k_tk_select: grid W, 1024 threads.  Digits, most significant first: the 12 bits of sign and
-// exponent, six 8-bit digits of the mantissa, its last 4 bits.  The first digit splits the
-// keys by binade (a top 8-bit digit would not: it holds the sign and the exponent's high
-// bits, alike for every norm).  Histograms live in one 4096-entry LDS array: flat for the
-// first digit, as 16 per-wave 256-bin histograms after it, summed before each choice.  Lanes
-// of a wave that share the first live lane's digit add once together (the keys' leading
-// digits are mostly alike, and same-address LDS atomics of one instruction serialise).
-// Passes over global keys read two keys per 16-byte load, kTkLoads loads in flight per
-// thread.  As soon as the keys that match the digits chosen so far fit in LDS (cand_cap,
-// dynamic LDS), the next pass also gathers them there, and the remaining passes read only
-// those.  The digit is chosen by all threads at once (a suffix sum over 4-bin groups).
+// Radix select of the K largest keys of each worker.  Digits, most significant first: the 12
+// bits of sign and exponent, six 8-bit digits of the mantissa, its last 4 bits.  The first
+// digit splits the keys by binade (a top 8-bit digit would not: it holds the sign and the
+// exponent's high bits, alike for every norm).  After each digit's histogram, the digit
+// taken is the largest b whose count from the top (bins >= b) reaches the number still to
+// take; the keys matching the digits taken so far are the candidates of the next digit.
+//
+// The first three digits are histogrammed by wide grids (k_tk_hist, one launch per digit,
+// global histograms), every workgroup first replaying the earlier choices from the global
+// histograms.  The first of those passes whose candidates fit in cand_cap keys also gathers
+// them into a global list.  k_tk_select (one workgroup per worker) replays the three choices,
+// finishes from the gathered list in LDS (or, if nothing fitted, from the keys, gathering into
+// LDS as soon as the candidates fit), and in the rare case that only some keys equal to the
+// K-th largest are taken writes the kept-block bitmap itself; otherwise k_tk_bitmap writes it
+// from the threshold, over a wide grid.
 constexpr int kTkLoads = 8;
-constexpr int kTkBitmapLoads = 16;
 constexpr int kTkHistWords = 4096;       // 2^12 bins of the first digit
+constexpr int kTkGlobalPasses = 3;       // digits histogrammed by the wide grids
+constexpr int kTkHistThreads = 256;
+constexpr uint32_t kTkSliceKeys = 2048;  // keys per k_tk_hist workgroup
 constexpr uint32_t kTkCandBig = 16384;   // 128 KiB of candidates where the device allows it
 constexpr uint32_t kTkCandSmall = 6000;  // else 47 KiB (with the histograms under 64 KiB)
+// Per-worker select scratch (uint32 words): the global histograms of the first three digits,
+// then the gathered-candidate count.
+constexpr uint32_t kTkScratchCount = kTkHistWords + 2 * 256;
+constexpr uint32_t kTkScratchWords = kTkScratchCount + 4;
 typedef unsigned long long u64x2 __attribute__((ext_vector_type(2)));
 
 // Digit p of a key: its lowest bit and its width.
 __device__ __forceinline__ int digit_shift(int p) { return p == 0 ? 52 : (p < 7 ? 52 - 8 * p : 0); }
 __device__ __forceinline__ int digit_bits(int p) { return p == 0 ? 12 : (p < 7 ? 8 : 4); }
+// Offset of digit p's histogram in a worker's global histograms (p < kTkGlobalPasses).
+__device__ __forceinline__ int ghist_offset(int p) { return p == 0 ? 0 : kTkHistWords + 256 * (p - 1); }
+
+// Select state: the digits taken so far (prefix), how many keys matching them are still to
+// be taken (rem) and how many match (eq); 1 <= rem <= eq.
+struct TkState {
+  uint64_t prefix, rem, eq;
+};
 
 // Counts each lane with `on` set into h[digit]; the lanes holding the first live lane's digit
-// add together.
+// add together (same-address LDS atomics of one instruction serialise, and the keys' leading
+// digits are mostly alike).
 __device__ __forceinline__ void hist_add(uint32_t* h, uint32_t digit, bool on, int lane) {
   const uint64_t live = __ballot(on);
   if (live == 0) return;
@@ -124,33 +148,172 @@ __device__ __forceinline__ void hist_add(uint32_t* h, uint32_t digit, bool on, i
   else if (on && digit != d0) atomicAdd(&h[digit], 1u);
 }
 
-// Appends v to list (count in *n) for each lane with `on` set: one atomic per wave.
-__device__ __forceinline__ void wave_append(uint64_t* list, uint32_t* n, uint64_t v, bool on,
-                                            int lane) {
+// Appends v to list (count in *n, LDS or global; room for cap) for each lane with `on` set:
+// one atomic per wave.  The callers append exactly as many keys as fit; the bound is a guard.
+__device__ __forceinline__ void wave_append(uint64_t* list, uint32_t* n, uint32_t cap,
+                                            uint64_t v, bool on, int lane) {
   const uint64_t m = __ballot(on);
   if (m == 0) return;
   const int leader = __ffsll((unsigned long long)m) - 1;
   uint32_t base = 0;
   if (lane == leader) base = atomicAdd(n, (uint32_t)__popcll(m));
   base = (uint32_t)__builtin_amdgcn_readlane((int)base, leader);
-  if (on) list[base + bits_below_lane(m)] = v;
+  const uint32_t at = base + bits_below_lane(m);
+  if (on && at < cap) list[at] = v;
 }
 
+// Chooses digit p from its histogram h[0 .. 2^bits) (LDS) and returns the new state to every
+// thread of the block.  Thread t holds a run of bins; with suf(t) the count of the bins of
+// threads >= t, the one thread with suf(t) >= rem > suf(t + 1) holds the digit.  wsum: one
+// slot per wave; out: LDS.  Ends with a barrier.
+template <int THREADS>
+__device__ TkState choose_digit(const uint32_t* h, int p, TkState st, uint64_t* wsum,
+                                TkState* out) {
+  constexpr int PER = kTkHistWords / THREADS;
+  constexpr int NW = THREADS / kWave;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int nbins = 1 << digit_bits(p);
+  uint64_t c[PER], tot = 0;
+#pragma unroll
+  for (int j = 0; j < PER; ++j) {
+    c[j] = PER * tid + j < nbins ? h[PER * tid + j] : 0u;
+    tot += c[j];
+  }
+  uint64_t suf = tot;
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+    const uint64_t t = __shfl_down(suf, off, kWave);
+    if (lane + off < kWave) suf += t;
+  }
+  if (lane == 0) wsum[wave] = suf;
+  __syncthreads();
+  for (int v = wave + 1; v < NW; ++v) suf += wsum[v];
+  uint64_t above = suf - tot;  // suf(t + 1)
+  if (suf >= st.rem && above < st.rem) {
+#pragma unroll
+    for (int j = PER - 1; j >= 0; --j) {
+      if (above + c[j] >= st.rem) {
+        TkState r;
+        r.rem = st.rem - above;
+        r.prefix = st.prefix | ((uint64_t)(PER * tid + j) << digit_shift(p));
+        r.eq = c[j];
+        *out = r;
+        break;
+      }
+      above += c[j];
+    }
+  }
+  __syncthreads();
+  const TkState r = *out;
+  __syncthreads();  // out and wsum may be rewritten next
+  return r;
+}
+
+// Replays the choices of digits 0 .. upto-1 from the worker's global histograms; eqs[q]
+// receives the candidate count after digit q.  True when a choice took every candidate
+// (rem == eq): the select is then complete, with the keys >= prefix kept.
+template <int THREADS>
+__device__ bool replay_digits(const uint32_t* gh, int upto, TkState& st, uint64_t* eqs,
+                              uint32_t* hist, uint64_t* wsum, TkState* out) {
+  for (int q = 0; q < upto; ++q) {
+    const int nbins = 1 << digit_bits(q);
+    for (int i = threadIdx.x; i < nbins; i += THREADS) hist[i] = gh[ghist_offset(q) + i];
+    __syncthreads();
+    st = choose_digit<THREADS>(hist, q, st, wsum, out);
+    eqs[q] = st.eq;
+    if (st.rem == st.eq) return true;
+  }
+  return false;
+}
+
+// The pass whose gathered candidates the select reads: the first of passes 1 .. 2 whose
+// candidate count (after the previous digit) fits, else 0.
+__device__ __forceinline__ int gather_pass(const uint64_t* eqs, uint32_t cap) {
+  if (eqs[0] <= cap) return 1;
+  if (eqs[1] <= cap) return 2;
+  return 0;
+}
+
+// k_tk_hist: grid (ceil(nb / kTkSliceKeys), W), 256 threads; histograms digit p over the
+// workgroup's slice of the keys matching the digits already taken, adds it into the global
+// histogram, and gathers those keys into the global list when this pass is the gather pass.
+__global__ __launch_bounds__(kTkHistThreads) void k_tk_hist(
+    const uint64_t* __restrict__ keys, uint64_t nb, uint64_t stride, uint64_t K, int p,
+    uint32_t* __restrict__ ghist, uint32_t ghist_words, uint64_t* __restrict__ gcand,
+    uint32_t cand_cap) {
+  constexpr int NW = kTkHistThreads / kWave;
+  __shared__ uint32_t hist[kTkHistWords];
+  __shared__ uint64_t wsum[NW];
+  __shared__ TkState s_out;
+  const uint32_t k = blockIdx.y;
+  const int tid = threadIdx.x, lane = tid & 63;
+  if (K == 0 || K >= nb) return;  // nothing to select
+  // the slice's keys are loaded first: their latency overlaps the replay
+  const uint64_t* key = keys + (uint64_t)k * stride;  // stride even: 16-byte aligned rows
+  const u64x2* key2 = reinterpret_cast<const u64x2*>(key);
+  const uint64_t lo = (uint64_t)blockIdx.x * kTkSliceKeys;  // even
+  const uint64_t hi = lo + kTkSliceKeys < nb ? lo + kTkSliceKeys : nb;
+  constexpr int U = kTkSliceKeys / 2 / kTkHistThreads;  // 16-byte loads per thread
+  u64x2 x[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const uint64_t pi = lo / 2 + (uint64_t)u * kTkHistThreads + tid;
+    x[u] = key2[2 * pi < hi ? pi : (hi - 1) / 2];  // clamped: the loads issue together
+  }
+  uint32_t* gh = ghist + (uint64_t)k * ghist_words;
+  TkState st = {0ull, K, nb};
+  uint64_t eqs[kTkGlobalPasses] = {nb, nb, nb};
+  if (replay_digits<kTkHistThreads>(gh, p, st, eqs, hist, wsum, &s_out)) return;
+  const bool gather = p >= 1 && gather_pass(eqs, cand_cap) == p;
+  for (int i = tid; i < kTkHistWords; i += kTkHistThreads) hist[i] = 0u;
+  __syncthreads();
+  const int shift = digit_shift(p), bits = digit_bits(p);
+  const uint32_t dmask = (1u << bits) - 1u;
+  const uint64_t hi_mask = shift + bits >= 64 ? 0ull : ~0ull << (shift + bits);
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const uint64_t pi = lo / 2 + (uint64_t)u * kTkHistThreads + tid;
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const uint64_t xv = e ? x[u].y : x[u].x;
+      const bool on = 2 * pi + e < hi && ((xv ^ st.prefix) & hi_mask) == 0;
+      hist_add(hist, (uint32_t)(xv >> shift) & dmask, on, lane);
+      if (gather)
+        wave_append(gcand + (uint64_t)k * cand_cap, gh + kTkScratchCount, cand_cap, xv, on, lane);
+    }
+  }
+  __syncthreads();
+  for (int i = tid; i < (1 << bits); i += kTkHistThreads)
+    if (hist[i]) atomicAdd(&gh[ghist_offset(p) + i], hist[i]);
+}
+
+// Per-worker outcome of the select for k_tk_bitmap: keys >= thr are kept (mode 0), all keys
+// (1), none (2), or the bitmap is already written (3).
+struct TkOutcome {
+  uint64_t thr;
+  uint64_t mode;
+};
+
+// k_tk_select: grid W, 1024 threads.  Per-wave 256-bin histograms in LDS for the digits it
+// histograms itself, summed before each choice.  Passes over global keys read two keys per
+// 16-byte load, kTkLoads loads in flight per thread.
 __global__ __launch_bounds__(kTkSelThreads) void k_tk_select(const uint64_t* __restrict__ keys,
                                                              uint64_t nb, uint64_t stride,
                                                              uint64_t K,
                                                              uint64_t* __restrict__ sel,
                                                              uint64_t sel_words,
-                                                             uint32_t cand_cap) {
+                                                             uint32_t cand_cap,
+                                                             const uint32_t* __restrict__ ghist,
+                                                             uint32_t ghist_words,
+                                                             const uint64_t* __restrict__ gcand,
+                                                             TkOutcome* __restrict__ outcome) {
   constexpr int NW = kTkSelThreads / kWave;
-  static_assert(kTkHistWords == NW * 256 && kTkHistWords == 4 * kTkSelThreads,
-                "the first digit's histogram is the per-wave histograms' storage, 4 bins a thread");
+  static_assert(kTkHistWords == NW * 256, "the per-wave histograms share the first digit's");
   __shared__ uint32_t hist[kTkHistWords];
   extern __shared__ uint64_t cand[];  // cand_cap keys
-  __shared__ uint64_t s_prefix;
-  __shared__ uint64_t s_rem, s_eq;
   __shared__ uint32_t s_ncand;
   __shared__ uint64_t wsum[NW];
+  __shared__ TkState s_out;
   const uint32_t k = blockIdx.x;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const uint64_t* key = keys + (uint64_t)k * stride;  // stride even: 16-byte aligned rows
@@ -158,147 +321,133 @@ __global__ __launch_bounds__(kTkSelThreads) void k_tk_select(const uint64_t* __r
   const uint64_t npairs = (nb + 1) / 2;
   uint64_t* out = sel + (uint64_t)k * sel_words;
 
-  uint64_t T = 0, take_eq = 0, n_eq = 0;
+  TkState st = {0ull, K, nb};
   const bool all = K >= nb, none = K == 0;
   if (!all && !none) {
-    if (tid == 0) {
-      s_prefix = 0;
-      s_rem = K;
-      s_eq = nb;  // keys matching the (empty) prefix
-      s_ncand = 0;
-    }
-    bool in_lds = false;
-    uint32_t ncand = 0;
-    for (int p = 0; p < 8; ++p) {
-      const int shift = digit_shift(p), bits = digit_bits(p);
-      const uint32_t dmask = (1u << bits) - 1u;
-#pragma unroll
-      for (int j = 0; j < kTkHistWords / kTkSelThreads; ++j) hist[tid + j * kTkSelThreads] = 0u;
-      __syncthreads();
-      const uint64_t prefix = s_prefix, rem = s_rem;
-      // keys whose digits above this one equal the prefix chosen so far
-      const uint64_t hi_mask = shift + bits >= 64 ? 0ull : ~0ull << (shift + bits);
-      uint32_t* h = p == 0 ? hist : hist + wave * 256;
-      if (in_lds) {
-        for (uint32_t i0 = 0; i0 < ncand; i0 += kTkSelThreads) {
-          const uint32_t i = i0 + tid;
-          const uint64_t x = i < ncand ? cand[i] : 0ull;
-          hist_add(h, (uint32_t)(x >> shift) & dmask, i < ncand && ((x ^ prefix) & hi_mask) == 0,
-                   lane);
-        }
-      } else {
-        const bool gather = s_eq <= (uint64_t)cand_cap;
-        for (uint64_t p0 = 0; p0 < npairs; p0 += (uint64_t)kTkSelThreads * kTkLoads) {
-          u64x2 x[kTkLoads];
-#pragma unroll
-          for (int u = 0; u < kTkLoads; ++u) {
-            const uint64_t pi = p0 + (uint64_t)u * kTkSelThreads + tid;
-            if (pi < npairs) x[u] = key2[pi];
+    uint64_t eqs[kTkGlobalPasses] = {nb, nb, nb};
+    if (!replay_digits<kTkSelThreads>(ghist + (uint64_t)k * ghist_words, kTkGlobalPasses, st,
+                                      eqs, hist, wsum, &s_out)) {
+      bool in_lds = false;
+      uint32_t ncand = 0;
+      if (tid == 0) s_ncand = 0;
+      const int gp = gather_pass(eqs, cand_cap);
+      if (gp > 0) {  // the gathered candidates: every key matching the digits before pass gp
+        ncand = ghist[(uint64_t)k * ghist_words + kTkScratchCount];  // == eqs[gp - 1] <= cap
+        if (ncand > cand_cap) ncand = cand_cap;
+        const uint64_t* gc = gcand + (uint64_t)k * cand_cap;
+        for (uint32_t i = tid; i < ncand; i += kTkSelThreads) cand[i] = gc[i];
+        in_lds = true;
+      }
+      for (int p = kTkGlobalPasses; p < 8; ++p) {
+        const int shift = digit_shift(p), bits = digit_bits(p);
+        const uint32_t dmask = (1u << bits) - 1u;
+        for (int i = tid; i < kTkHistWords; i += kTkSelThreads) hist[i] = 0u;
+        __syncthreads();
+        // keys whose digits above this one equal the prefix chosen so far
+        const uint64_t hi_mask = shift + bits >= 64 ? 0ull : ~0ull << (shift + bits);
+        uint32_t* h = hist + wave * 256;
+        if (in_lds) {
+          for (uint32_t i0 = 0; i0 < ncand; i0 += kTkSelThreads) {
+            const uint32_t i = i0 + tid;
+            const uint64_t x = i < ncand ? cand[i] : 0ull;
+            hist_add(h, (uint32_t)(x >> shift) & dmask,
+                     i < ncand && ((x ^ st.prefix) & hi_mask) == 0, lane);
           }
+        } else {
+          const bool gather = st.eq <= (uint64_t)cand_cap;
+          for (uint64_t p0 = 0; p0 < npairs; p0 += (uint64_t)kTkSelThreads * kTkLoads) {
+            u64x2 x[kTkLoads];
 #pragma unroll
-          for (int u = 0; u < kTkLoads; ++u) {
-            const uint64_t pi = p0 + (uint64_t)u * kTkSelThreads + tid;
+            for (int u = 0; u < kTkLoads; ++u) {
+              const uint64_t pi = p0 + (uint64_t)u * kTkSelThreads + tid;
+              if (pi < npairs) x[u] = key2[pi];
+            }
 #pragma unroll
-            for (int e = 0; e < 2; ++e) {
-              const uint64_t xv = e ? x[u].y : x[u].x;
-              const bool on = 2 * pi + e < nb && ((xv ^ prefix) & hi_mask) == 0;
-              hist_add(h, (uint32_t)(xv >> shift) & dmask, on, lane);
-              if (gather) wave_append(cand, &s_ncand, xv, on, lane);
+            for (int u = 0; u < kTkLoads; ++u) {
+              const uint64_t pi = p0 + (uint64_t)u * kTkSelThreads + tid;
+#pragma unroll
+              for (int e = 0; e < 2; ++e) {
+                const uint64_t xv = e ? x[u].y : x[u].x;
+                const bool on = 2 * pi + e < nb && ((xv ^ st.prefix) & hi_mask) == 0;
+                hist_add(h, (uint32_t)(xv >> shift) & dmask, on, lane);
+                if (gather) wave_append(cand, &s_ncand, cand_cap, xv, on, lane);
+              }
             }
           }
+          if (gather) in_lds = true;  // uniform: st is the same in every thread
         }
-        if (gather) in_lds = true;  // uniform: s_eq was read by every thread
-      }
-      __syncthreads();
-      ncand = s_ncand;
-      if (p > 0 && tid < 256) {
-        uint32_t c = 0;
-        for (int v = 0; v < NW; ++v) c += hist[v * 256 + tid];
-        hist[tid] = c;
-      }
-      __syncthreads();
-      // The digit taken is the largest b whose count from the top (bins >= b) reaches rem.
-      // Thread t holds bins 4t..4t+3; with suf(t) the count of the bins of threads >= t, the
-      // one thread with suf(t) >= rem > suf(t + 1) holds it.
-      const int nbins = 1 << bits;
-      uint64_t c[4] = {0, 0, 0, 0}, tot = 0;
-      if (4 * tid < nbins) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) tot += (c[j] = hist[4 * tid + j]);
-      }
-      uint64_t suf = tot;
-#pragma unroll
-      for (int off = 1; off < kWave; off <<= 1) {
-        const uint64_t t = __shfl_down(suf, off, kWave);
-        if (lane + off < kWave) suf += t;
-      }
-      if (lane == 0) wsum[wave] = suf;
-      __syncthreads();
-      for (int v = wave + 1; v < NW; ++v) suf += wsum[v];
-      uint64_t above = suf - tot;  // suf(t + 1)
-      if (suf >= rem && above < rem) {
-#pragma unroll
-        for (int j = 3; j >= 0; --j) {
-          if (above + c[j] >= rem) {
-            s_rem = rem - above;
-            s_prefix = prefix | ((uint64_t)(4 * tid + j) << shift);
-            s_eq = c[j];
-            break;
-          }
-          above += c[j];
+        __syncthreads();
+        if (gp == 0) ncand = s_ncand < cand_cap ? s_ncand : cand_cap;  // gathered here, if any
+        if (tid < 256) {
+          uint32_t c = 0;
+          for (int v = 0; v < NW; ++v) c += hist[v * 256 + tid];
+          hist[tid] = c;
         }
+        __syncthreads();
+        st = choose_digit<kTkSelThreads>(hist, p, st, wsum, &s_out);
+        // every key matching the prefix is taken: the keys kept are those >= the prefix
+        if (st.rem == st.eq) break;
       }
-      __syncthreads();
-      // every key matching the prefix is taken: the keys kept are those >= the prefix
-      if (s_rem == s_eq) break;
     }
-    T = s_prefix;
-    take_eq = s_rem;  // 1 <= take_eq <= n_eq
-    n_eq = s_eq;
   }
+  const uint64_t T = st.prefix, take_eq = st.rem, n_eq = st.eq;  // 1 <= take_eq <= n_eq
 
-  // kept-block bitmap, 64 keys per wave step
   if (all || none || take_eq == n_eq) {
-    constexpr int U = kTkBitmapLoads;
-    for (uint64_t b0 = (uint64_t)wave * kWave; b0 < nb; b0 += (uint64_t)kTkSelThreads * U) {
-      uint64_t x[U];
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const uint64_t i = b0 + (uint64_t)u * kTkSelThreads + lane;
-        x[u] = (i < nb && !all && !none) ? key[i] : 0ull;
-      }
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const uint64_t base = b0 + (uint64_t)u * kTkSelThreads;
-        const bool kept = base + lane < nb && (all || (!none && x[u] >= T));
-        const uint64_t word = __ballot(kept);
-        if (lane == 0 && base < nb) out[base / 64] = word;
-      }
+    if (tid == 0) {
+      TkOutcome o;
+      o.thr = T;
+      o.mode = all ? 1u : (none ? 2u : 0u);
+      outcome[k] = o;
     }
-  } else {
-    // only some keys equal to T fit: they go to the lowest block ids, so the tie rank is a
-    // prefix count in id order, chunk by chunk
-    uint64_t carry = 0;
-    for (uint64_t base = 0; base < nb; base += kTkSelThreads) {
-      const uint64_t i = base + tid;
-      const uint64_t x = i < nb ? key[i] : 0ull;
-      const bool tie = i < nb && x == T;
-      const uint64_t tb = __ballot(tie);
-      if (lane == 0) wsum[wave] = (uint64_t)__popcll(tb);
-      __syncthreads();
-      uint64_t before = carry, total = 0;
-      for (int v = 0; v < NW; ++v) {
-        if (v < wave) before += wsum[v];
-        total += wsum[v];
-      }
-      const uint64_t rank = before + bits_below_lane(tb);
-      const bool kept = i < nb && (x > T || (tie && rank < take_eq));
-      const uint64_t word = __ballot(kept);
-      if (lane == 0 && i < nb) out[i / 64] = word;
-      carry += total;
-      __syncthreads();  // wsum is rewritten next chunk
-    }
+    return;
   }
+  if (tid == 0) {
+    TkOutcome o;
+    o.thr = T;
+    o.mode = 3u;
+    outcome[k] = o;
+  }
+  // only some keys equal to T fit: they go to the lowest block ids, so the tie rank is a
+  // prefix count in id order, chunk by chunk
+  uint64_t carry = 0;
+  for (uint64_t base = 0; base < nb; base += kTkSelThreads) {
+    const uint64_t i = base + tid;
+    const uint64_t x = i < nb ? key[i] : 0ull;
+    const bool tie = i < nb && x == T;
+    const uint64_t tb = __ballot(tie);
+    if (lane == 0) wsum[wave] = (uint64_t)__popcll(tb);
+    __syncthreads();
+    uint64_t before = carry, total = 0;
+    for (int v = 0; v < NW; ++v) {
+      if (v < wave) before += wsum[v];
+      total += wsum[v];
+    }
+    const uint64_t rank = before + bits_below_lane(tb);
+    const bool kept = i < nb && (x > T || (tie && rank < take_eq));
+    const uint64_t word = __ballot(kept);
+    if (lane == 0 && i < nb) out[i / 64] = word;
+    carry += total;
+    __syncthreads();  // wsum is rewritten next chunk
+  }
+}
+
+// k_tk_bitmap: grid (ceil(sel_words / 4), W), 256 threads: one wave per kept-block word from
+// the select's outcome (nothing to do where the select wrote the bitmap itself).
+__global__ __launch_bounds__(256) void k_tk_bitmap(const uint64_t* __restrict__ keys,
+                                                   uint64_t nb, uint64_t stride,
+                                                   const TkOutcome* __restrict__ outcome,
+                                                   uint64_t* __restrict__ sel,
+                                                   uint64_t sel_words) {
+  const uint32_t k = blockIdx.y;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const uint64_t q = (uint64_t)blockIdx.x * 4 + wave;
+  const TkOutcome o = outcome[k];
+  if (q >= sel_words || o.mode == 3u) return;  // whole wave
+  const uint64_t i = q * 64 + lane;
+  const uint64_t x = i < nb && o.mode == 0u ? keys[(uint64_t)k * stride + i] : 0ull;
+  const bool kept = i < nb && (o.mode == 1u || (o.mode == 0u && x >= o.thr));
+  const uint64_t word = __ballot(kept);
+  if (lane == 0) sel[(uint64_t)k * sel_words + q] = word;
 }
 
 // ---------------------------------------------------------------------------------------
@@ -447,7 +596,14 @@ TopkLayout topk_layout(uint32_t W, uint64_t n, uint64_t block) {
   off += ((size_t)W * L.key_stride * 8 + 255) & ~(size_t)255;
   L.off_sel = off;
   off += ((size_t)W * L.sel_words * 8 + 255) & ~(size_t)255;
-  L.total = off > 0 ? off : 256;
+  L.scratch_words = kTkScratchWords;
+  L.off_scratch = off;
+  off += ((size_t)W * L.scratch_words * 4 + 255) & ~(size_t)255;
+  L.off_gcand = off;
+  off += (size_t)W * kTkCandBig * 8;
+  L.off_outcome = off;
+  off += ((size_t)W * sizeof(TkOutcome) + 255) & ~(size_t)255;
+  L.total = off;
   return L;
 }
 
@@ -459,15 +615,33 @@ hipError_t launch_topk(uint32_t W, const float* grad, float* residual, uint64_t 
   char* ws = static_cast<char*>(workspace);
   uint64_t* keys = reinterpret_cast<uint64_t*>(ws + L.off_keys);
   uint64_t* sel = selected ? selected : reinterpret_cast<uint64_t*>(ws + L.off_sel);
+  uint32_t* scratch = reinterpret_cast<uint32_t*>(ws + L.off_scratch);  // [W][scratch_words]
+  uint64_t* gcand = reinterpret_cast<uint64_t*>(ws + L.off_gcand);
+  TkOutcome* outcome = reinterpret_cast<TkOutcome*>(ws + L.off_outcome);
   const int vec4 = (block % 4 == 0) && (ld % 4 == 0);
   const uint64_t ngroups = (L.nb + kTkNormThreads / kWave - 1) / (kTkNormThreads / kWave);
   hipLaunchKernelGGL(k_tk_norm, dim3((uint32_t)ngroups, W), dim3(kTkNormThreads), 0, s, grad,
-                     residual, n, ld, block, L.nb, L.key_stride, keys, vec4);
+                     residual, n, ld, block, L.nb, L.key_stride, keys, vec4, scratch,
+                     L.scratch_words);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const uint32_t cap = select_cand_cap();
+  if (K > 0 && K < L.nb) {  // else the select has nothing to histogram
+    const uint32_t slices = (uint32_t)((L.nb + kTkSliceKeys - 1) / kTkSliceKeys);
+    for (int p = 0; p < kTkGlobalPasses; ++p) {
+      hipLaunchKernelGGL(k_tk_hist, dim3(slices, W), dim3(kTkHistThreads), 0, s, keys, L.nb,
+                         L.key_stride, K, p, scratch, L.scratch_words, gcand, cap);
+      e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
+  }
   hipLaunchKernelGGL(k_tk_select, dim3(W), dim3(kTkSelThreads), cap * sizeof(uint64_t), s, keys,
-                     L.nb, L.key_stride, K, sel, L.sel_words, cap);
+                     L.nb, L.key_stride, K, sel, L.sel_words, cap, scratch, L.scratch_words,
+                     gcand, outcome);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k_tk_bitmap, dim3((uint32_t)((L.sel_words + 3) / 4), W), dim3(256), 0, s,
+                     keys, L.nb, L.key_stride, outcome, sel, L.sel_words);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   const uint64_t per = 4ull * kTkApplyThreads * kTkApplyIters;

@@ -76,6 +76,23 @@ def test_topk_ties_by_block_id(K):
     gp.assert_topk_matches(grads, res, n, block, K, out, res_out, sel, f"ties K={K}")
 
 
+@pytest.mark.parametrize("K", [100, 5_000, 59_000])
+def test_topk_large_tie_group(K):
+    """60,000 blocks, all but 100 of them with one identical norm: more equal keys than any
+    candidate list holds, so the select ranks the whole tie group from the keys themselves;
+    K inside the group keeps the lowest block ids, K = 100 keeps exactly the distinct ones."""
+    W, n, block = 2, 240_000, 4
+    gp.say(f"topk large tie group K={K}")
+    grads = np.ones((W, n), dtype=np.float32)
+    for k in range(W):
+        rows = np.random.default_rng(70 + k).choice(n // block, 100, replace=False)
+        for r in rows:
+            grads[k, r * block:(r + 1) * block] = 2.0
+    res = np.zeros_like(grads)
+    out, res_out, sel = gp.run_topk(grads, res, n, block, K)
+    gp.assert_topk_matches(grads, res, n, block, K, out, res_out, sel, f"tie group K={K}")
+
+
 def test_topk_zero_blocks_fill_K():
     """Fewer non-zero blocks than K: the zero blocks tie at 0 and the lowest ids fill K."""
     W, n, block, K = 2, 6400, 64, 30
