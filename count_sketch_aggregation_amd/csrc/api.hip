@@ -64,7 +64,7 @@ EncodeLayout encode_layout(const s2r_params& p, uint32_t W, uint64_t n, uint64_t
   L.off_btot = off;
   off = align256(off + (size_t)W * scan_blocks(L.tiles) * 16);
   L.off_spans = off;
-  off = align256(off + (size_t)W * ((L.tiles + 1) / 2) * 4);
+  off = align256(off + (size_t)W * ((L.tiles + 1) / 2) * 8);
   L.off_nspan = off;
   off = align256(off + (size_t)W * 8);
   L.off_ebm = off;  // element bitmaps when the output bitmap is block-granular
@@ -166,11 +166,11 @@ s2r_status s2r_encode(const s2r_params* p, uint32_t W, const float* grad, uint64
   if (p->log2_block)
     S2R_TRY(launch_blockbits(W, ebm, words, n, p->log2_block,
                              s2r_block_bitmap_words(n, p->log2_block), bitmaps, s));
-  uint32_t* spans = reinterpret_cast<uint32_t*>(ws + L.off_spans);
+  uint2* spans = reinterpret_cast<uint2*>(ws + L.off_spans);
   uint32_t* nspan = reinterpret_cast<uint32_t*>(ws + L.off_nspan);
   S2R_TRY(launch_scan(W, L.tiles, counts, offsets, nnz, nullptr, 0, cap,
                       reinterpret_cast<uint4*>(ws + L.off_btot), spans, nspan, s));
-  S2R_TRY(launch_expand(W, grad, ld, L.tiles, ebm, words, offsets, spans, nspan, idx, val, cap, s));
+  S2R_TRY(launch_expand(W, grad, ld, L.tiles, ebm, words, spans, nspan, idx, val, cap, s));
   if (L.partitioned) {
     uint2* bins = reinterpret_cast<uint2*>(ws + L.off_bins);
     uint32_t* prefix = reinterpret_cast<uint32_t*>(ws + L.off_prefix);

@@ -166,7 +166,7 @@ __global__ __launch_bounds__(kScanThreads) void k_scan_sum(uint64_t tiles,
 __global__ __launch_bounds__(kScanThreads) void k_scan(
     uint64_t tiles, const uint32_t* __restrict__ counts, uint32_t* __restrict__ offsets,
     uint64_t* __restrict__ nnz, uint32_t* __restrict__ chunk_tile, uint64_t chunks,
-    uint64_t limit, const uint4* __restrict__ btot, uint32_t* __restrict__ spans,
+    uint64_t limit, const uint4* __restrict__ btot, uint2* __restrict__ spans,
     uint32_t* __restrict__ nspan) {
   constexpr int PER = kScanPass / kScanThreads;  // tiles per thread, whole spans
   static_assert(PER % 2 == 0, "a thread's run holds whole spans");
@@ -179,7 +179,7 @@ __global__ __launch_bounds__(kScanThreads) void k_scan(
   uint32_t* off = offsets + (uint64_t)k * (tiles + 1);
   uint32_t* ct = chunk_tile + (uint64_t)k * chunks;
   const uint64_t nsp = (tiles + 1) / 2;
-  uint32_t* sp = spans ? spans + (uint64_t)k * nsp : nullptr;
+  uint2* sp = spans ? spans + (uint64_t)k * nsp : nullptr;
   const uint64_t base = (uint64_t)b * kScanPass;
   uint32_t carry = 0, scarry = 0, dcarry = 0;
   if (b > 0) {  // totals of the blocks before this one
@@ -259,7 +259,8 @@ __global__ __launch_bounds__(kScanThreads) void k_scan(
     }
     if (sp && (u & 1)) {
       const uint32_t c = v[u - 1] + v[u];
-      const uint32_t span = (uint32_t)((t0 + u) >> 1);
+      // the span and the list position of its first pair (run still holds v[u - 1])
+      const uint2 span = make_uint2((uint32_t)((t0 + u) >> 1), run - v[u - 1]);
       if (c > kDenseSpan) sp[nsp - 1 - drun++] = span;
       else if (c) sp[srun++] = span;
     }
@@ -283,17 +284,18 @@ __global__ __launch_bounds__(kScanThreads) void k_scan(
 
 // ---------------------------------------------------------------------------------------
 // k_expand_dense / k_expand_sparse: list the non-empty spans (tile pairs of 8192 elements and
-// 128 words, from k_scan), so empty regions cost nothing.  Each writes a span's pairs at list
-// positions offsets[2 t] + (rank within the span), re-reading only the 16-byte gradient
-// groups that hold a set bit.
+// 128 words, from k_scan, each with the list position of its first pair), so empty regions
+// cost nothing.  Each writes a span's pairs at that position + (rank within the span),
+// re-reading only the 16-byte gradient groups that hold a set bit; the next span's entry is
+// loaded while the current one is expanded.
 //   dense spans (more than kDenseSpan non-zeros), grid (G, W), 256 threads: a workgroup per
 //     span; the words and their popcount prefix go to LDS and each thread takes 8 groups of
 //     four elements, all 8 loads issued before use;
 //   sparse spans, grid (G, W), 256 threads: a wave per span, so four spans per workgroup are
 //     in flight with no workgroup barrier; lane l loads words 2l and 2l+1, a wave prefix sum
 //     of their popcounts gives every word's rank offset, both go to the wave's own LDS rows,
-//     and lane l takes the groups g = l + 64 m (m = 0..31), kExpandUnroll at a time (a round
-//     with no set group issues no load).
+//     and lane l owns the groups g = l + 64 m (m = 0..31): it lists those holding a set bit
+//     and loads them kExpandUnroll at a time.
 constexpr int kExpandSpan = 2 * kTile;
 constexpr int kExpandWords = kExpandSpan / 64;  // 128
 constexpr int kExpandWaves = kExpandThreads / kWave;
@@ -316,22 +318,24 @@ __device__ __forceinline__ void expand_store(uint32_t* oi, float* ov, uint64_t c
 
 __global__ __launch_bounds__(kExpandThreads) void k_expand_dense(
     const float* __restrict__ grad, uint64_t ld, uint64_t tiles,
-    const uint64_t* __restrict__ bitmaps, uint64_t words, const uint32_t* __restrict__ offsets,
-    const uint32_t* __restrict__ spans, const uint32_t* __restrict__ nspan,
-    uint32_t* __restrict__ idx, float* __restrict__ val, uint64_t cap) {
+    const uint64_t* __restrict__ bitmaps, uint64_t words, const uint2* __restrict__ spans,
+    const uint32_t* __restrict__ nspan, uint32_t* __restrict__ idx, float* __restrict__ val,
+    uint64_t cap) {
   const uint32_t k = blockIdx.y;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const uint32_t* off = offsets + (uint64_t)k * (tiles + 1);
   const uint64_t nsp = (tiles + 1) / 2;
-  const uint32_t* sl = spans + (uint64_t)k * nsp;
+  const uint2* sl = spans + (uint64_t)k * nsp;
   const uint32_t nd = nspan[2 * k + 1];
   __shared__ uint64_t lwords[kExpandWords];
   __shared__ uint32_t lwoff[kExpandWords + 2];
   uint32_t* oi = idx + (uint64_t)k * cap;
   float* ov = val + (uint64_t)k * cap;
+  uint2 next = blockIdx.x < nd ? sl[nsp - 1 - blockIdx.x] : make_uint2(0u, 0u);
   for (uint32_t si = blockIdx.x; si < nd; si += gridDim.x) {
-    const uint32_t t = sl[nsp - 1 - si];
-    const uint64_t o_t = off[2ull * t];
+    const uint32_t t = next.x;
+    const uint64_t o_t = next.y;
+    // the following span's entry, one round trip ahead
+    if (si + gridDim.x < nd) next = sl[nsp - 1 - (si + gridDim.x)];
     if (o_t >= cap) continue;  // beyond the list capacity (uniform)
     if (tid < kExpandWords) {
       const uint64_t q = (uint64_t)t * kExpandWords + tid;
@@ -377,14 +381,13 @@ __device__ __forceinline__ void wave_lds_sync() {
 
 __global__ __launch_bounds__(kExpandThreads) void k_expand_sparse(
     const float* __restrict__ grad, uint64_t ld, uint64_t tiles,
-    const uint64_t* __restrict__ bitmaps, uint64_t words, const uint32_t* __restrict__ offsets,
-    const uint32_t* __restrict__ spans, const uint32_t* __restrict__ nspan,
-    uint32_t* __restrict__ idx, float* __restrict__ val, uint64_t cap) {
+    const uint64_t* __restrict__ bitmaps, uint64_t words, const uint2* __restrict__ spans,
+    const uint32_t* __restrict__ nspan, uint32_t* __restrict__ idx, float* __restrict__ val,
+    uint64_t cap) {
   const uint32_t k = blockIdx.y;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const uint32_t* off = offsets + (uint64_t)k * (tiles + 1);
   const uint64_t nsp = (tiles + 1) / 2;
-  const uint32_t* sl = spans + (uint64_t)k * nsp;
+  const uint2* sl = spans + (uint64_t)k * nsp;
   const uint32_t ns = nspan[2 * k];
   __shared__ uint64_t lwords[kExpandWaves][kExpandWords];
   __shared__ uint32_t lwoff[kExpandWaves][kExpandWords];
@@ -393,9 +396,12 @@ __global__ __launch_bounds__(kExpandThreads) void k_expand_sparse(
   uint32_t* oi = idx + (uint64_t)k * cap;
   float* ov = val + (uint64_t)k * cap;
   const uint32_t stride = gridDim.x * kExpandWaves;
-  for (uint32_t si = blockIdx.x * kExpandWaves + wave; si < ns; si += stride) {
-    const uint32_t t = sl[si];
-    const uint64_t o_t = off[2ull * t];
+  const uint32_t s0 = blockIdx.x * kExpandWaves + wave;
+  uint2 next = s0 < ns ? sl[s0] : make_uint2(0u, 0u);
+  for (uint32_t si = s0; si < ns; si += stride) {
+    const uint32_t t = next.x;
+    const uint64_t o_t = next.y;
+    if (si + stride < ns) next = sl[si + stride];  // one round trip ahead
     if (o_t >= cap) continue;  // beyond the list capacity (wave-uniform)
     uint64_t wv[2];
     uint32_t pc[2];
@@ -413,26 +419,38 @@ __global__ __launch_bounds__(kExpandThreads) void k_expand_sparse(
     lo[2 * lane + 1] = inc - pc[1];
     wave_lds_sync();
     const float* row = grad + (uint64_t)k * ld + (uint64_t)t * kExpandSpan;
+    // lane l owns groups g = l + 64 m (m = 0..31): word (l >> 4) + 4 m, nibble 4 (l & 15).
+    // Its set groups are listed first, then taken kExpandUnroll at a time, so the wave makes
+    // one round trip per kExpandUnroll set groups of its busiest lane.
+    const int sh = 4 * (lane & 15), qb = lane >> 4;
+    uint32_t mask = 0;
+#pragma unroll
+    for (int m = 0; m < kExpandSpan / 4 / kWave; ++m)
+      mask |= (uint32_t)(((lw[qb + 4 * m] >> sh) & 0xFull) != 0ull) << m;
     constexpr int UN = kExpandUnroll;
-#pragma unroll 1
-    for (int m0 = 0; m0 < kExpandSpan / 4 / kWave; m0 += UN) {
+    while (__ballot(mask != 0u) != 0ull) {
       f32x4 v[UN];
-      uint32_t nib[UN], pos0[UN];
+      uint32_t nib[UN], pos0[UN], g[UN];
 #pragma unroll
       for (int u = 0; u < UN; ++u) {
-        const int g = lane + kWave * (m0 + u);
-        const int q = g >> 4, sh = 4 * (g & 15);
+        const bool has = mask != 0u;
+        const int m = has ? __builtin_ctz(mask) : 0;
+        mask &= mask - 1u;  // 0 stays 0
+        g[u] = (uint32_t)(lane + kWave * m);
+        const int q = qb + 4 * m;
         const uint64_t w = lw[q];
-        nib[u] = (uint32_t)(w >> sh) & 0xFu;
+        nib[u] = has ? (uint32_t)(w >> sh) & 0xFu : 0u;
         pos0[u] = lo[q] + (uint32_t)__popcll(w & ((1ull << sh) - 1ull));
-        if (nib[u]) v[u] = *reinterpret_cast<const f32x4*>(row + 4 * g);
+        // unconditional, so the loads issue together: a lane with nothing left reads the
+        // span's first group, which lies inside the row (the span holds a set bit, and
+        // ld % 4 == 0); a set group lies below n <= ld, 4-aligned
+        v[u] = *reinterpret_cast<const f32x4*>(row + (has ? 4u * g[u] : 0u));
       }
 #pragma unroll
       for (int u = 0; u < UN; ++u)
         if (nib[u])
-          expand_store(oi, ov, cap, o_t + pos0[u],
-                       t * (uint32_t)kExpandSpan + 4u * (uint32_t)(lane + kWave * (m0 + u)),
-                       nib[u], v[u]);
+          expand_store(oi, ov, cap, o_t + pos0[u], t * (uint32_t)kExpandSpan + 4u * g[u], nib[u],
+                       v[u]);
     }
   }
 }
@@ -731,7 +749,7 @@ uint32_t scan_blocks(uint64_t tiles) {
 
 hipError_t launch_scan(uint32_t W, uint64_t tiles, const uint32_t* counts, uint32_t* offsets,
                        uint64_t* nnz, uint32_t* chunk_tile, uint64_t chunks, uint64_t cap,
-                       uint4* btot, uint32_t* spans, uint32_t* nspan, hipStream_t s) {
+                       uint4* btot, uint2* spans, uint32_t* nspan, hipStream_t s) {
   const uint32_t nb = tiles > 0 ? scan_blocks(tiles) : 1;
   if (nb > 1) {
     hipLaunchKernelGGL(k_scan_sum, dim3(nb, W), dim3(kScanThreads), 0, s, tiles, counts, btot);
@@ -760,21 +778,21 @@ hipError_t launch_blockbits(uint32_t W, const uint64_t* ebm, uint64_t ewords, ui
 }
 
 hipError_t launch_expand(uint32_t W, const float* grad, uint64_t ld, uint64_t tiles,
-                         const uint64_t* bitmaps, uint64_t words, const uint32_t* offsets,
-                         const uint32_t* spans, const uint32_t* nspan, uint32_t* idx, float* val,
-                         uint64_t cap, hipStream_t s) {
+                         const uint64_t* bitmaps, uint64_t words, const uint2* spans,
+                         const uint32_t* nspan, uint32_t* idx, float* val, uint64_t cap,
+                         hipStream_t s) {
   if (tiles == 0 || cap == 0) return hipSuccess;
   const uint64_t nsp = (tiles + 1) / 2;
   uint64_t g = (kExpandGroups + W - 1) / W;
   if (g > nsp) g = nsp;
   hipLaunchKernelGGL(k_expand_dense, dim3((uint32_t)g, W), dim3(kExpandThreads), 0, s, grad, ld,
-                     tiles, bitmaps, words, offsets, spans, nspan, idx, val, cap);
+                     tiles, bitmaps, words, spans, nspan, idx, val, cap);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   uint64_t gs = (nsp + kExpandWaves - 1) / kExpandWaves;
   if (gs > g) gs = g;
   hipLaunchKernelGGL(k_expand_sparse, dim3((uint32_t)gs, W), dim3(kExpandThreads), 0, s, grad, ld,
-                     tiles, bitmaps, words, offsets, spans, nspan, idx, val, cap);
+                     tiles, bitmaps, words, spans, nspan, idx, val, cap);
   return hipGetLastError();
 }
 

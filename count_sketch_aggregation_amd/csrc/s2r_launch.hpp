@@ -54,19 +54,20 @@ HashArgs make_hash_args(const s2r_params& p);
 hipError_t launch_stream(uint32_t W, const float* grad, uint64_t n, uint64_t ld,
                          uint64_t tiles, uint64_t* bitmaps, uint32_t* counts, hipStream_t s);
 // tiles are scanned in blocks of kScanPass; more than one block needs W * scan_blocks(tiles)
-// uint4 block totals.  spans (W * ceil(tiles / 2) uint32) and nspan (2 W uint32) may be null.
+// uint4 block totals.  spans (W * ceil(tiles / 2) uint2: span, list position of its first
+// pair) and nspan (2 W uint32) may be null.
 uint32_t scan_blocks(uint64_t tiles);
 hipError_t launch_scan(uint32_t W, uint64_t tiles, const uint32_t* counts, uint32_t* offsets,
                        uint64_t* nnz, uint32_t* chunk_tile, uint64_t chunks, uint64_t cap,
-                       uint4* btot, uint32_t* spans, uint32_t* nspan, hipStream_t s);
+                       uint4* btot, uint2* spans, uint32_t* nspan, hipStream_t s);
 hipError_t launch_fill_zero(float* p, uint64_t count, hipStream_t s);
 // block-granular bitmaps [W][bwords] from element bitmaps [W][ewords]
 hipError_t launch_blockbits(uint32_t W, const uint64_t* ebm, uint64_t ewords, uint64_t n,
                             uint32_t log2_block, uint64_t bwords, uint64_t* bbm, hipStream_t s);
 hipError_t launch_expand(uint32_t W, const float* grad, uint64_t ld, uint64_t tiles,
-                         const uint64_t* bitmaps, uint64_t words, const uint32_t* offsets,
-                         const uint32_t* spans, const uint32_t* nspan, uint32_t* idx, float* val,
-                         uint64_t cap, hipStream_t s);
+                         const uint64_t* bitmaps, uint64_t words, const uint2* spans,
+                         const uint32_t* nspan, uint32_t* idx, float* val, uint64_t cap,
+                         hipStream_t s);
 hipError_t launch_scatter(const HashArgs& h, uint32_t W, uint64_t tiles, const uint32_t* offsets,
                           const uint32_t* idx, const float* val, uint64_t cap, uint64_t chunks,
                           float* sketches, uint64_t w, hipStream_t s);
