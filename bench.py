@@ -48,14 +48,19 @@ def log(msg: str) -> None:
     print(msg, file=sys.stderr, flush=True)
 
 
-def build_inputs(wl, dev, hash_family: str, log2_block: int = 0):
+def build_inputs(wl, dev, hash_family: str, log2_block: int = 0, log2_part: int | None = None):
     import numpy as np
     import torch
 
     import count_sketch_aggregation_amd as s2r
     import workloads as WL
 
-    K = wl.log2_w if hash_family == "independent" else s2r.s2r_default_log2_part(wl.d, wl.log2_w)
+    if hash_family == "independent":
+        K = wl.log2_w
+    elif log2_part is not None:
+        K = log2_part
+    else:
+        K = s2r.s2r_default_log2_part(wl.d, wl.log2_w)
     p = s2r.s2r_params_from_seed(wl.hash_seed, wl.d, wl.log2_w, K, log2_block=log2_block)
     ld = (wl.N + 3) // 4 * 4
     grad = torch.zeros((wl.W, ld), dtype=torch.float32, device=dev)
@@ -277,6 +282,9 @@ def main() -> int:
                     choices=["partitioned", "independent"])
     ap.add_argument("--block", type=int, default=0, metavar="LOG2_B",
                     help="bitmap granularity: one bit per 2^LOG2_B elements (default 0: per element)")
+    ap.add_argument("--log2-part", type=int, default=None, metavar="K",
+                    help="partitioned hash: 2^K buckets per partition and row (default: the "
+                         "library's s2r_default_log2_part)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cold-reps", type=int, default=20,
                     help="extra steps timed alone after flushing the caches (0 to skip)")
@@ -311,7 +319,7 @@ def main() -> int:
     wl = names[args.workload]
     dev = torch.device("cuda:0")
     log(f"workload {wl.name}: W={wl.W} N={wl.N} d={wl.d} w=2^{wl.log2_w} hash={args.hash_family}")
-    p, grad, ld, cap, sparse = build_inputs(wl, dev, args.hash_family, args.block)
+    p, grad, ld, cap, sparse = build_inputs(wl, dev, args.hash_family, args.block, args.log2_part)
     buf = s2r.alloc_encode_buffers(p, wl.W, wl.N, cap, dev)
     words = s2r.s2r_block_bitmap_words(wl.N, args.block)
     bm = torch.empty(max(words, 1), dtype=torch.int64, device=dev)

@@ -6,9 +6,10 @@
 //
 // Two paths.
 //
-// Direct (no workspace, or a table small enough to stay cache-resident): k_dwrite gathers,
-// for every set bit of its 8192-element tile, the d sketch cells from memory and takes a
-// register median; the tile is written with 128-bit coalesced stores, zeros included.
+// Direct (no workspace, or a table small enough to stay cache-resident): k_dwrite_direct
+// gathers, for every set bit of its 8192-element tile, the d sketch cells from memory (the
+// gathers of several set bits in flight per thread) and takes a register median; the tile
+// is written with 128-bit coalesced stores, zeros included.
 // Random gathers into a table larger than L2 run at ~55-80 G/s on MI355X, so this path is
 // bound by the d*U gathers.
 //
@@ -41,7 +42,7 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 constexpr int kDecThreads = 256;
 constexpr int kDecTile = 8192;
 constexpr int kDecWords = kDecTile / 64;     // 128
-constexpr uint64_t kDirectTableBytes = 8ull << 20;
+constexpr uint64_t kDirectTableBytes = 4ull << 20;  // one XCD's L2
 constexpr int kDBinThreads = 512;
 constexpr int kDUnsortThreads = 512;
 constexpr int kDMedianUnroll = 4;  // items in flight per thread (stride kAccThreads)
@@ -453,6 +454,91 @@ __global__ __launch_bounds__(kDecThreads) void k_dwrite(HashArgs h, uint64_t n, 
 }
 
 // ---------------------------------------------------------------------------------------
+// k_dwrite_direct: the direct path (no partitioned workspace), grid = tiles, 256 threads.
+// Thread t owns the float4 groups g = t + 256 r (r = 0..7) of its 8192-element tile, as in
+// k_dwrite, and collects the set bits of those 32 elements into one mask.  It then walks
+// the mask kDirectBatch set bits at a time: the d gathers of every bit in the batch issue
+// before any median is taken, so a thread waits once per batch rather than once per group.
+// Each median goes to the element's place in an LDS copy of the tile; the thread reads its
+// own groups back (no barrier: no other thread touches them) and stores them, zeros at
+// clear bits, with 128-bit stores.
+template <int D>
+constexpr int direct_batch() { return D <= 3 ? 8 : 4; }
+
+template <int D>
+__global__ __launch_bounds__(kDecThreads) void k_dwrite_direct(
+    HashArgs h, uint64_t n, uint64_t nwords, const uint64_t* __restrict__ bitmap,
+    const float* __restrict__ sketch, uint64_t w, float* __restrict__ out) {
+  __shared__ __align__(16) float lout[kDecTile];
+  const int tid = threadIdx.x;
+  const uint64_t base = (uint64_t)blockIdx.x * kDecTile;
+  constexpr int RPT = kDecTile / 4 / kDecThreads;  // 8 groups per thread
+  // group g = tid + 256 r lies in word g >> 4 = (tid >> 4) + 16 r at bit 4 (tid & 15)
+  uint64_t raw[RPT];
+#pragma unroll
+  for (int r = 0; r < RPT; ++r) {  // all eight loads first, then the (branchy) masking
+    const uint64_t q = (uint64_t)blockIdx.x * kDecWords + (tid >> 4) + 16 * r;
+    raw[r] = bitmap[masked_src(q < nwords ? q : nwords - 1, h.lb)];
+  }
+  uint32_t mask = 0;
+#pragma unroll
+  for (int r = 0; r < RPT; ++r) {
+    const uint64_t q = (uint64_t)blockIdx.x * kDecWords + (tid >> 4) + 16 * r;
+    const uint64_t wv = masked_from(raw[r], nwords, n, q, h.lb);
+    mask |= (uint32_t)((wv >> (4 * (tid & 15))) & 0xFu) << (4 * r);
+  }
+  constexpr int B = direct_batch<D>();
+  for (uint32_t left = mask; left != 0;) {
+    uint32_t slot[B];
+    bool on[B];
+#pragma unroll
+    for (int u = 0; u < B; ++u) {
+      on[u] = left != 0;
+      const uint32_t q = on[u] ? (uint32_t)__builtin_ctz(left) : 0u;  // bit 4r + b
+      left &= left - 1u;                                                // 0 stays 0
+      slot[u] = 4u * (tid + kDecThreads * (q >> 2)) + (q & 3u);         // element in the tile
+    }
+    float v[B][D];
+#pragma unroll
+    for (int u = 0; u < B; ++u) {
+      const uint32_t i = (uint32_t)(base + slot[u]);
+      const uint32_t part = partition_of(h, i);
+      // unconditional: a lane past its last set bit gathers element `base`'s cells (the
+      // same cells for all such lanes) and drops them, so no load waits on a branch
+#pragma unroll
+      for (int j = 0; j < D; ++j)
+        v[u][j] = apply_sign(sketch[(uint64_t)j * w + bucket_of(h, part, j, i)],
+                             sign_mask(h, j, i));
+    }
+#pragma unroll
+    for (int u = 0; u < B; ++u)
+      if (on[u]) lout[slot[u]] = median_of<D>(v[u]);
+  }
+  f32x4 o[RPT];
+#pragma unroll
+  for (int r = 0; r < RPT; ++r) {
+    const uint32_t nib = (mask >> (4 * r)) & 0xFu;
+    const f32x4 x = *reinterpret_cast<const f32x4*>(&lout[4 * (tid + kDecThreads * r)]);
+    o[r] = f32x4{(nib & 1u) ? x.x : 0.f, (nib & 2u) ? x.y : 0.f, (nib & 4u) ? x.z : 0.f,
+                 (nib & 8u) ? x.w : 0.f};
+  }
+  if (base + kDecTile <= n) {
+    f32x4* o4 = reinterpret_cast<f32x4*>(out + base);
+#pragma unroll
+    for (int r = 0; r < RPT; ++r) o4[tid + kDecThreads * r] = o[r];
+  } else {
+#pragma unroll
+    for (int r = 0; r < RPT; ++r) {
+      const uint64_t e = base + 4 * (uint64_t)(tid + kDecThreads * r);
+      if (e + 0 < n) out[e + 0] = o[r].x;
+      if (e + 1 < n) out[e + 1] = o[r].y;
+      if (e + 2 < n) out[e + 2] = o[r].z;
+      if (e + 3 < n) out[e + 3] = o[r].w;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------------------
 // host side
 
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -494,8 +580,9 @@ hipError_t launch_decode(const HashArgs& h, const s2r_params& p, uint64_t n,
   const uint64_t w = 1ull << p.log2_w;
   const uint64_t nwords = (n + 63) / 64;
   const DecodeLayout L = decode_layout(p, n, max_set);
-  // direct gathers win while the table stays cache-resident (measured on MI355X: a 6 MiB
-  // table decodes faster directly, a 21 MiB one 2.5x faster partitioned)
+  // direct gathers win while the table fits one XCD's L2; past it every gather pulls a
+  // line from the Infinity Cache or HBM (measured on MI355X: a 6 MiB table decodes 1.3x
+  // faster partitioned, a 21 MiB one 2.5x)
   const uint64_t table_bytes = ((uint64_t)p.d << p.log2_w) * sizeof(float);
   const bool part = L.partitioned && workspace != nullptr && ws_bytes >= L.total &&
                     table_bytes > kDirectTableBytes;
@@ -557,9 +644,15 @@ hipError_t launch_decode(const HashArgs& h, const s2r_params& p, uint64_t n,
     }
   }
   const uint64_t tiles = (n + kDecTile - 1) / kDecTile;
-  S2R_DISPATCH_D(p.d, hipLaunchKernelGGL((k_dwrite<D>), dim3((uint32_t)tiles), dim3(kDecThreads),
-                                         0, s, h, n, nwords, bitmap, sketch, w, out, ws, tiles,
-                                         part ? 1 : 0));
+  if (part) {
+    S2R_DISPATCH_D(p.d, hipLaunchKernelGGL((k_dwrite<D>), dim3((uint32_t)tiles),
+                                           dim3(kDecThreads), 0, s, h, n, nwords, bitmap, sketch,
+                                           w, out, ws, tiles, 1));
+  } else {
+    S2R_DISPATCH_D(p.d, hipLaunchKernelGGL((k_dwrite_direct<D>), dim3((uint32_t)tiles),
+                                           dim3(kDecThreads), 0, s, h, n, nwords, bitmap, sketch,
+                                           w, out));
+  }
   return hipGetLastError();
 }
 

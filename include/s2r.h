@@ -159,7 +159,7 @@ size_t s2r_decode_workspace_bytes(const s2r_params* p, uint64_t n, uint64_t max_
  * the sketch.  out may not overlap the inputs.
  * Paths: with workspace == NULL (or ws_bytes == 0) every set bit gathers its d cells from
  * the sketch directly.  With a workspace of s2r_decode_workspace_bytes(p, n, max_set)
- * bytes (contents on entry irrelevant) and a sketch larger than 8 MiB, the set bits are
+ * bytes (contents on entry irrelevant) and a sketch larger than 4 MiB, the set bits are
  * grouped by partition and each partition's cells are read once into LDS (smaller sketches
  * stay cache-resident and are gathered directly); if the bitmap turns out to hold more than
  * max_set set bits below n, the call still completes correctly through direct gathers
