@@ -95,15 +95,25 @@ __device__ __forceinline__ uint64_t masked_word(const uint64_t* __restrict__ bit
 }
 
 // ---------------------------------------------------------------------------------------
-__global__ __launch_bounds__(kDecWords) void k_dcount(const uint64_t* __restrict__ bitmap,
-                                                      uint64_t n, uint64_t nwords, uint32_t lb,
-                                                      uint32_t* __restrict__ tcount) {
-  const uint64_t q = (uint64_t)blockIdx.x * kDecWords + threadIdx.x;
-  const uint32_t c = wave_sum((uint32_t)__popcll(masked_word(bitmap, nwords, n, q, lb)));
-  __shared__ uint32_t part[kDecWords / kWave];
-  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = c;
-  __syncthreads();
-  if (threadIdx.x == 0) tcount[blockIdx.x] = part[0] + part[1];
+// k_dcount: 256 threads, a wave per 8192-element tile (kDcountTiles tiles per workgroup, no
+// barrier): lane l takes words 2l and 2l + 1 of the tile, both loads issued before either
+// is masked, and a wave sum gives the tile's count.
+constexpr int kDcountThreads = 256;
+constexpr int kDcountTiles = kDcountThreads / kWave;
+
+__global__ __launch_bounds__(kDcountThreads) void k_dcount(const uint64_t* __restrict__ bitmap,
+                                                           uint64_t n, uint64_t nwords,
+                                                           uint64_t tiles, uint32_t lb,
+                                                           uint32_t* __restrict__ tcount) {
+  const uint64_t t = (uint64_t)blockIdx.x * kDcountTiles + (threadIdx.x >> 6);
+  if (t >= tiles) return;  // wave-uniform
+  const int lane = threadIdx.x & 63;
+  const uint64_t q0 = t * kDecWords + 2 * lane;
+  const uint64_t r0 = bitmap[masked_src(q0 < nwords ? q0 : nwords - 1, lb)];
+  const uint64_t r1 = bitmap[masked_src(q0 + 1 < nwords ? q0 + 1 : nwords - 1, lb)];
+  const uint32_t c = wave_sum((uint32_t)(__popcll(masked_from(r0, nwords, n, q0, lb)) +
+                                         __popcll(masked_from(r1, nwords, n, q0 + 1, lb))));
+  if (lane == 0) tcount[t] = c;
 }
 
 // ---------------------------------------------------------------------------------------
@@ -138,22 +148,27 @@ __global__ __launch_bounds__(kDBinThreads) void k_dbin(HashArgs h, uint64_t n,
   const uint32_t cnt = (uint32_t)(U - start < kChunk ? U - start : kChunk);
   const uint64_t end = start + cnt;
 
-  // 1. expand ranks [start, end) into litem, 2048 bitmap words per round: each thread holds
-  //    4 words and their ranks, and the waves expand only the non-empty words that meet
-  //    the chunk (expand_owned_words)
+  // 1. expand ranks [start, end) into litem, kDBinBatchWords bitmap words per round: each
+  //    thread holds kDBinWordsPerThread words and their ranks, and the waves expand only the
+  //    non-empty words that meet the chunk (expand_owned_words).  The chunk's last rank lies
+  //    at or before the tile where the next chunk starts, so words past that tile are not
+  //    read (a thread past it re-reads the last word in range and drops it).
   uint64_t q0 = (uint64_t)t0 * kDecWords;
   uint64_t rank0 = ws.toff[t0];
-  while (rank0 < end && q0 < nwords) {
+  const uint64_t t_last = end < U ? (uint64_t)ws.chunk_tile[c + 1] : tiles - 1;
+  const uint64_t q_end = (t_last + 1) * kDecWords < nwords ? (t_last + 1) * kDecWords : nwords;
+  while (rank0 < end && q0 < q_end) {
     uint64_t wv[kDBinWordsPerThread];
     uint32_t sum = 0;
 #pragma unroll
     for (int u = 0; u < kDBinWordsPerThread; ++u) {  // all loads first, then the masking
       const uint64_t q = q0 + (uint64_t)tid * kDBinWordsPerThread + u;
-      wv[u] = bitmap[masked_src(q < nwords ? q : nwords - 1, h.lb)];
+      wv[u] = bitmap[masked_src(q < q_end ? q : q_end - 1, h.lb)];
     }
 #pragma unroll
     for (int u = 0; u < kDBinWordsPerThread; ++u) {
-      wv[u] = masked_from(wv[u], nwords, n, q0 + (uint64_t)tid * kDBinWordsPerThread + u, h.lb);
+      const uint64_t q = q0 + (uint64_t)tid * kDBinWordsPerThread + u;
+      wv[u] = q < q_end ? masked_from(wv[u], nwords, n, q, h.lb) : 0ull;
       sum += (uint32_t)__popcll(wv[u]);
     }
     const uint32_t inc = wave_inclusive_sum(sum);
@@ -602,7 +617,8 @@ hipError_t launch_decode(const HashArgs& h, const s2r_params& p, uint64_t n,
     ws.chunks = L.chunks;
     ws.max_set = L.chunks * kChunk < max_set ? L.chunks * kChunk : max_set;
     if (ws.max_set > n) ws.max_set = n;
-    hipLaunchKernelGGL(k_dcount, dim3((uint32_t)L.tiles), dim3(kDecWords), 0, s, bitmap, n, nwords, h.lb,
+    hipLaunchKernelGGL(k_dcount, dim3((uint32_t)((L.tiles + kDcountTiles - 1) / kDcountTiles)),
+                       dim3(kDcountThreads), 0, s, bitmap, n, nwords, L.tiles, h.lb,
                        tcount);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;

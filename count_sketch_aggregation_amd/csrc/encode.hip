@@ -593,24 +593,38 @@ __global__ __launch_bounds__(kAccThreads) void k_accumulate(
   const uint32_t cells = D * pw;
   for (uint32_t c = tid; c < cells; c += kAccThreads) tile[c] = 0.f;
 
-  const uint64_t total = offsets[(uint64_t)k * (tiles + 1) + tiles];
-  const uint64_t lim = total < cap ? total : cap;
-  const uint32_t nch = (uint32_t)((lim + kChunk - 1) / kChunk);
   // column p of the worker's chunk-major offsets: strided, but the XCD grouping runs the
   // partitions that share each cache line on one XCD at about the same time
   const uint32_t* pf = prefix + (uint64_t)k * chunks * (partitions + 1) + p;
   const uint64_t kbase = (uint64_t)k * chunks * kChunk;
   constexpr int PER = kSegBatch / kAccThreads;
+  // The first batch's offsets are read in the same round trip as the list length, before
+  // the number of filled chunks is known: rows up to the workspace's last chunk are in
+  // bounds, and those past the filled ones are dropped below.
+  uint32_t lo[PER], hi[PER];
+  if (chunks > 0) {
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const uint64_t c = tid * PER + u < chunks ? tid * PER + u : chunks - 1;
+      lo[u] = pf[c * (partitions + 1)];
+      hi[u] = pf[c * (partitions + 1) + 1];
+    }
+  }
+  const uint64_t total = offsets[(uint64_t)k * (tiles + 1) + tiles];
+  const uint64_t lim = total < cap ? total : cap;
+  const uint32_t nch = (uint32_t)((lim + kChunk - 1) / kChunk);
   for (uint32_t cb = 0; cb < nch; cb += kSegBatch) {
     const uint32_t nb = nch - cb < (uint32_t)kSegBatch ? nch - cb : (uint32_t)kSegBatch;
     __syncthreads();  // the previous batch is consumed (and the tile is zeroed)
-    uint32_t lo[PER], hi[PER], len[PER], sum = 0;
+    uint32_t len[PER], sum = 0;
+    if (cb > 0) {
 #pragma unroll
-    for (int u = 0; u < PER; ++u) {  // clamped, unconditional loads: all in flight at once
-      const uint32_t c = tid * PER + u < nb ? tid * PER + u : nb - 1;
-      const uint64_t row = (uint64_t)(cb + c) * (partitions + 1);
-      lo[u] = pf[row];
-      hi[u] = pf[row + 1];
+      for (int u = 0; u < PER; ++u) {  // clamped, unconditional loads: all in flight at once
+        const uint32_t c = tid * PER + u < nb ? tid * PER + u : nb - 1;
+        const uint64_t row = (uint64_t)(cb + c) * (partitions + 1);
+        lo[u] = pf[row];
+        hi[u] = pf[row + 1];
+      }
     }
 #pragma unroll
     for (int u = 0; u < PER; ++u) {
