@@ -573,6 +573,48 @@ __global__ __launch_bounds__(kBinThreads) void k_bin(
   if ((cnt & 1u) && tid == 0) out[cnt - 1] = spair[cnt - 1];
 }
 
+// One group of k_accumulate's entries, e0 + u * kAccThreads (u < UN) of a batch of E > 0
+// flattened entries: each entry's segment (branch-free search) and its (index, value bits)
+// pair.  Entries at or past E are read as entry E - 1, so every load issues unconditionally;
+// acc_add drops them.
+template <int UN>
+__device__ __forceinline__ void acc_fetch(const uint32_t* seg_off, const uint32_t* seg_src,
+                                          uint32_t nb, uint32_t E, const uint2* kb, uint32_t e0,
+                                          uint2* pr) {
+  uint32_t x[UN], c[UN];
+#pragma unroll
+  for (int u = 0; u < UN; ++u) {
+    const uint32_t e = e0 + u * kAccThreads;
+    x[u] = e < E ? e : E - 1;
+  }
+  segments_of<UN>(seg_off, nb, x, c);
+#pragma unroll
+  for (int u = 0; u < UN; ++u) pr[u] = kb[seg_src[c[u]] + (x[u] - seg_off[c[u]])];
+}
+
+// Adds the group's pairs (entries below E) into the LDS tile: s_j(i) g(i) into row j's
+// bucket Q_j(i), all D x UN compare-and-swaps in flight together.
+template <int D, int UN>
+__device__ __forceinline__ void acc_add(const HashArgs& h, float* tile, uint32_t pw, uint32_t E,
+                                        uint32_t e0, const uint2* pr) {
+  uint32_t cell[UN * D];
+  float add[UN * D];
+  bool live[UN * D];
+#pragma unroll
+  for (int u = 0; u < UN; ++u) {
+    const bool on = e0 + u * kAccThreads < E;
+    const uint32_t i = pr[u].x;
+    const float g = __uint_as_float(pr[u].y);
+#pragma unroll
+    for (int j = 0; j < D; ++j) {
+      live[u * D + j] = on;
+      cell[u * D + j] = j * pw + row_bucket(h, j, i);
+      add[u * D + j] = apply_sign(g, sign_mask(h, j, i));
+    }
+  }
+  lds_add_f32_many<UN * D>(tile, cell, add, live);
+}
+
 // k_accumulate (partitioned path): grid (P, W), 512 threads, items XCD-grouped; the tile
 // leaves with non-temporal stores when nt is set.  The partition's d x 2^K
 // buckets live in LDS.  Its entries are spread over one short segment per list chunk; the
@@ -652,41 +694,23 @@ __global__ __launch_bounds__(kAccThreads) void k_accumulate(
     if (tid == kAccThreads - 1 && nb == (uint32_t)kSegBatch) seg_off[kSegBatch] = run;
     __syncthreads();
     const uint32_t E = seg_off[nb];
+    if (E == 0) continue;  // uniform
+    // This thread's entries come in groups of UN (e0 + u * kAccThreads, e0 = tid + m * kStep).
+    // Software pipeline: the segment search and list loads of the next group issue before the
+    // current group's adds, so one group's global round trip overlaps the previous group's LDS
+    // work.  The register sets a and b alternate, so no loaded register is ever copied (a copy
+    // would wait for its load).
     constexpr int UN = acc_unroll(D);
-    for (uint32_t e0 = tid; e0 < E; e0 += kAccThreads * UN) {
-      // UN entries e0 + u * kAccThreads: coalesced across the wave, searched,
-      // loaded and added with all of them in flight
-      uint32_t e[UN], c[UN];
-#pragma unroll
-      for (int u = 0; u < UN; ++u) e[u] = e0 + u * kAccThreads;
-      segments_of<UN>(seg_off, nb, e, c);
-      uint32_t ii[UN];
-      float gg[UN];
-      bool on[UN];
-#pragma unroll
-      for (int u = 0; u < UN; ++u) {
-        on[u] = e[u] < E;
-        ii[u] = 0;
-        gg[u] = 0.f;
-        if (on[u]) {
-          const uint2 pr = bins[kbase + seg_src[c[u]] + (e[u] - seg_off[c[u]])];
-          ii[u] = pr.x;
-          gg[u] = __uint_as_float(pr.y);
-        }
-      }
-      uint32_t cell[UN * D];
-      float add[UN * D];
-      bool live[UN * D];
-#pragma unroll
-      for (int u = 0; u < UN; ++u) {
-#pragma unroll
-        for (int j = 0; j < D; ++j) {
-          live[u * D + j] = on[u];
-          cell[u * D + j] = j * pw + row_bucket(h, j, ii[u]);
-          add[u * D + j] = apply_sign(gg[u], sign_mask(h, j, ii[u]));
-        }
-      }
-      lds_add_f32_many<UN * D>(tile, cell, add, live);
+    constexpr uint32_t kStep = kAccThreads * UN;
+    const uint2* kb = bins + kbase;
+    uint2 pa[UN], pb[UN];
+    acc_fetch<UN>(seg_off, seg_src, nb, E, kb, tid, pa);
+    for (uint32_t e0 = tid; e0 < E; e0 += 2 * kStep) {
+      acc_fetch<UN>(seg_off, seg_src, nb, E, kb, e0 + kStep, pb);
+      acc_add<D, UN>(h, tile, pw, E, e0, pa);
+      if (e0 + kStep >= E) break;
+      acc_fetch<UN>(seg_off, seg_src, nb, E, kb, e0 + 2 * kStep, pa);
+      acc_add<D, UN>(h, tile, pw, E, e0 + kStep, pb);
     }
   }
   __syncthreads();
