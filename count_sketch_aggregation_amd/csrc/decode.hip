@@ -472,8 +472,9 @@ __global__ __launch_bounds__(kDecThreads) void k_dwrite(HashArgs h, uint64_t n, 
 // k_dwrite_direct: the direct path (no partitioned workspace), grid = tiles, 256 threads.
 // Thread t owns the float4 groups g = t + 256 r (r = 0..7) of its 8192-element tile, as in
 // k_dwrite, and collects the set bits of those 32 elements into one mask.  It then walks
-// the mask kDirectBatch set bits at a time: the d gathers of every bit in the batch issue
-// before any median is taken, so a thread waits once per batch rather than once per group.
+// the mask direct_batch<D>() set bits at a time (8 for d <= 3, else 4): the d gathers of
+// every bit in the batch issue before any median is taken, so a thread waits once per
+// batch rather than once per group.
 // Each median goes to the element's place in an LDS copy of the tile; the thread reads its
 // own groups back (no barrier: no other thread touches them) and stores them, zeros at
 // clear bits, with 128-bit stores.
