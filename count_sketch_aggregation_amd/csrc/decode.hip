@@ -130,6 +130,54 @@ struct DecodeWs {
   uint64_t max_set;
 };
 
+// Raw bitmap words q .. q + WPT - 1 of a k_dbin round (clamped below q_end, so every load
+// issues unconditionally; masked in dbin_round).
+template <int WPT>
+__device__ __forceinline__ void dbin_words(const uint64_t* __restrict__ bitmap, uint64_t q,
+                                           uint64_t q_end, uint32_t lb, uint64_t* wv) {
+#pragma unroll
+  for (int u = 0; u < WPT; ++u)
+    wv[u] = bitmap[masked_src(q + u < q_end ? q + u : q_end - 1, lb)];
+}
+
+// One round of k_dbin's rank expansion over words [q0, q0 + kDBinBatchWords): masks the
+// thread's raw words, ranks them with a workgroup scan and expands the set bits whose rank
+// lies in [start, end) into litem; advances q0 and rank0.  Called by the whole workgroup
+// (two barriers).
+__device__ __forceinline__ void dbin_round(const uint64_t* raw, uint64_t n, uint64_t nwords,
+                                           uint64_t q_end, uint32_t lb, uint64_t start,
+                                           uint64_t end, uint64_t& q0, uint64_t& rank0,
+                                           uint32_t* litem, uint32_t* wtot, int tid) {
+  const int wave = tid >> 6, lane = tid & 63;
+  uint64_t wv[kDBinWordsPerThread];
+  uint32_t sum = 0;
+#pragma unroll
+  for (int u = 0; u < kDBinWordsPerThread; ++u) {
+    const uint64_t q = q0 + (uint64_t)tid * kDBinWordsPerThread + u;
+    wv[u] = q < q_end ? masked_from(raw[u], nwords, n, q, lb) : 0ull;
+    sum += (uint32_t)__popcll(wv[u]);
+  }
+  const uint32_t inc = wave_inclusive_sum(sum);
+  if (lane == kWave - 1) wtot[wave] = inc;
+  __syncthreads();
+  uint32_t before = inc - sum, batch_total = 0;
+  for (int v = 0; v < kDBinThreads / kWave; ++v) {
+    if (v < wave) before += wtot[v];
+    batch_total += wtot[v];
+  }
+  uint64_t rk0[kDBinWordsPerThread];
+#pragma unroll
+  for (int u = 0; u < kDBinWordsPerThread; ++u) {
+    rk0[u] = rank0 + before;
+    before += (uint32_t)__popcll(wv[u]);
+  }
+  expand_owned_words<kDBinWordsPerThread>(wv, rk0, q0 + (uint64_t)tid * kDBinWordsPerThread,
+                                          start, end, litem, lane);
+  rank0 += batch_total;
+  q0 += kDBinBatchWords;
+  __syncthreads();  // wtot is reused next round
+}
+
 __global__ __launch_bounds__(kDBinThreads) void k_dbin(HashArgs h, uint64_t n,
                                                        const uint64_t* __restrict__ bitmap,
                                                        uint64_t nwords, uint64_t tiles,
@@ -157,39 +205,19 @@ __global__ __launch_bounds__(kDBinThreads) void k_dbin(HashArgs h, uint64_t n,
   uint64_t rank0 = ws.toff[t0];
   const uint64_t t_last = end < U ? (uint64_t)ws.chunk_tile[c + 1] : tiles - 1;
   const uint64_t q_end = (t_last + 1) * kDecWords < nwords ? (t_last + 1) * kDecWords : nwords;
+  // The next round's words are loaded before the current round is expanded (register sets
+  // a and b alternate, so no loaded register is copied); past q_end they re-read the last
+  // word in range and are never used.
+  uint64_t wa[kDBinWordsPerThread], wb[kDBinWordsPerThread];
+  dbin_words<kDBinWordsPerThread>(bitmap, q0 + (uint64_t)tid * kDBinWordsPerThread, q_end, h.lb, wa);
   while (rank0 < end && q0 < q_end) {
-    uint64_t wv[kDBinWordsPerThread];
-    uint32_t sum = 0;
-#pragma unroll
-    for (int u = 0; u < kDBinWordsPerThread; ++u) {  // all loads first, then the masking
-      const uint64_t q = q0 + (uint64_t)tid * kDBinWordsPerThread + u;
-      wv[u] = bitmap[masked_src(q < q_end ? q : q_end - 1, h.lb)];
-    }
-#pragma unroll
-    for (int u = 0; u < kDBinWordsPerThread; ++u) {
-      const uint64_t q = q0 + (uint64_t)tid * kDBinWordsPerThread + u;
-      wv[u] = q < q_end ? masked_from(wv[u], nwords, n, q, h.lb) : 0ull;
-      sum += (uint32_t)__popcll(wv[u]);
-    }
-    const uint32_t inc = wave_inclusive_sum(sum);
-    if (lane == kWave - 1) wtot[wave] = inc;
-    __syncthreads();
-    uint32_t before = inc - sum, batch_total = 0;
-    for (int v = 0; v < kDBinThreads / kWave; ++v) {
-      if (v < wave) before += wtot[v];
-      batch_total += wtot[v];
-    }
-    uint64_t rk0[kDBinWordsPerThread];
-#pragma unroll
-    for (int u = 0; u < kDBinWordsPerThread; ++u) {
-      rk0[u] = rank0 + before;
-      before += (uint32_t)__popcll(wv[u]);
-    }
-    expand_owned_words<kDBinWordsPerThread>(wv, rk0, q0 + (uint64_t)tid * kDBinWordsPerThread,
-                                            start, end, litem, lane);
-    rank0 += batch_total;
-    q0 += kDBinBatchWords;
-    __syncthreads();  // wtot is reused next round
+    dbin_words<kDBinWordsPerThread>(bitmap, q0 + kDBinBatchWords + (uint64_t)tid * kDBinWordsPerThread,
+                                    q_end, h.lb, wb);
+    dbin_round(wa, n, nwords, q_end, h.lb, start, end, q0, rank0, litem, wtot, tid);
+    if (!(rank0 < end && q0 < q_end)) break;
+    dbin_words<kDBinWordsPerThread>(bitmap, q0 + kDBinBatchWords + (uint64_t)tid * kDBinWordsPerThread,
+                                    q_end, h.lb, wa);
+    dbin_round(wb, n, nwords, q_end, h.lb, start, end, q0, rank0, litem, wtot, tid);
   }
   for (uint32_t p = tid; p <= P; p += kDBinThreads) hist[p] = 0;
   __syncthreads();
