@@ -373,9 +373,13 @@ __global__ __launch_bounds__(kAccThreads) void k_dmedian(HashArgs h, uint64_t ti
 // ---------------------------------------------------------------------------------------
 // k_dunsort: grid = rank chunks, kDUnsortThreads threads.  Puts a chunk's medians from slot
 // order into rank order in place: the chunk's 8192 values are staged in LDS with coalesced
-// loads, then rank r takes the value at its slot, with coalesced slot reads and stores.
+// loads, then rank r takes the value at its slot, with coalesced slot reads and stores.  The
+// slot reads issue together with the value loads, before the barrier (clamped indices, so
+// every load issues unconditionally; the workspace holds whole chunks, so index 0 and the
+// first 16 bytes of the chunk are always in bounds).
 __global__ __launch_bounds__(kDUnsortThreads) void k_dunsort(uint64_t tiles, DecodeWs ws) {
   __shared__ __align__(16) float lv[kChunk];
+  constexpr int VPT = kChunk / kDUnsortThreads;  // 16 ranks per thread
   const uint32_t c = blockIdx.x;
   const int tid = threadIdx.x;
   const uint64_t U = ws.toff[tiles];
@@ -386,11 +390,30 @@ __global__ __launch_bounds__(kDUnsortThreads) void k_dunsort(uint64_t tiles, Dec
   float* g = ws.gval + start;
   const uint16_t* sl = ws.slot + start;
   const uint32_t cnt4 = cnt / 4;
-  for (uint32_t q = tid; q < cnt4; q += kDUnsortThreads)
-    *reinterpret_cast<f32x4*>(&lv[4 * q]) = *reinterpret_cast<const f32x4*>(g + 4 * q);
+  f32x4 gv[VPT / 4];
+  uint32_t sv[VPT];
+#pragma unroll
+  for (int m = 0; m < VPT / 4; ++m) {
+    const uint32_t q = tid + kDUnsortThreads * m;
+    gv[m] = *reinterpret_cast<const f32x4*>(g + 4 * (q < cnt4 ? q : 0u));
+  }
+#pragma unroll
+  for (int m = 0; m < VPT; ++m) {
+    const uint32_t r = tid + kDUnsortThreads * m;
+    sv[m] = sl[r < cnt ? r : 0u];
+  }
+#pragma unroll
+  for (int m = 0; m < VPT / 4; ++m) {
+    const uint32_t q = tid + kDUnsortThreads * m;
+    if (q < cnt4) *reinterpret_cast<f32x4*>(&lv[4 * q]) = gv[m];
+  }
   for (uint32_t s = 4 * cnt4 + tid; s < cnt; s += kDUnsortThreads) lv[s] = g[s];
   __syncthreads();
-  for (uint32_t r = tid; r < cnt; r += kDUnsortThreads) g[r] = lv[sl[r]];
+#pragma unroll
+  for (int m = 0; m < VPT; ++m) {
+    const uint32_t r = tid + kDUnsortThreads * m;
+    if (r < cnt) g[r] = lv[sv[m]];
+  }
 }
 
 // ---------------------------------------------------------------------------------------
