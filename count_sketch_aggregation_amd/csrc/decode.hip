@@ -46,6 +46,7 @@ constexpr uint64_t kDirectTableBytes = 4ull << 20;  // one XCD's L2
 constexpr int kDBinThreads = 512;
 constexpr int kDUnsortThreads = 512;
 constexpr int kDMedianUnroll = 4;  // items in flight per thread (stride kAccThreads)
+constexpr int kTileLoads = 8;      // 16-byte cell loads per thread in flight when a tile fills
 constexpr uint64_t kDMedianTargetGroups = 1536;
 constexpr uint32_t kDMedianMaxSplits = 8;
 constexpr int kDBinWordsPerThread = 4;
@@ -291,19 +292,25 @@ __global__ __launch_bounds__(kAccThreads) void k_dmedian(HashArgs h, uint64_t ti
   const uint32_t p = item % P, split = item / P;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const uint64_t U = ws.toff[tiles];
-  if (U > ws.max_set || U == 0) return;
-  const uint64_t nch = (U + kChunk - 1) / kChunk;
-  const uint32_t c_lo = (uint32_t)(nch * split / gridDim.y);
-  const uint32_t c_hi = (uint32_t)(nch * (split + 1) / gridDim.y);
-  if (c_lo >= c_hi) return;
   const uint32_t pw = 1u << h.K;
   const float* sk = sketch + (uint64_t)p * pw;
+  // The partition's cells are loaded in the same round trip as U (they do not depend on
+  // it), kTileLoads per thread with every load issued before any is stored to LDS.
   if (vec4) {
-    const uint32_t pw4 = pw / 4;
-    for (uint32_t c = tid; c < D * pw4; c += kAccThreads) {
-      const uint32_t j = c / pw4, q = c - j * pw4;
-      *reinterpret_cast<f32x4*>(&tile[j * pw + 4 * q]) =
-          *reinterpret_cast<const f32x4*>(sk + (uint64_t)j * w + 4 * q);
+    const uint32_t pw4 = pw / 4, n4 = D * pw4;
+    for (uint32_t c0 = tid; c0 < n4; c0 += kAccThreads * kTileLoads) {
+      f32x4 v[kTileLoads];
+#pragma unroll
+      for (int u = 0; u < kTileLoads; ++u) {
+        const uint32_t c = c0 + u * kAccThreads < n4 ? c0 + u * kAccThreads : n4 - 1;
+        const uint32_t j = c / pw4, q = c - j * pw4;
+        v[u] = *reinterpret_cast<const f32x4*>(sk + (uint64_t)j * w + 4 * q);
+      }
+#pragma unroll
+      for (int u = 0; u < kTileLoads; ++u) {
+        const uint32_t c = c0 + u * kAccThreads;
+        if (c < n4) *reinterpret_cast<f32x4*>(&tile[4 * c]) = v[u];  // j pw + 4 q = 4 c
+      }
     }
   } else {
     for (uint32_t c = tid; c < D * pw; c += kAccThreads) {
@@ -311,21 +318,31 @@ __global__ __launch_bounds__(kAccThreads) void k_dmedian(HashArgs h, uint64_t ti
       tile[c] = sk[(uint64_t)j * w + q];
     }
   }
+  if (U > ws.max_set || U == 0) return;
+  const uint64_t nch = (U + kChunk - 1) / kChunk;
+  const uint32_t c_lo = (uint32_t)(nch * split / gridDim.y);
+  const uint32_t c_hi = (uint32_t)(nch * (split + 1) / gridDim.y);
+  if (c_lo >= c_hi) return;
   const uint32_t* pf = ws.prefix + p;  // column p of the chunk-major offsets
   constexpr int PER = kSegBatch / kAccThreads;
   for (uint32_t cb = c_lo; cb < c_hi; cb += kSegBatch) {
     const uint32_t nb = c_hi - cb < (uint32_t)kSegBatch ? c_hi - cb : (uint32_t)kSegBatch;
     __syncthreads();  // the previous batch is consumed (and the tile is loaded)
-    uint32_t len[PER], sum = 0;
+    uint32_t lo[PER], hi[PER], len[PER], sum = 0;
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {  // clamped, unconditional loads: all in flight at once
+      const uint32_t c = tid * PER + u < nb ? tid * PER + u : nb - 1;
+      const uint64_t row = (uint64_t)(cb + c) * (P + 1);
+      lo[u] = pf[row];
+      hi[u] = pf[row + 1];
+    }
 #pragma unroll
     for (int u = 0; u < PER; ++u) {
       const uint32_t c = tid * PER + u;
       len[u] = 0;
       if (c < nb) {
-        const uint64_t row = (uint64_t)(cb + c) * (P + 1);
-        const uint32_t lo = pf[row], hi = pf[row + 1];
-        seg_src[c] = (cb + c) * (uint32_t)kChunk + lo;
-        len[u] = hi - lo;
+        seg_src[c] = (cb + c) * (uint32_t)kChunk + lo[u];
+        len[u] = hi[u] - lo[u];
       }
       sum += len[u];
     }
@@ -349,13 +366,17 @@ __global__ __launch_bounds__(kAccThreads) void k_dmedian(HashArgs h, uint64_t ti
       for (int u = 0; u < kDMedianUnroll; ++u) e[u] = e0 + u * kAccThreads;
       segments_of<kDMedianUnroll>(seg_off, nb, e, c);
       uint32_t at[kDMedianUnroll], ii[kDMedianUnroll];
+      // Unconditional loads (an item at or past E is read as item E - 1 of the last segment,
+      // which its search returned, and dropped below); the empty asm uses the values so the
+      // compiler cannot sink a load into the branch that consumes it, after other stores.
 #pragma unroll
       for (int u = 0; u < kDMedianUnroll; ++u) {
-        if (e[u] < E) {
-          at[u] = seg_src[c[u]] + (e[u] - seg_off[c[u]]);
-          ii[u] = ws.bidx[at[u]];
-        }
+        const uint32_t x = e[u] < E ? e[u] : E - 1;
+        at[u] = seg_src[c[u]] + (x - seg_off[c[u]]);
+        ii[u] = ws.bidx[at[u]];
       }
+#pragma unroll
+      for (int u = 0; u < kDMedianUnroll; ++u) asm volatile("" : "+v"(ii[u]));
 #pragma unroll
       for (int u = 0; u < kDMedianUnroll; ++u) {
         if (e[u] < E) {
@@ -417,20 +438,19 @@ __global__ __launch_bounds__(kDUnsortThreads) void k_dunsort(uint64_t tiles, Dec
 }
 
 // ---------------------------------------------------------------------------------------
-// k_dwrite: grid = tiles, 256 threads.  Thread t writes the float4 groups g = t + 256 r
-// (elements base + 4g .. 4g + 3, r = 0..7) straight from registers, zeros included.  The
-// tile's 128 bitmap words and their rank offsets sit in LDS; the set bits of a group take
-// consecutive ranks starting at the word's offset plus the popcount of the bits below the
-// group.  partitioned = 1 reads the medians in rank order (after k_dunsort); direct
-// (partitioned = 0, or U over the capacity) gathers each set bit's d cells and takes the
-// median in registers.
+// k_dwrite (partitioned path): grid = tiles, 256 threads.  Thread t writes the float4 groups
+// g = t + 256 r (elements base + 4g .. 4g + 3, r = 0..7) straight from registers, zeros
+// included.  The tile's 128 bitmap words and their rank offsets sit in LDS; the set bits of
+// a group take consecutive ranks starting at the word's offset plus the popcount of the
+// bits below the group, and their medians are read in rank order (after k_dunsort).  If U
+// exceeds the workspace capacity (the other partitioned kernels then did nothing), each set
+// bit instead gathers its d cells and takes the median in registers.
 template <int D>
 __global__ __launch_bounds__(kDecThreads) void k_dwrite(HashArgs h, uint64_t n, uint64_t nwords,
                                                         const uint64_t* __restrict__ bitmap,
                                                         const float* __restrict__ sketch,
                                                         uint64_t w, float* __restrict__ out,
-                                                        DecodeWs ws, uint64_t tiles,
-                                                        int partitioned) {
+                                                        DecodeWs ws, uint64_t tiles) {
   __shared__ uint64_t lw[kDecWords];
   __shared__ uint32_t lwo[kDecWords];
   __shared__ uint32_t wtot[2];
@@ -448,12 +468,8 @@ __global__ __launch_bounds__(kDecThreads) void k_dwrite(HashArgs h, uint64_t n, 
   __syncthreads();
   if (tid < kDecWords) lwo[tid] = inc - pc + (wave ? wtot[0] : 0u);
   __syncthreads();
-  bool direct = !partitioned;
-  uint64_t rank0 = 0;
-  if (partitioned) {
-    direct = ws.toff[tiles] > ws.max_set;
-    rank0 = ws.toff[blockIdx.x];
-  }
+  const bool direct = ws.toff[tiles] > ws.max_set;
+  const uint64_t rank0 = ws.toff[blockIdx.x];
   constexpr int RPT = kDecTile / 4 / kDecThreads;  // 8 groups per thread
   uint32_t nib[RPT], rk[RPT];
 #pragma unroll
@@ -715,7 +731,7 @@ hipError_t launch_decode(const HashArgs& h, const s2r_params& p, uint64_t n,
   if (part) {
     S2R_DISPATCH_D(p.d, hipLaunchKernelGGL((k_dwrite<D>), dim3((uint32_t)tiles),
                                            dim3(kDecThreads), 0, s, h, n, nwords, bitmap, sketch,
-                                           w, out, ws, tiles, 1));
+                                           w, out, ws, tiles));
   } else {
     S2R_DISPATCH_D(p.d, hipLaunchKernelGGL((k_dwrite_direct<D>), dim3((uint32_t)tiles),
                                            dim3(kDecThreads), 0, s, h, n, nwords, bitmap, sketch,

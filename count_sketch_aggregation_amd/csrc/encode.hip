@@ -364,6 +364,7 @@ __global__ __launch_bounds__(kExpandThreads) void k_expand_dense(
       // a set bit lies below n <= ld and the group is 4-aligned: the load stays in the row
       if (nib[m]) v[m] = *reinterpret_cast<const f32x4*>(row + 4 * gidx);
     }
+    wait_vector_memory();  // one wait for the loads, then the stores issue back to back
 #pragma unroll
     for (int m = 0; m < G; ++m)
       if (nib[m])
@@ -448,6 +449,9 @@ __global__ __launch_bounds__(kExpandThreads) void k_expand_sparse(
         // ld % 4 == 0); a set group lies below n <= ld, 4-aligned
         v[u] = *reinterpret_cast<const f32x4*>(row + (has ? 4u * g[u] : 0u));
       }
+      wait_vector_memory();  // one wait for the loads, then the stores issue back to back
+#pragma unroll
+      for (int u = 0; u < UN; ++u) asm volatile("" : "+v"(v[u]));  // keeps the loads above it
 #pragma unroll
       for (int u = 0; u < UN; ++u)
         if (nib[u])
@@ -524,26 +528,30 @@ __global__ __launch_bounds__(kBinThreads) void k_bin(
   __shared__ uint32_t wtot[kBinThreads / kWave];
   const uint32_t c = blockIdx.x, k = blockIdx.y;
   const int tid = threadIdx.x;
-  const uint64_t total = offsets[(uint64_t)k * (tiles + 1) + tiles];
-  const uint64_t lim = total < cap ? total : cap;
+  // start < min(cap, n): the grid has ceil(min(cap, n) / kChunk) chunks
   const uint64_t start = (uint64_t)c * kChunk;
-  if (start >= lim) return;
-  const uint32_t cnt = (uint32_t)(lim - start < kChunk ? lim - start : kChunk);
-  for (uint32_t p = tid; p <= P; p += kBinThreads) hist[p] = 0;
-  __syncthreads();
   constexpr int R = kChunk / kBinThreads;
   uint32_t ii[R], pp[R], rk[R];
   float gg[R];
   const uint32_t* li = idx + (uint64_t)k * cap + start;
   const float* lv = val + (uint64_t)k * cap + start;
+  // The chunk's entries are read in the same round trip as the list length: indices are
+  // clamped inside the worker's list capacity, so every load issues unconditionally, and
+  // entries at or past the length are ignored below.
+  const uint64_t room = cap - start;
 #pragma unroll
   for (int r = 0; r < R; ++r) {
-    const uint32_t s = tid + kBinThreads * r;
-    if (s < cnt) {
-      ii[r] = li[s];
-      gg[r] = lv[s];
-    }
+    const uint64_t s = tid + kBinThreads * r;
+    const uint64_t sc = s < room ? s : room - 1;
+    ii[r] = li[sc];
+    gg[r] = lv[sc];
   }
+  const uint64_t total = offsets[(uint64_t)k * (tiles + 1) + tiles];
+  const uint64_t lim = total < cap ? total : cap;
+  if (start >= lim) return;
+  const uint32_t cnt = (uint32_t)(lim - start < kChunk ? lim - start : kChunk);
+  for (uint32_t p = tid; p <= P; p += kBinThreads) hist[p] = 0;
+  __syncthreads();
 #pragma unroll
   for (int r = 0; r < R; ++r) {
     const uint32_t s = tid + kBinThreads * r;

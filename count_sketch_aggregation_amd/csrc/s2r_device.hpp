@@ -176,6 +176,17 @@ __device__ __forceinline__ void lds_add_f32_many(float* tile, const uint32_t* ce
   }
 }
 
+// Waits for every outstanding vector memory operation of the wave (s_waitcnt vmcnt(0), the
+// other counters left alone).  Placed once after a batch of loads whose values are stored
+// under data-dependent branches: past the branch joins the compiler can no longer count
+// which operations are still in flight and would otherwise wait before each store for the
+// previous store's completion.
+__device__ __forceinline__ void wait_vector_memory() {
+  __builtin_amdgcn_sched_barrier(0);   // no instruction is scheduled across the wait
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // gfx9 encoding: vmcnt 0, expcnt 7, lgkmcnt 15
+  __builtin_amdgcn_sched_barrier(0);
+}
+
 // Workgroups are dispatched to the 8 XCDs round-robin by linear id, and each XCD has its own
 // L2.  This maps the linear id so that XCD x runs the x-th eighth of the (x-fastest) work
 // items in order: neighbouring items, which share cache lines at their edges, then run on one
