@@ -43,14 +43,14 @@ constexpr int kDecThreads = 256;
 constexpr int kDecTile = 8192;
 constexpr int kDecWords = kDecTile / 64;     // 128
 constexpr uint64_t kDirectTableBytes = 4ull << 20;  // one XCD's L2
-constexpr int kDBinThreads = 512;
+constexpr int kDBinThreads = 512;         // dense bitmaps: a chunk's set bits span few words
+constexpr int kDBinThreadsWide = 1024;    // sparse bitmaps: a chunk spans many rounds of words
 constexpr int kDUnsortThreads = 512;
 constexpr int kDMedianUnroll = 4;  // items in flight per thread (stride kAccThreads)
 constexpr int kTileLoads = 8;      // 16-byte cell loads per thread in flight when a tile fills
 constexpr uint64_t kDMedianTargetGroups = 1536;
 constexpr uint32_t kDMedianMaxSplits = 8;
 constexpr int kDBinWordsPerThread = 4;
-constexpr int kDBinBatchWords = kDBinThreads * kDBinWordsPerThread;  // 2048 words per round
 
 // Element word q (elements 64q .. 64q+63) of the query set, bits at or beyond n cleared.
 // nwords = ceil(n / 64).  With a block-granular bitmap (lb = log2 B > 0) the word is built
@@ -141,10 +141,11 @@ __device__ __forceinline__ void dbin_words(const uint64_t* __restrict__ bitmap, 
     wv[u] = bitmap[masked_src(q + u < q_end ? q + u : q_end - 1, lb)];
 }
 
-// One round of k_dbin's rank expansion over words [q0, q0 + kDBinBatchWords): masks the
+// One round of k_dbin's rank expansion over words [q0, q0 + NT * kDBinWordsPerThread): masks the
 // thread's raw words, ranks them with a workgroup scan and expands the set bits whose rank
 // lies in [start, end) into litem; advances q0 and rank0.  Called by the whole workgroup
 // (two barriers).
+template <int NT>
 __device__ __forceinline__ void dbin_round(const uint64_t* raw, uint64_t n, uint64_t nwords,
                                            uint64_t q_end, uint32_t lb, uint64_t start,
                                            uint64_t end, uint64_t& q0, uint64_t& rank0,
@@ -162,7 +163,7 @@ __device__ __forceinline__ void dbin_round(const uint64_t* raw, uint64_t n, uint
   if (lane == kWave - 1) wtot[wave] = inc;
   __syncthreads();
   uint32_t before = inc - sum, batch_total = 0;
-  for (int v = 0; v < kDBinThreads / kWave; ++v) {
+  for (int v = 0; v < NT / kWave; ++v) {
     if (v < wave) before += wtot[v];
     batch_total += wtot[v];
   }
@@ -175,18 +176,19 @@ __device__ __forceinline__ void dbin_round(const uint64_t* raw, uint64_t n, uint
   expand_owned_words<kDBinWordsPerThread>(wv, rk0, q0 + (uint64_t)tid * kDBinWordsPerThread,
                                           start, end, litem, lane);
   rank0 += batch_total;
-  q0 += kDBinBatchWords;
+  q0 += (uint64_t)NT * kDBinWordsPerThread;
   __syncthreads();  // wtot is reused next round
 }
 
-__global__ __launch_bounds__(kDBinThreads) void k_dbin(HashArgs h, uint64_t n,
+template <int NT>
+__global__ __launch_bounds__(NT) void k_dbin(HashArgs h, uint64_t n,
                                                        const uint64_t* __restrict__ bitmap,
                                                        uint64_t nwords, uint64_t tiles,
                                                        DecodeWs ws, uint32_t P) {
   extern __shared__ uint32_t hist[];  // P + 1
   __shared__ uint32_t litem[kChunk];  // indices in rank order
   __shared__ __align__(16) uint32_t sitem[kChunk];  // indices in partition order
-  __shared__ uint32_t wtot[kDBinThreads / kWave];
+  __shared__ uint32_t wtot[NT / kWave];
   const uint32_t c = blockIdx.x;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const uint64_t U = ws.toff[tiles];
@@ -197,7 +199,7 @@ __global__ __launch_bounds__(kDBinThreads) void k_dbin(HashArgs h, uint64_t n,
   const uint32_t cnt = (uint32_t)(U - start < kChunk ? U - start : kChunk);
   const uint64_t end = start + cnt;
 
-  // 1. expand ranks [start, end) into litem, kDBinBatchWords bitmap words per round: each
+  // 1. expand ranks [start, end) into litem, NT * kDBinWordsPerThread bitmap words per round: each
   //    thread holds kDBinWordsPerThread words and their ranks, and the waves expand only the
   //    non-empty words that meet the chunk (expand_owned_words).  The chunk's last rank lies
   //    at or before the tile where the next chunk starts, so words past that tile are not
@@ -209,26 +211,27 @@ __global__ __launch_bounds__(kDBinThreads) void k_dbin(HashArgs h, uint64_t n,
   // The next round's words are loaded before the current round is expanded (register sets
   // a and b alternate, so no loaded register is copied); past q_end they re-read the last
   // word in range and are never used.
+  constexpr uint64_t kRound = (uint64_t)NT * kDBinWordsPerThread;  // words per round
   uint64_t wa[kDBinWordsPerThread], wb[kDBinWordsPerThread];
   dbin_words<kDBinWordsPerThread>(bitmap, q0 + (uint64_t)tid * kDBinWordsPerThread, q_end, h.lb, wa);
   while (rank0 < end && q0 < q_end) {
-    dbin_words<kDBinWordsPerThread>(bitmap, q0 + kDBinBatchWords + (uint64_t)tid * kDBinWordsPerThread,
+    dbin_words<kDBinWordsPerThread>(bitmap, q0 + kRound + (uint64_t)tid * kDBinWordsPerThread,
                                     q_end, h.lb, wb);
-    dbin_round(wa, n, nwords, q_end, h.lb, start, end, q0, rank0, litem, wtot, tid);
+    dbin_round<NT>(wa, n, nwords, q_end, h.lb, start, end, q0, rank0, litem, wtot, tid);
     if (!(rank0 < end && q0 < q_end)) break;
-    dbin_words<kDBinWordsPerThread>(bitmap, q0 + kDBinBatchWords + (uint64_t)tid * kDBinWordsPerThread,
+    dbin_words<kDBinWordsPerThread>(bitmap, q0 + kRound + (uint64_t)tid * kDBinWordsPerThread,
                                     q_end, h.lb, wa);
-    dbin_round(wb, n, nwords, q_end, h.lb, start, end, q0, rank0, litem, wtot, tid);
+    dbin_round<NT>(wb, n, nwords, q_end, h.lb, start, end, q0, rank0, litem, wtot, tid);
   }
-  for (uint32_t p = tid; p <= P; p += kDBinThreads) hist[p] = 0;
+  for (uint32_t p = tid; p <= P; p += NT) hist[p] = 0;
   __syncthreads();
 
   // 2. counting sort by partition
-  constexpr int R = kChunk / kDBinThreads;
+  constexpr int R = kChunk / NT;
   uint32_t pp[R], rk[R];
 #pragma unroll
   for (int r = 0; r < R; ++r) {
-    const uint32_t s = tid + kDBinThreads * r;
+    const uint32_t s = tid + NT * r;
     if (s < cnt) {
       pp[r] = partition_of(h, litem[s]);
       rk[r] = atomicAdd(&hist[pp[r]], 1u);
@@ -236,7 +239,7 @@ __global__ __launch_bounds__(kDBinThreads) void k_dbin(HashArgs h, uint64_t n,
   }
   __syncthreads();
   {  // exclusive scan of hist[0..P) in place
-    const uint32_t per = (P + kDBinThreads - 1) / kDBinThreads;
+    const uint32_t per = (P + NT - 1) / NT;
     const uint32_t lo = tid * per < P ? tid * per : P;
     const uint32_t hi = lo + per < P ? lo + per : P;
     uint32_t sum = 0;
@@ -254,12 +257,12 @@ __global__ __launch_bounds__(kDBinThreads) void k_dbin(HashArgs h, uint64_t n,
     __syncthreads();
   }
   uint32_t* pf = ws.prefix + (uint64_t)c * (P + 1);  // one contiguous row per chunk
-  for (uint32_t p = tid; p < P; p += kDBinThreads) pf[p] = hist[p];
+  for (uint32_t p = tid; p < P; p += NT) pf[p] = hist[p];
   if (tid == 0) pf[P] = cnt;
   uint16_t* sl = ws.slot + start;
 #pragma unroll
   for (int r = 0; r < R; ++r) {
-    const uint32_t s = tid + kDBinThreads * r;
+    const uint32_t s = tid + NT * r;
     if (s < cnt) {
       const uint32_t pos = hist[pp[r]] + rk[r];
       sitem[pos] = litem[s];
@@ -269,9 +272,9 @@ __global__ __launch_bounds__(kDBinThreads) void k_dbin(HashArgs h, uint64_t n,
   __syncthreads();
   uint32_t* bo = ws.bidx + start;
   const uint32_t cnt4 = cnt / 4;
-  for (uint32_t q = tid; q < cnt4; q += kDBinThreads)
+  for (uint32_t q = tid; q < cnt4; q += NT)
     *reinterpret_cast<uint4*>(bo + 4 * q) = *reinterpret_cast<const uint4*>(&sitem[4 * q]);
-  for (uint32_t s = 4 * cnt4 + tid; s < cnt; s += kDBinThreads) bo[s] = sitem[s];
+  for (uint32_t s = 4 * cnt4 + tid; s < cnt; s += NT) bo[s] = sitem[s];
 }
 
 // ---------------------------------------------------------------------------------------
@@ -696,11 +699,23 @@ hipError_t launch_decode(const HashArgs& h, const s2r_params& p, uint64_t n,
     if (e != hipSuccess) return e;
     if (L.chunks > 0) {
       const size_t lds = (L.partitions + 1) * sizeof(uint32_t);
-      e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_dbin),
-                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+      // A chunk of kChunk set bits spans about nwords * kChunk / U bitmap words (max_set
+      // stands in for U on the host).  Where that is more than four rounds of the 512-thread
+      // kernel, twice the threads halve the rounds (measured on MI355X: 99 -> 80 us on a
+      // 1e9-element bitmap at 0.8% density; on denser ones the wide kernel is 40-65% slower)
+      const bool wide = nwords * (uint64_t)kChunk >
+                        4 * (uint64_t)kDBinThreads * kDBinWordsPerThread * ws.max_set;
+      const void* kfn = wide ? reinterpret_cast<const void*>(&k_dbin<kDBinThreadsWide>)
+                             : reinterpret_cast<const void*>(&k_dbin<kDBinThreads>);
+      e = hipFuncSetAttribute(kfn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
       if (e != hipSuccess) return e;
-      hipLaunchKernelGGL(k_dbin, dim3((uint32_t)L.chunks), dim3(kDBinThreads), lds, s, h, n,
-                         bitmap, nwords, L.tiles, ws, (uint32_t)L.partitions);
+      if (wide)
+        hipLaunchKernelGGL(k_dbin<kDBinThreadsWide>, dim3((uint32_t)L.chunks),
+                           dim3(kDBinThreadsWide), lds, s, h, n, bitmap, nwords, L.tiles, ws,
+                           (uint32_t)L.partitions);
+      else
+        hipLaunchKernelGGL(k_dbin<kDBinThreads>, dim3((uint32_t)L.chunks), dim3(kDBinThreads),
+                           lds, s, h, n, bitmap, nwords, L.tiles, ws, (uint32_t)L.partitions);
       e = hipGetLastError();
       if (e != hipSuccess) return e;
       const size_t tlds = ((size_t)p.d << p.log2_part) * sizeof(float);

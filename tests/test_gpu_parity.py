@@ -217,6 +217,23 @@ def test_decode_capacity_boundary():
         gp.assert_decode_matches(out, want, tol, gp.bits_of(bm, n), exact=True)
 
 
+@pytest.mark.parametrize("n,density", [(3_000_000, 0.003), (1_000_003, 0.0004)])
+def test_decode_sparse_bitmap_tight_capacity(n, density):
+    """A sparse bitmap (fewer set bits than bitmap words) with max_set = U: the partitioned
+    decode bins each rank chunk with the wide 1024-thread kernel, over many rounds of
+    bitmap words per chunk."""
+    d, L = 5, 20  # a 20 MiB table: the partitioned path
+    p, op = gp.params_pair(77, d, L)
+    sketch = WL.random_sketch((d, 1 << L), 5)
+    bm = WL.random_bitmap(n, density, 6)
+    U = int(gp.bits_of(bm, n).sum())
+    assert U < (n + 63) // 64
+    gp.say(f"decode sparse bitmap n={n} U={U}")
+    want, tol = oracle.decode_dense(op, n, bm, sketch.astype(np.float64))
+    out = gp.run_decode(p, n, bm, sketch, path="partitioned", max_set=U)
+    gp.assert_decode_matches(out, want, tol, gp.bits_of(bm, n), exact=True)
+
+
 # ---------------------------------------------------------------------------------------
 # end to end
 
