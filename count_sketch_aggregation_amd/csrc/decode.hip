@@ -96,25 +96,36 @@ __device__ __forceinline__ uint64_t masked_word(const uint64_t* __restrict__ bit
 }
 
 // ---------------------------------------------------------------------------------------
-// k_dcount: 256 threads, a wave per 8192-element tile (kDcountTiles tiles per workgroup, no
-// barrier): lane l takes words 2l and 2l + 1 of the tile, both loads issued before either
-// is masked, and a wave sum gives the tile's count.
+// k_dcount: 256 threads, a wave per two 8192-element tiles (no barrier): lane l takes words
+// 4l .. 4l + 3 of the wave's 256 (lanes 0-31 the first tile, 32-63 the second), all four
+// loads issued before any is masked, and a half-wave sum gives each tile's count.
 constexpr int kDcountThreads = 256;
-constexpr int kDcountTiles = kDcountThreads / kWave;
+constexpr int kDcountTiles = 2 * kDcountThreads / kWave;  // tiles per workgroup
+
+// Sum over the 32 lanes of each half of the wave.
+__device__ __forceinline__ uint32_t half_wave_sum(uint32_t x) {
+#pragma unroll
+  for (int off = kWave / 4; off > 0; off >>= 1) x += __shfl_xor(x, off, kWave);
+  return x;
+}
 
 __global__ __launch_bounds__(kDcountThreads) void k_dcount(const uint64_t* __restrict__ bitmap,
                                                            uint64_t n, uint64_t nwords,
                                                            uint64_t tiles, uint32_t lb,
                                                            uint32_t* __restrict__ tcount) {
-  const uint64_t t = (uint64_t)blockIdx.x * kDcountTiles + (threadIdx.x >> 6);
-  if (t >= tiles) return;  // wave-uniform
   const int lane = threadIdx.x & 63;
-  const uint64_t q0 = t * kDecWords + 2 * lane;
-  const uint64_t r0 = bitmap[masked_src(q0 < nwords ? q0 : nwords - 1, lb)];
-  const uint64_t r1 = bitmap[masked_src(q0 + 1 < nwords ? q0 + 1 : nwords - 1, lb)];
-  const uint32_t c = wave_sum((uint32_t)(__popcll(masked_from(r0, nwords, n, q0, lb)) +
-                                         __popcll(masked_from(r1, nwords, n, q0 + 1, lb))));
-  if (lane == 0) tcount[t] = c;
+  const uint64_t t0 = ((uint64_t)blockIdx.x * (kDcountThreads / kWave) + (threadIdx.x >> 6)) * 2;
+  if (t0 >= tiles) return;  // wave-uniform
+  const uint64_t q0 = t0 * kDecWords + 4 * lane;
+  uint64_t r[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) r[u] = bitmap[masked_src(q0 + u < nwords ? q0 + u : nwords - 1, lb)];
+  uint32_t c = 0;
+#pragma unroll
+  for (int u = 0; u < 4; ++u) c += (uint32_t)__popcll(masked_from(r[u], nwords, n, q0 + u, lb));
+  c = half_wave_sum(c);
+  const uint64_t t = t0 + (lane >> 5);
+  if ((lane & 31) == 0 && t < tiles) tcount[t] = c;
 }
 
 // ---------------------------------------------------------------------------------------

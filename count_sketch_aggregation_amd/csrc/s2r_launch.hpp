@@ -17,7 +17,7 @@ constexpr int kTileWords = kTile / 64;              // 64 bitmap words per tile
 constexpr int kStreamWaveSpan = kTile / (kStreamThreads / 64);  // elements per wave
 
 constexpr int kExpandThreads = 256;
-constexpr uint64_t kExpandGroups = 4096;             // expand workgroups per launch, all workers
+constexpr uint64_t kExpandGroups = 8192;             // expand workgroups per launch, all workers
 constexpr uint32_t kDenseSpan = 1024;                // non-zeros above which a span is expanded
                                                      // by a whole workgroup, not one wave
 constexpr int kScatterThreads = 256;
