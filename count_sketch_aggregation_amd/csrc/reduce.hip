@@ -27,7 +27,9 @@ __global__ __launch_bounds__(256) void k_reduce(uint32_t W, uint64_t cells, uint
     for (uint64_t c = gid; c < c4; c += stride) {
       f32x4 acc = __builtin_nontemporal_load(in + c);
       for (uint32_t k = 1; k < W; ++k) acc += __builtin_nontemporal_load(in + (uint64_t)k * c4 + c);
-      out[c] = acc;
+      // non-temporal: the merged sketch is read once by the decode, well after this pass
+      // (measured on MI355X: 9 us faster over the 1e9-element workload's 2.6 GB, same elsewhere)
+      __builtin_nontemporal_store(acc, out + c);
     }
   } else {
     for (uint64_t c = gid; c < cells; c += stride) {
