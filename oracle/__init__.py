@@ -88,6 +88,8 @@ def _bind(L: ctypes.CDLL) -> ctypes.CDLL:
     L.orc_reduce.restype = None
     L.orc_decode.argtypes = [P(OrcParams), u64, vp, vp, vp, vp, vp, vp, u64]
     L.orc_decode.restype = u64
+    L.orc_gather_sum.argtypes = [u32, vp, vp, vp, u64, u64, vp, vp]
+    L.orc_gather_sum.restype = None
     L.orc_topk_ef.argtypes = [vp, vp, u64, u64, u64, vp, vp, vp]
     L.orc_topk_ef.restype = ctypes.c_int
     L.orc_bitmap_words.argtypes = [P(OrcParams), u64]
@@ -272,6 +274,24 @@ def decode_dense(p: OrcParams, n: int, bitmap, S, A=None):
     out[i] = v
     tol[i] = t
     return out, tol
+
+
+def gather_sum(lists, n: int):
+    """Exact aggregate of W workers' (index, value) lists, worker by worker: dense fp64
+    out[n] and the absolute mass[n] (sum of |value| per element)."""
+    W = len(lists)
+    stride = max([max(int(i.size), 1) for i, _ in lists] + [1])
+    idx = np.zeros((W, stride), dtype=np.uint32)
+    val = np.zeros((W, stride), dtype=np.float32)
+    ln = np.zeros(W, dtype=np.uint64)
+    for k, (i, v) in enumerate(lists):
+        idx[k, :i.size] = i
+        val[k, :v.size] = v
+        ln[k] = i.size
+    out = np.empty(max(n, 1), dtype=np.float64)
+    mass = np.empty(max(n, 1), dtype=np.float64)
+    lib().orc_gather_sum(W, _ptr(idx), _ptr(val), _ptr(ln), stride, n, _ptr(out), _ptr(mass))
+    return out[:n], mass[:n]
 
 
 def topk_ef(grad: np.ndarray, residual: np.ndarray | None, block: int, K: int):

@@ -13,6 +13,8 @@
 //   * Section 3.1, "Decompressing Sparse Gradient" and Algorithm 1: for every set bit
 //     i of the merged bitmap, g_hat(i) is the median over the r rows of
 //     s_j(i) * S[j, h_j(i)].
+//   * Section 1 and Section 2.2 (Fig. 1(b)): the lossless alternative the sketch is
+//     measured against, the gathered (index, value) lists of all workers added up.
 //
 // Readings taken where the pages leave a step open (each also listed in the design notes):
 //   * one bitmap bit per block of 2^log2_block consecutive elements (the pages give the
@@ -246,6 +248,28 @@ uint64_t orc_decode(const orc_params* p, uint64_t n, const uint64_t* bitmap, con
     ++count;
   }
   return count;
+}
+
+// ---------------------------------------------------------------------------------
+// Lossless aggregation, the comparator the sketch is measured against (Section 1 and
+// Section 2.2 with Fig. 1(b): without a mergeable structure, workers gather one another's
+// indices and values and add them).  For each worker k = 0..W-1 in turn, every entry t below
+// len[k] of its list adds val[k][t] to element idx[k][t]; entries at or beyond n are skipped.
+//   idx, val [W][stride]; out [n] = the exact sum in fp64; mass [n] = the sum of |value|.
+void orc_gather_sum(uint32_t W, const uint32_t* idx, const float* val, const uint64_t* len,
+                    uint64_t stride, uint64_t n, double* out, double* mass) {
+  for (uint64_t i = 0; i < n; ++i) {
+    out[i] = 0.0;
+    mass[i] = 0.0;
+  }
+  for (uint32_t k = 0; k < W; ++k)
+    for (uint64_t t = 0; t < len[k]; ++t) {
+      const uint64_t i = idx[(uint64_t)k * stride + t];
+      if (i >= n) continue;
+      const double v = (double)val[(uint64_t)k * stride + t];
+      out[i] += v;
+      mass[i] += std::fabs(v);
+    }
 }
 
 // ---------------------------------------------------------------------------------

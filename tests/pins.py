@@ -21,7 +21,10 @@ Each ``pin_*`` function raises AssertionError when the oracle (whichever build t
   * block-wise Top-K with error feedback (Section 2.2; Appendix A.2): numpy's block norms
     and ordering, out + residual = g, the kept mass bound of Theorem 2's proof, and the
     telescoping sum of the error sequence;
-  * unbiasedness of the single-row estimate over random hash constants (Theorem 1).
+  * unbiasedness of the single-row estimate over random hash constants (Theorem 1);
+  * the decode bound tol(i) = 1e-5 max_j (mass of row j's cell) + 1e-12, recomputed from the
+    explicit |A_j|^T |g| of every worker;
+  * the lossless gathered sum (Section 1; Section 2.2, Fig. 1(b)) as numpy's dense sum.
 
 The test modules run every pin against the real oracle and against altered copies of it.
 """
@@ -356,6 +359,55 @@ def pin_block_query():
         assert np.array_equal(tol > 0, inset)
 
 
+def pin_decode_tolerance():
+    """The decode bound the parity tests use, tol(i) = 1e-5 * max_j M_j[h_j(i)] + 1e-12 with
+    M_j = sum_k |A_j|^T |g_k| the absolute mass of row j after aggregation (the sum of the
+    magnitudes of every contribution to the cell, Section 3.1's projection A^T g with |A|
+    and |g|), recomputed here from explicit mapping matrices at every queried element:
+    rows d = 1..7, two workers, an element-granular and a block-granular bitmap.  Integer
+    data make every mass exact, so the bound must match bit for bit."""
+    n, W = 120, 2
+    for (d, L, K, lb) in [(1, 4, 4, 0), (2, 5, 2, 0), (3, 4, 1, 0), (4, 6, 6, 0), (5, 5, 3, 0),
+                          (6, 4, 4, 0), (7, 5, 2, 0), (3, 5, 3, 2)]:
+        p = O.params_from_seed(900 + 10 * d + lb, d, L, K, log2_block=lb)
+        gs = [_int_grad(n, 0.2, 60 + 7 * d + k) for k in range(W)]
+        # one large-magnitude element, so the bound differs from cell to cell by orders
+        gs[1][17] = np.float32(3000.0)
+        encs = [O.encode_dense(p, g) for g in gs]
+        bm, S, A = O.reduce(np.stack([e["bitmap"] for e in encs]), np.stack([e["S"] for e in encs]),
+                            np.stack([e["A"] for e in encs]))
+        idx, _, tol = O.decode(p, n, bm, S, A)
+        mats = _mapping_matrices(p, n)
+        absg = sum(np.abs(g.astype(np.float64)) for g in gs)
+        mass = np.stack([np.abs(mats[j]).T @ absg for j in range(d)])  # [d][w]
+        keys = idx.astype(np.int64)
+        per_row = np.stack([mass[j][np.argmax(np.abs(mats[j][keys]), axis=1)] for j in range(d)])
+        want = 1e-5 * per_row.max(axis=0) + 1e-12
+        assert idx.size > 0 and np.array_equal(tol, want), (d, lb)
+
+
+def pin_gather_sum():
+    """The lossless aggregate (Section 1; Section 2.2, Fig. 1(b)): gathering every worker's
+    (index, value) list and adding gives numpy's sum of the dense gradients; the mass is the
+    sum of magnitudes; indices at or beyond n are skipped; an empty list adds nothing."""
+    n, W = 700, 4
+    gs = [_int_grad(n, 0.15, 500 + k) for k in range(W)]
+    gs[2][:] = 0  # one worker with an empty list
+    lists = [(np.flatnonzero(g).astype(np.uint32), g[g != 0]) for g in gs]
+    out, mass = O.gather_sum(lists, n)
+    dense = np.stack(gs).astype(np.float64)
+    assert np.array_equal(out, dense.sum(axis=0))
+    assert np.array_equal(mass, np.abs(dense).sum(axis=0))
+    # entries at or beyond n change nothing
+    extra = [(np.append(i, np.uint32(n + k)), np.append(v, np.float32(5.0))) for k, (i, v) in
+             enumerate(lists)]
+    out2, _ = O.gather_sum(extra, n)
+    assert np.array_equal(out2, out)
+    # one worker alone: its gradient back
+    out1, _ = O.gather_sum(lists[:1], n)
+    assert np.array_equal(out1, gs[0].astype(np.float64))
+
+
 def _topk_numpy(g, block, K):
     """numpy: squared block norms (fp64), kept blocks by (norm desc, id asc), out, residual."""
     n = g.size
@@ -438,6 +490,7 @@ ALL_PINS = [
     pin_splitmix64, pin_params_draw_order, pin_hash_closed_forms, pin_hash_statistics,
     pin_bitmap_and_list, pin_sketch_projection, pin_zeros_do_not_matter, pin_linearity,
     pin_signed_permutation, pin_reduce, pin_median_query, pin_exact_recovery,
-    pin_unbiased_single_row, pin_block_bitmap, pin_block_query, pin_topk_numpy,
+    pin_unbiased_single_row, pin_decode_tolerance, pin_block_bitmap, pin_block_query,
+    pin_gather_sum, pin_topk_numpy,
     pin_topk_identities, pin_topk_error_feedback,
 ]
