@@ -3,8 +3,8 @@
 
 One step = s2r_encode (all W workers) -> s2r_reduce -> s2r_decode over one batch of
 synthetic gradients already resident in HBM.  The metric is gradient elements per second,
-W * N / t_step, in units of 1e9, plus the fraction of the 8 TB/s HBM roofline that the
-dominant phase reaches on its algorithmic bytes:
+W * N / t_step, in units of 1e9, and the fraction of the 8 TB/s HBM peak the step reaches
+on its algorithmic bytes:
 
   encode  W * (4N + 8 words + 4 d w)        read gradients, write bitmaps and sketches
   reduce  (W + 1) * (4 d w + 8 words)       read W sketches/bitmaps, write one of each
@@ -12,16 +12,22 @@ dominant phase reaches on its algorithmic bytes:
 
 (words = bitmap words, ceil(N/64) at the default per-element granularity; U = elements
 queried by the decode, the set bits of the merged bitmap).  List writes and any extra
-traffic of the implementation are not credited.
+traffic of the implementation are not credited.  The default workload is `large`
+(W = 8, N = 1e9), the largest configuration.
 
-Besides `value` (K steps back to back, host-timed), the line reports the median and minimum
-of the per-step event times, the same for `--cold-reps` steps each timed alone after an
-untimed 512 MiB write that evicts L2 and the Infinity Cache, a plain streaming read of
-2 GiB measured on the same GPU (the achievable read ceiling) with the step's fraction of it,
-the estimation error of the decoded aggregate against the exact sum, and the CPU oracle's
-rate on a bounded sample of the same workload.
+`value` and `ms_per_step` come from K steps back to back, host-timed.  The same K steps are
+then run again with the library's kernel trace attached (HIP events recorded on the
+library's stream around every launch, include/s2r_diag.h): `kernels` lists each kernel's
+average launch time and its algorithmic bytes per launch, and `roofline` is the dominant
+kernel's algorithmic bytes per launch over its average launch time against the 8 TB/s
+peak.  The line also carries the median and minimum per-step event times, cold-cache steps
+(each timed alone after an untimed 512 MiB write that evicts L2 and the Infinity Cache), a
+plain streaming read of 2 GiB on the same GPU (the achievable read ceiling), the sketch
+ratio lambda both ways, the estimation error of the decoded aggregate against the exact sum
+formed on the GPU by the lossless comparator (s2r_gather_sum, which is timed too), and the
+CPU oracle's rate on a bounded sample of the same workload with the host's identity.
 
-Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--workload embedding]
+Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--workload large]
 Prints ONE JSON line on stdout; progress goes to stderr.
 
 `python bench.py --copy-reference` instead runs a plain 1 GiB device copy (an elementwise
@@ -77,66 +83,82 @@ def build_inputs(wl, dev, hash_family: str, log2_block: int = 0, log2_part: int 
     return p, grad, ld, cap, sparse
 
 
-def estimation_error(wl, sparse, out_dev) -> dict:
-    """Relative l2 error of the decoded aggregate against the exact sum of the workers'
-    gradients, sum_k g_k, formed in fp64 with numpy from the same seeded (index, value) lists:
-    ||g_hat - sum_k g_k|| / ||sum_k g_k||, over all N elements, and over the union of the
-    workers' non-zeros.  Measured after the timed region."""
-    import numpy as np
+def kernel_alg_bytes(name: str, wl, W: int, ewords: int, bwords: int, nnz_total: int, U: int):
+    """Algorithmic bytes of one launch of a library kernel (what its step must move at
+    least; list writes, partition round trips and atomic read-modify-writes are not
+    credited).  None for kernels whose work is not a byte stream (scans, list expansion)."""
+    N, dw = wl.N, wl.d * wl.w
+    table = {
+        "k_stream": W * (4 * N + 8 * ewords),            # read gradient, write bitmap
+        "k_blockbits": W * 8 * (ewords + bwords),
+        "k_bin": 16 * nnz_total,                         # read and write (index, value)
+        "k_accumulate": 8 * nnz_total + 4 * W * dw,      # read pairs, write sketch
+        "k_scatter": 8 * nnz_total,
+        "k_fill_zero": 4 * W * dw,
+        "k_reduce": (W + 1) * (4 * dw + 8 * bwords),     # W sketches + bitmaps in, one out
+        "k_dcount": 8 * bwords,
+        "k_dbin": 8 * bwords + 6 * U,                    # bitmap in, index + rank slot out
+        "k_dmedian": 4 * dw + 8 * U,                     # cells once, index in, median out
+        "k_dunsort": 10 * U,
+        "k_dwrite": 8 * bwords + 4 * N + 4 * U,          # bitmap and medians in, g_hat out
+        "k_dwrite_direct": 8 * bwords + 4 * N + min(4 * dw, 4 * wl.d * U),
+    }
+    return table.get(name)
 
-    idx_all = np.concatenate([x[0] for x in sparse]).astype(np.int64)
-    val_all = np.concatenate([x[1] for x in sparse]).astype(np.float64)
-    sup, inv = np.unique(idx_all, return_inverse=True)
-    gsum = np.zeros(sup.size, dtype=np.float64)
-    np.add.at(gsum, inv, val_all)
-    ghat = out_dev.cpu().numpy().astype(np.float64)
-    on_sup = ghat[sup] - gsum
-    err2_sup = float(np.dot(on_sup, on_sup))
-    off = ghat.copy()
-    off[sup] = 0.0
-    err2_all = err2_sup + float(np.dot(off, off))
-    ref2 = float(np.dot(gsum, gsum))
-    return {"rel_l2_all": round((err2_all / ref2) ** 0.5, 6) if ref2 else None,
-            "rel_l2_support": round((err2_sup / ref2) ** 0.5, 6) if ref2 else None,
-            "union_nnz": int(sup.size)}
 
-
-def library_source_sha256() -> str:
-    """sha256 over the library's sources (kernels, launchers, C header), by file name."""
-    import glob
+def library_source_sha256(files) -> str:
+    """sha256 over the named library sources (relative to the repository root)."""
     import hashlib
 
     h = hashlib.sha256()
-    files = sorted(glob.glob(os.path.join(ROOT, "count_sketch_aggregation_amd", "csrc", "*")))
-    files.append(os.path.join(ROOT, "include", "s2r.h"))
-    for f in files:
+    for f in sorted(files):
         h.update(os.path.basename(f).encode())
-        with open(f, "rb") as fh:
+        with open(os.path.join(ROOT, f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()
 
 
-def measured_traffic(workload: str, phase: str):
-    """HBM bytes per call of `phase` from the committed counter summary
-    (profiles/<workload>_traffic.md: FETCH_SIZE and WRITE_SIZE passes scaled by the copy
-    reference), or None if there is none or the library sources changed since it was taken."""
-    path = os.path.join(ROOT, "profiles", f"{workload}_traffic.md")
-    if phase != "encode" or not os.path.exists(path):
+def measured_traffic(workload: str, kernel: str):
+    """HBM bytes per launch of `kernel` from the committed counter summary
+    profiles/<kernel>_<workload>_traffic.md (FETCH_SIZE and WRITE_SIZE passes, each scaled by
+    what the counter reads for a plain copy of known size), or None if there is none or the
+    sources it names have changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_traffic.md")
+    if not os.path.exists(path):
         return None
     vals = {}
     with open(path) as fh:
         for line in fh:
-            if ":" in line and line.split(":", 1)[0] in ("traffic_bytes_per_call", "source_sha256"):
+            if ":" in line:
                 k, v = line.split(":", 1)
-                vals[k] = v.strip()
-    if vals.get("source_sha256") != library_source_sha256() or "traffic_bytes_per_call" not in vals:
+                if k in ("traffic_bytes_per_launch", "source_sha256", "source_files"):
+                    vals[k] = v.strip()
+    if not {"traffic_bytes_per_launch", "source_sha256", "source_files"} <= set(vals):
         return None
-    return int(vals["traffic_bytes_per_call"])
+    if library_source_sha256(vals["source_files"].split()) != vals["source_sha256"]:
+        return None
+    return int(vals["traffic_bytes_per_launch"])
+
+
+def host_identity() -> dict:
+    """CPU model and core counts of the host the CPU baseline ran on."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"cpu_model": model, "nproc": len(os.sched_getaffinity(0)),
+            "cpu_count": os.cpu_count()}
 
 
 def cpu_baseline(wl, sparse, p_dict, budget_s: float = 20.0):
-    """The fp64 oracle, single-threaded, on the first workers of the same workload until
-    about `budget_s` seconds of oracle work are done (at least one worker)."""
+    """The fp64 oracle, single-threaded, on the first workers of the same workload (each at
+    its full N) until about `budget_s` seconds of oracle work are done (at least one
+    worker): encode of each, then reduce and decode over them."""
     import numpy as np
 
     import oracle
@@ -144,22 +166,25 @@ def cpu_baseline(wl, sparse, p_dict, budget_s: float = 20.0):
 
     op = oracle.params_from_constants(p_dict["d"], p_dict["log2_w"], p_dict["log2_part"],
                                       p_dict["pA"], p_dict["pB"], p_dict["hA"], p_dict["hB"],
-                                      p_dict["sA"], p_dict["sB"])
+                                      p_dict["sA"], p_dict["sB"], log2_block=p_dict["log2_block"])
     elapsed = 0.0
     encs = []
     for k in range(wl.W):
         g = WL.dense_from_sparse(wl.N, *sparse[k])
         t0 = time.perf_counter()
-        encs.append(oracle.encode_dense(op, g))
+        # the list capacity the GPU path gets: the largest worker's non-zero count
+        encs.append(oracle.encode_dense(op, g, cap=max(x[0].size for x in sparse)))
         elapsed += time.perf_counter() - t0
         del g
-        est_total = elapsed / len(encs) * (len(encs) + 1) * 1.5
+        # reduce + decode cost about as much again as the encodes (more for sparse bitmaps)
+        est_total = elapsed / len(encs) * (len(encs) + 1) * 2.0
         if est_total > budget_s:
             break
     Wp = len(encs)
     t0 = time.perf_counter()
     bm, S, A = oracle.reduce(np.stack([e["bitmap"] for e in encs]), np.stack([e["S"] for e in encs]),
                              np.stack([e["A"] for e in encs]))
+    del encs
     oracle.decode(op, wl.N, bm, S, A)
     elapsed += time.perf_counter() - t0
     return {
@@ -169,6 +194,7 @@ def cpu_baseline(wl, sparse, p_dict, budget_s: float = 20.0):
         "kind": "oracle",
         "sample": f"{Wp} of {wl.W} workers of the {wl.name} workload (full N={wl.N} each): "
                   f"fp64 encode of each, reduce and decode over them; {elapsed:.1f} s",
+        "host": host_identity(),
     }
 
 
@@ -271,13 +297,106 @@ def topk_stage(args) -> int:
     return 0
 
 
+def traced_steps(step, steps: int, stream):
+    """Runs `steps` more steps with a kernel trace attached (include/s2r_diag.h): the library
+    records a HIP event on its stream before every kernel it launches and after each call's
+    last launch.  Returns {kernel: (launches, total ms)} over those steps and their wall ms."""
+    import torch
+
+    import count_sketch_aggregation_amd as s2r
+
+    traces = []
+    for _ in range(steps):
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(s2r.TRACE_MAX)]
+        for e in evs:
+            e.record(stream)  # creates the event; the library records it again below
+        t = s2r.s2r_trace()
+        t.capacity = s2r.TRACE_MAX
+        t.count = 0
+        for i, e in enumerate(evs):
+            t.events[i] = e.cuda_event
+        traces.append((t, evs))
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for t, _ in traces:
+        s2r.s2r_diag_trace_attach(t)
+        try:
+            step()
+        finally:
+            s2r.s2r_diag_trace_attach(None)
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1e3
+    per = {}
+    for t, evs in traces:
+        for i in range(t.count - 1):
+            name = t.names[i].decode()
+            if name == "end":
+                continue
+            n, ms = per.get(name, (0, 0.0))
+            per[name] = (n + 1, ms + evs[i].elapsed_time(evs[i + 1]))
+    return per, wall_ms
+
+
+def gpu_estimation_error(s2r, wl, cap, buf, out, stream) -> dict:
+    """Relative l2 error of the decoded aggregate against the exact sum of the workers'
+    gradients, ||g_hat - sum_k g_k|| / ||sum_k g_k||, with the exact sum formed on the GPU by
+    the lossless comparator (s2r_gather_sum over the encode's own lists, an fp32 sum in worker
+    order, within (W - 1) 2^-24 relative of the exact real sum) and both norms accumulated
+    in fp64 on the device.  Also times the comparator."""
+    import torch
+
+    exact = torch.empty(wl.N, dtype=torch.float32, device=out.device)
+
+    def gather():
+        s2r.s2r_gather_sum(wl.W, buf["idx"], buf["val"], cap, buf["nnz"], wl.N, exact, stream=stream)
+
+    gather()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    reps = 5
+    e0.record(stream)
+    for _ in range(reps):
+        gather()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    err2 = ref2 = err2_listed = 0.0
+    listed = 0
+    chunk = 1 << 27
+    for a in range(0, wl.N, chunk):
+        x = exact[a:a + chunk].double()
+        y = out[a:a + chunk].double()
+        dif = y - x
+        on = x != 0
+        err2 += float((dif * dif).sum())
+        err2_listed += float((dif[on] * dif[on]).sum())
+        ref2 += float((x * x).sum())
+        listed += int(on.sum())
+    nnz_total = int(buf["nnz"].sum())
+    return {
+        "rel_l2_all": round((err2 / ref2) ** 0.5, 6) if ref2 else None,
+        "rel_l2_on_nonzero_sum": round((err2_listed / ref2) ** 0.5, 6) if ref2 else None,
+        "nonzero_sum_elements": listed,
+        "exact_sum": "s2r_gather_sum (lossless comparator) on the device",
+        "lossless_comparator": {
+            "ms": round(ms, 4),
+            "G_elem_s": round(wl.W * wl.N / (ms * 1e-3) / 1e9, 3),
+            # zero-fill of the dense output, then W list reads and scattered adds
+            "alg_bytes": 4 * wl.N + 8 * nnz_total,
+            "note": "consumes the compacted lists the encode writes; the sketch step's time "
+                    "includes producing them",
+        },
+    }
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="embedding",
-                    help="tiny | embedding | resnet50_blocktopk | transformer_mixed | large")
+    ap.add_argument("--workload", default="large",
+                    help="tiny | embedding | resnet50_blocktopk | transformer_mixed | large "
+                         "(default: large, the largest single-GPU configuration)")
     ap.add_argument("--hash", dest="hash_family", default="partitioned",
                     choices=["partitioned", "independent"])
     ap.add_argument("--block", type=int, default=0, metavar="LOG2_B",
@@ -289,7 +408,10 @@ def main() -> int:
     ap.add_argument("--cold-reps", type=int, default=20,
                     help="extra steps timed alone after flushing the caches (0 to skip)")
     ap.add_argument("--no-error", action="store_true",
-                    help="skip the estimation-error report (relative l2 error vs the exact sum)")
+                    help="skip the estimation error and the lossless comparator")
+    ap.add_argument("--no-trace", action="store_true",
+                    help="skip the per-kernel event trace (the roofline then falls back to the "
+                         "dominant call)")
     ap.add_argument("--stage", default="aggregate", choices=["aggregate", "topk"],
                     help="aggregate: encode+reduce+decode (default); topk: the block-wise Top-K "
                          "with error feedback that precedes it (ResNet-50 workload)")
@@ -322,6 +444,7 @@ def main() -> int:
     p, grad, ld, cap, sparse = build_inputs(wl, dev, args.hash_family, args.block, args.log2_part)
     buf = s2r.alloc_encode_buffers(p, wl.W, wl.N, cap, dev)
     words = s2r.s2r_block_bitmap_words(wl.N, args.block)
+    ewords = s2r.s2r_bitmap_words(wl.N)
     bm = torch.empty(max(words, 1), dtype=torch.int64, device=dev)
     sk = torch.empty((wl.d, 1 << wl.log2_w), dtype=torch.float32, device=dev)
     out = torch.empty(wl.N, dtype=torch.float32, device=dev)
@@ -349,12 +472,14 @@ def main() -> int:
     torch.cuda.synchronize()
     nnz = buf["nnz"].cpu().numpy()
     assert all(int(x) <= cap for x in nnz), "list capacity exceeded"
+    nnz_total = int(nnz.sum())
     # U = elements queried by the decode (every element of every set block)
     B = 1 << args.block
     nblocks = (wl.N + B - 1) // B
     setb = np.flatnonzero(np.unpackbits(bm.cpu().numpy().view(np.uint8), bitorder="little")[:nblocks])
     U = int(setb.size) * B - ((nblocks * B - wl.N) if setb.size and setb[-1] == nblocks - 1 else 0)
 
+    # --- the timed region: K steps back to back, host clock around them -----------------
     events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -381,10 +506,40 @@ def main() -> int:
     phases = {k: {"ms": round(phase_ms[k], 4), "alg_bytes": b_alg[k],
                   "alg_GBs": round(b_alg[k] / (phase_ms[k] * 1e-3) / 1e9, 1)} for k in phase_ms}
     step_ev = sorted(ev[0].elapsed_time(ev[3]) for ev in events)
+    step_alg = sum(b_alg.values()) / (ms_per_step * 1e-3) / 1e9
 
-    # Cold-cache repetitions: before each, an untimed 512 MiB write evicts L2 and the
-    # Infinity Cache; each step is timed alone with events.  Then a plain streaming read of
-    # 2 GiB on the same GPU for the measured read ceiling.
+    # --- per-kernel durations: the same steps again with the kernel trace attached -------
+    kernels = {}
+    traced_ms = None
+    if not args.no_trace:
+        per, traced_wall = traced_steps(step, args.steps, stream)
+        traced_ms = traced_wall / args.steps
+        for name, (n, ms) in sorted(per.items(), key=lambda kv: -kv[1][1]):
+            us = ms * 1e3 / n
+            ab = kernel_alg_bytes(name, wl, wl.W, ewords, words, nnz_total, U)
+            kernels[name] = {"avg_us": round(us, 2), "launches_per_step": round(n / args.steps, 3),
+                             "alg_bytes_per_launch": ab,
+                             "alg_GBs": round(ab / (us * 1e-6) / 1e9, 1) if ab else None}
+    if kernels:
+        dom = max(kernels, key=lambda k: kernels[k]["avg_us"] * kernels[k]["launches_per_step"])
+        kd = kernels[dom]
+        achieved = kd["alg_GBs"]
+        roofline = {"bound": "hbm", "kernel": dom, "achieved": achieved, "peak": HBM_PEAK_GBS,
+                    "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4) if achieved else None,
+                    "traffic": measured_traffic(wl.name, dom),
+                    "alg_bytes_per_launch": kd["alg_bytes_per_launch"], "avg_launch_us": kd["avg_us"],
+                    "timing": "HIP events recorded by the library on its stream around each launch "
+                              f"of {dom} over {args.steps} traced steps"}
+    else:  # no trace: the dominant call, as a whole
+        domc = max(phase_ms, key=phase_ms.get)
+        achieved = b_alg[domc] / (phase_ms[domc] * 1e-3) / 1e9
+        roofline = {"bound": "hbm", "kernel": f"s2r_{domc} (a call, not one kernel)",
+                    "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                    "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None}
+
+    # --- cold-cache repetitions and the measured read ceiling ----------------------------
+    # Before each cold step an untimed 512 MiB write evicts L2 and the Infinity Cache; each
+    # step is timed alone with events.  Then a plain streaming read of 2 GiB.
     flush = torch.empty(512 << 18, dtype=torch.float32, device=dev)
     cold = []
     for _ in range(args.cold_reps):
@@ -407,11 +562,13 @@ def main() -> int:
     torch.cuda.synchronize()
     read_GBs = 5 * nbytes / (r0.elapsed_time(r1) * 1e-3) / 1e9
     del big
-    dom = max(phase_ms, key=phase_ms.get)
-    achieved = b_alg[dom] / (phase_ms[dom] * 1e-3) / 1e9
-    step_alg = sum(b_alg.values()) / (ms_per_step * 1e-3) / 1e9
-    log(f"ms/step {ms_per_step:.3f}  phases {phases}  step alg GB/s {step_alg:.0f}")
+    log(f"ms/step {ms_per_step:.3f}  phases {phases}  step alg GB/s {step_alg:.0f}  "
+        f"roofline {roofline['kernel']} {roofline['achieved']} GB/s")
 
+    lam = {"dw_over_nnz": s2r.s2r_sketch_lambda(wl.d, wl.log2_w, int(nnz.max())),
+           "w_over_nnz": s2r.s2r_sketch_lambda(wl.d, wl.log2_w, int(nnz.max()), per_row=True),
+           "dw_over_merged": s2r.s2r_sketch_lambda(wl.d, wl.log2_w, U),
+           "w_over_merged": s2r.s2r_sketch_lambda(wl.d, wl.log2_w, U, per_row=True)}
     result = {
         "metric": "G gradient-elements/s (encode+reduce+decode) and % of peak HBM GB/s",
         "value": round(value, 3),
@@ -427,23 +584,24 @@ def main() -> int:
         "data": "synthetic",
         "config": {"workload": wl.name, "W": wl.W, "N": wl.N, "d": wl.d, "w": 1 << wl.log2_w,
                    "log2_part": p.log2_part, "log2_block": args.block, "hash": args.hash_family,
-                   "nnz_per_worker": int(nnz.max()),
-                   "set_bits_merged": U},
-        "roofline": {"bound": "hbm", "kernel": f"s2r_{dom}", "achieved": round(achieved, 1),
-                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": measured_traffic(wl.name, dom)},
+                   "nnz_per_worker": int(nnz.max()), "set_bits_merged": U,
+                   "lambda": {k: round(v, 4) for k, v in lam.items()}},
+        "roofline": roofline,
         "step_alg_GBs": round(step_alg, 1),
         "step_hbm_frac": round(step_alg / HBM_PEAK_GBS, 4),
         "step_ms_events": {"median": round(step_ev[len(step_ev) // 2], 4), "min": round(step_ev[0], 4)},
+        "traced_ms_per_step": round(traced_ms, 4) if traced_ms else None,
         "cold_cache_step_ms": ({"median": round(cold[len(cold) // 2], 4), "min": round(cold[0], 4),
                                 "reps": len(cold)} if cold else None),
         "measured_read_GBs": round(read_GBs, 1),
         "step_frac_of_measured_read": round(step_alg / read_GBs, 4),
         "phases": phases,
+        "kernels": kernels,
     }
     if not args.no_error:
-        log("estimation error vs the exact sum ...")
-        result["estimation_error"] = estimation_error(wl, sparse, out)
+        log("estimation error against the lossless comparator ...")
+        result["estimation_error"] = gpu_estimation_error(s2r, wl, cap, buf, out, stream)
+    del grad
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle) ...")
         result["cpu_baseline"] = cpu_baseline(wl, sparse, p.as_dict())

@@ -77,6 +77,10 @@ def lib() -> ctypes.CDLL:
         L.s2r_params_from_seed.restype = st
         L.s2r_default_log2_part.argtypes = [u32, u32]
         L.s2r_default_log2_part.restype = u32
+        L.s2r_sketch_lambda.argtypes = [u32, u32, u64, ctypes.c_int]
+        L.s2r_sketch_lambda.restype = ctypes.c_double
+        L.s2r_log2_w_for_lambda.argtypes = [u32, u64, ctypes.c_double, ctypes.c_int]
+        L.s2r_log2_w_for_lambda.restype = u32
         L.s2r_bitmap_words.argtypes = [u64]
         L.s2r_bitmap_words.restype = u64
         L.s2r_block_bitmap_words.argtypes = [u64, u32]
@@ -94,6 +98,10 @@ def lib() -> ctypes.CDLL:
         L.s2r_decode.restype = st
         L.s2r_hash.argtypes = [P(s2r_params), vp, u64, vp, vp, vp]
         L.s2r_hash.restype = st
+        L.s2r_gather_sum.argtypes = [u32, vp, vp, u64, vp, u64, vp, vp]
+        L.s2r_gather_sum.restype = st
+        L.s2r_diag_trace_attach.argtypes = [vp]
+        L.s2r_diag_trace_attach.restype = st
         L.s2r_topk_workspace_bytes.argtypes = [u32, u64, u64]
         L.s2r_topk_workspace_bytes.restype = sz
         L.s2r_topk_ef.argtypes = [u32, vp, vp, u64, u64, u64, u64, vp, vp, vp, sz, vp]
@@ -154,6 +162,17 @@ def s2r_default_log2_part(d: int, log2_w: int) -> int:
     return int(lib().s2r_default_log2_part(d, log2_w))
 
 
+def s2r_sketch_lambda(rows: int, log2_w: int, nnz: int, per_row: bool = False) -> float:
+    """Sketch size over the non-zero count: rows * 2^log2_w / nnz, or 2^log2_w / nnz with
+    per_row (see include/s2r.h)."""
+    return float(lib().s2r_sketch_lambda(rows, log2_w, nnz, 1 if per_row else 0))
+
+
+def s2r_log2_w_for_lambda(rows: int, nnz: int, lam: float, per_row: bool = False) -> int:
+    """Smallest log2_w reaching the ratio `lam`; 2^32 - 1 when none can."""
+    return int(lib().s2r_log2_w_for_lambda(rows, nnz, lam, 1 if per_row else 0))
+
+
 def s2r_bitmap_words(n: int) -> int:
     return int(lib().s2r_bitmap_words(n))
 
@@ -200,6 +219,12 @@ def s2r_hash(p: s2r_params, keys, m: int, buckets, signs, stream=None) -> None:
                           _stream(stream)), "s2r_hash")
 
 
+def s2r_gather_sum(W: int, idx, val, cap: int, nnz, n: int, out, stream=None) -> None:
+    """Exact sum of the workers' (index, value) lists into dense out[n] (worker order)."""
+    _check(lib().s2r_gather_sum(W, _ptr(idx), _ptr(val), cap, _ptr(nnz), n, _ptr(out),
+                                _stream(stream)), "s2r_gather_sum")
+
+
 def s2r_topk_workspace_bytes(W: int, n: int, block: int) -> int:
     return int(lib().s2r_topk_workspace_bytes(W, n, block))
 
@@ -213,6 +238,26 @@ def s2r_topk_ef(W: int, grad, residual, n: int, ld: int, block: int, K: int, out
     _check(lib().s2r_topk_ef(W, _ptr(grad), _ptr(residual), n, ld, block, K, _ptr(out),
                              _ptr(selected), _ptr(workspace), ws_bytes, _stream(stream)),
            "s2r_topk_ef")
+
+
+TRACE_MAX = 64
+
+
+class s2r_trace(ctypes.Structure):
+    """Mirror of ``s2r_trace`` in include/s2r_diag.h."""
+
+    _fields_ = [
+        ("capacity", ctypes.c_uint32),
+        ("count", ctypes.c_uint32),
+        ("events", ctypes.c_void_p * TRACE_MAX),
+        ("names", ctypes.c_char_p * TRACE_MAX),
+    ]
+
+
+def s2r_diag_trace_attach(trace) -> None:
+    """Attach an s2r_trace (or None to detach) to the calling thread (include/s2r_diag.h)."""
+    _check(lib().s2r_diag_trace_attach(None if trace is None else ctypes.addressof(trace)),
+           "s2r_diag_trace_attach")
 
 
 def s2r_diag_stream_read(buf, nbytes: int, sink, stream=None) -> None:
@@ -251,8 +296,10 @@ def alloc_encode_buffers(p: s2r_params, W: int, n: int, cap: int, device="cuda")
 
 __all__ = [
     "s2r_params", "S2RError", "s2r_params_from_seed", "s2r_default_log2_part", "s2r_bitmap_words",
+    "s2r_sketch_lambda", "s2r_log2_w_for_lambda",
     "s2r_block_bitmap_words",
     "s2r_encode_workspace_bytes", "s2r_encode", "s2r_reduce", "s2r_decode_workspace_bytes",
-    "s2r_decode", "s2r_hash", "s2r_topk_workspace_bytes", "s2r_topk_ef",
+    "s2r_decode", "s2r_hash", "s2r_gather_sum", "s2r_topk_workspace_bytes", "s2r_topk_ef",
+    "s2r_trace", "s2r_diag_trace_attach",
     "alloc_encode_buffers", "status_string", "lib",
 ]

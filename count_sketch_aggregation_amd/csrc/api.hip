@@ -4,6 +4,7 @@
 // nothing.
 #include <string.h>
 
+#include "s2r_diag.h"
 #include "s2r_launch.hpp"
 
 namespace s2r {
@@ -39,6 +40,19 @@ HashArgs make_hash_args(const s2r_params& p) {
     h.sB[j] = p.sB[j];
   }
   return h;
+}
+
+// The trace of the calling host thread, set only by s2r_diag_trace_attach.
+static thread_local s2r_trace* t_trace = nullptr;
+
+void trace_mark(hipStream_t s, const char* name) {
+  s2r_trace* t = t_trace;
+  if (t == nullptr || t->count >= t->capacity) return;
+  if (hipEventRecord(static_cast<hipEvent_t>(t->events[t->count]), s) != hipSuccess) {
+    (void)hipGetLastError();  // an unusable event is skipped; the launch is not affected
+    return;
+  }
+  t->names[t->count++] = name;
 }
 
 bool use_partitioned(const s2r_params& p) {
@@ -114,6 +128,21 @@ uint32_t s2r_default_log2_part(uint32_t d, uint32_t log2_w) {
   return K;
 }
 
+double s2r_sketch_lambda(uint32_t rows, uint32_t log2_w, uint64_t nnz, int per_row) {
+  if (nnz == 0 || rows < 1 || rows > S2R_MAX_ROWS || log2_w > 31) return 0.0;
+  const double cells = (double)(per_row ? 1u : rows) * (double)(1ull << log2_w);
+  return cells / (double)nnz;
+}
+
+uint32_t s2r_log2_w_for_lambda(uint32_t rows, uint64_t nnz, double lambda, int per_row) {
+  if (rows < 1 || rows > S2R_MAX_ROWS || !(lambda > 0.0) || !(lambda <= 1.7e308))
+    return UINT32_MAX;
+  if (nnz == 0) return 0;
+  for (uint32_t L = 0; L <= 31; ++L)
+    if (s2r_sketch_lambda(rows, L, nnz, per_row) >= lambda) return L;
+  return UINT32_MAX;
+}
+
 uint64_t s2r_bitmap_words(uint64_t n) { return (n + 63) / 64; }
 
 uint64_t s2r_block_bitmap_words(uint64_t n, uint32_t log2_block) {
@@ -181,6 +210,7 @@ s2r_status s2r_encode(const s2r_params* p, uint32_t W, const float* grad, uint64
   } else {
     S2R_TRY(launch_scatter(h, W, L.tiles, offsets, idx, val, cap, L.chunks, sketches, w, s));
   }
+  trace_mark(static_cast<hipStream_t>(stream), "end");
   return S2R_OK;
 }
 
@@ -196,6 +226,7 @@ s2r_status s2r_reduce(const s2r_params* p, uint32_t W, uint64_t n, const uint64_
   const uint64_t cells = (uint64_t)p->d << p->log2_w;
   S2R_TRY(launch_reduce(W, cells, s2r_block_bitmap_words(n, p->log2_block), bitmaps, sketches,
                         bitmap_out, sketch_out, static_cast<hipStream_t>(stream)));
+  trace_mark(static_cast<hipStream_t>(stream), "end");
   return S2R_OK;
 }
 
@@ -216,6 +247,7 @@ s2r_status s2r_decode(const s2r_params* p, uint64_t n, const uint64_t* bitmap,
     return S2R_ERR_WORKSPACE;
   S2R_TRY(launch_decode(make_hash_args(*p), *p, n, bitmap, sketch, out, max_set, workspace,
                         ws_bytes, static_cast<hipStream_t>(stream)));
+  trace_mark(static_cast<hipStream_t>(stream), "end");
   return S2R_OK;
 }
 
@@ -227,6 +259,19 @@ s2r_status s2r_hash(const s2r_params* p, const uint32_t* keys, uint64_t m, uint3
   if (!aligned(keys, 4) || !aligned(buckets, 4)) return S2R_ERR_ALIGN;
   S2R_TRY(launch_hash(make_hash_args(*p), keys, m, buckets, signs,
                       static_cast<hipStream_t>(stream)));
+  trace_mark(static_cast<hipStream_t>(stream), "end");
+  return S2R_OK;
+}
+
+s2r_status s2r_gather_sum(uint32_t W, const uint32_t* idx, const float* val, uint64_t cap,
+                          const uint64_t* nnz, uint64_t n, float* out, void* stream) {
+  if (n > 0 && !out) return S2R_ERR_NULL;
+  if (n > 0 && cap > 0 && (!idx || !val || !nnz)) return S2R_ERR_NULL;
+  if (W == 0 || W > 65535 || n >= (1ull << 32)) return S2R_ERR_DIM;
+  if (!aligned(out, 16) || !aligned(idx, 4) || !aligned(val, 4) || !aligned(nnz, 8))
+    return S2R_ERR_ALIGN;
+  S2R_TRY(launch_gather_sum(W, idx, val, cap, nnz, n, out, static_cast<hipStream_t>(stream)));
+  trace_mark(static_cast<hipStream_t>(stream), "end");
   return S2R_OK;
 }
 
@@ -247,6 +292,13 @@ s2r_status s2r_topk_ef(uint32_t W, const float* grad, float* residual, uint64_t 
   if (n > 0 && residual == grad) return S2R_ERR_DIM;
   S2R_TRY(launch_topk(W, grad, residual, n, ld, block, K, out, selected, workspace,
                       static_cast<hipStream_t>(stream)));
+  trace_mark(static_cast<hipStream_t>(stream), "end");
+  return S2R_OK;
+}
+
+s2r_status s2r_diag_trace_attach(s2r_trace* t) {
+  if (t && (t->capacity > S2R_TRACE_MAX || t->count > t->capacity)) return S2R_ERR_DIM;
+  t_trace = t;
   return S2R_OK;
 }
 

@@ -699,6 +699,7 @@ hipError_t launch_decode(const HashArgs& h, const s2r_params& p, uint64_t n,
     ws.chunks = L.chunks;
     ws.max_set = L.chunks * kChunk < max_set ? L.chunks * kChunk : max_set;
     if (ws.max_set > n) ws.max_set = n;
+    trace_mark(s, "k_dcount");
     hipLaunchKernelGGL(k_dcount, dim3((uint32_t)((L.tiles + kDcountTiles - 1) / kDcountTiles)),
                        dim3(kDcountThreads), 0, s, bitmap, n, nwords, L.tiles, h.lb,
                        tcount);
@@ -720,6 +721,7 @@ hipError_t launch_decode(const HashArgs& h, const s2r_params& p, uint64_t n,
                              : reinterpret_cast<const void*>(&k_dbin<kDBinThreads>);
       e = hipFuncSetAttribute(kfn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
       if (e != hipSuccess) return e;
+      trace_mark(s, "k_dbin");
       if (wide)
         hipLaunchKernelGGL(k_dbin<kDBinThreadsWide>, dim3((uint32_t)L.chunks),
                            dim3(kDBinThreadsWide), lds, s, h, n, bitmap, nwords, L.tiles, ws,
@@ -740,13 +742,16 @@ hipError_t launch_decode(const HashArgs& h, const s2r_params& p, uint64_t n,
       S2R_DISPATCH_D(p.d, {
         e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_dmedian<D>),
                                 hipFuncAttributeMaxDynamicSharedMemorySize, (int)tlds);
-        if (e == hipSuccess)
+        if (e == hipSuccess) {
+          trace_mark(s, "k_dmedian");
           hipLaunchKernelGGL((k_dmedian<D>), dim3((uint32_t)L.partitions, splits), dim3(kAccThreads), tlds,
                              s, h, L.tiles, sketch, w, ws, (uint32_t)L.partitions, vec4);
+        }
       });
       if (e != hipSuccess) return e;
       e = hipGetLastError();
       if (e != hipSuccess) return e;
+      trace_mark(s, "k_dunsort");
       hipLaunchKernelGGL(k_dunsort, dim3((uint32_t)L.chunks), dim3(kDUnsortThreads), 0, s, L.tiles,
                          ws);
       e = hipGetLastError();
@@ -755,10 +760,12 @@ hipError_t launch_decode(const HashArgs& h, const s2r_params& p, uint64_t n,
   }
   const uint64_t tiles = (n + kDecTile - 1) / kDecTile;
   if (part) {
+    trace_mark(s, "k_dwrite");
     S2R_DISPATCH_D(p.d, hipLaunchKernelGGL((k_dwrite<D>), dim3((uint32_t)tiles),
                                            dim3(kDecThreads), 0, s, h, n, nwords, bitmap, sketch,
                                            w, out, ws, tiles));
   } else {
+    trace_mark(s, "k_dwrite_direct");
     S2R_DISPATCH_D(p.d, hipLaunchKernelGGL((k_dwrite_direct<D>), dim3((uint32_t)tiles),
                                            dim3(kDecThreads), 0, s, h, n, nwords, bitmap, sketch,
                                            w, out));

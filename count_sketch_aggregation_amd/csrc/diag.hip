@@ -40,6 +40,7 @@ extern "C" s2r_status s2r_diag_stream_read(const void* buf, size_t bytes, float*
   uint64_t blocks = (n4 + s2r::kDiagThreads * s2r::kDiagLoads - 1) /
                     (s2r::kDiagThreads * s2r::kDiagLoads);
   if (blocks > 2048) blocks = 2048;  // 2048 x 256 lanes, grid-stride: the best measured shape
+  s2r::trace_mark(static_cast<hipStream_t>(stream), "k_diag_read");
   hipLaunchKernelGGL(s2r::k_diag_read, dim3((uint32_t)blocks), dim3(s2r::kDiagThreads), 0,
                      static_cast<hipStream_t>(stream), reinterpret_cast<const s2r::f32x4*>(buf),
                      n4, sink);

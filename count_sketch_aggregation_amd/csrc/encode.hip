@@ -114,9 +114,11 @@ __global__ __launch_bounds__(kStreamThreads) void k_stream(
 // it records the tile holding its first position.
 __device__ __forceinline__ uint32_t scan_pad(uint32_t i) { return i + (i >> 4); }
 
-// p[i] for i < n, else 0 (n > 0): an unconditional load of a clamped index, so that a
-// thread's loads issue back to back rather than as one guarded round trip each.
+// p[i] for i < n, else 0: an unconditional load of a clamped index, so that a thread's
+// loads issue back to back rather than as one guarded round trip each.  With n == 0 there
+// is no element to clamp to, so nothing is loaded (n is uniform across the grid).
 __device__ __forceinline__ uint32_t load_or_zero(const uint32_t* p, uint64_t i, uint64_t n) {
+  if (n == 0) return 0u;
   const uint32_t v = p[i < n ? i : n - 1];
   return i < n ? v : 0u;
 }
@@ -786,6 +788,7 @@ hipError_t launch_stream(uint32_t W, const float* grad, uint64_t n, uint64_t ld,
                          uint64_t* bitmaps, uint32_t* counts, hipStream_t s) {
   if (tiles == 0) return hipSuccess;
   const uint64_t words = (n + 63) / 64;
+  trace_mark(s, "k_stream");
   hipLaunchKernelGGL(k_stream, dim3((uint32_t)tiles, W), dim3(kStreamThreads), 0, s, grad, n, ld,
                      tiles, words, bitmaps, counts);
   return hipGetLastError();
@@ -800,10 +803,12 @@ hipError_t launch_scan(uint32_t W, uint64_t tiles, const uint32_t* counts, uint3
                        uint4* btot, uint2* spans, uint32_t* nspan, hipStream_t s) {
   const uint32_t nb = tiles > 0 ? scan_blocks(tiles) : 1;
   if (nb > 1) {
+    trace_mark(s, "k_scan_sum");
     hipLaunchKernelGGL(k_scan_sum, dim3(nb, W), dim3(kScanThreads), 0, s, tiles, counts, btot);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
+  trace_mark(s, "k_scan");
   hipLaunchKernelGGL(k_scan, dim3(nb, W), dim3(kScanThreads), 0, s, tiles, counts, offsets, nnz,
                      chunk_tile, chunks, cap, btot, spans, nspan);
   return hipGetLastError();
@@ -813,6 +818,7 @@ hipError_t launch_fill_zero(float* p, uint64_t count, hipStream_t s) {
   if (count == 0) return hipSuccess;
   uint64_t blocks = (count + 255) / 256;
   if (blocks > 8192) blocks = 8192;
+  trace_mark(s, "k_fill_zero");
   hipLaunchKernelGGL(k_fill_zero, dim3((uint32_t)blocks), dim3(256), 0, s, p, count);
   return hipGetLastError();
 }
@@ -820,6 +826,7 @@ hipError_t launch_fill_zero(float* p, uint64_t count, hipStream_t s) {
 hipError_t launch_blockbits(uint32_t W, const uint64_t* ebm, uint64_t ewords, uint64_t n,
                             uint32_t log2_block, uint64_t bwords, uint64_t* bbm, hipStream_t s) {
   if (bwords == 0) return hipSuccess;
+  trace_mark(s, "k_blockbits");
   hipLaunchKernelGGL(k_blockbits, dim3((uint32_t)((bwords + 3) / 4), W), dim3(256), 0, s, ebm, ewords,
                      n, log2_block, bwords, bbm);
   return hipGetLastError();
@@ -833,12 +840,14 @@ hipError_t launch_expand(uint32_t W, const float* grad, uint64_t ld, uint64_t ti
   const uint64_t nsp = (tiles + 1) / 2;
   uint64_t g = (kExpandGroups + W - 1) / W;
   if (g > nsp) g = nsp;
+  trace_mark(s, "k_expand_dense");
   hipLaunchKernelGGL(k_expand_dense, dim3((uint32_t)g, W), dim3(kExpandThreads), 0, s, grad, ld,
                      tiles, bitmaps, words, spans, nspan, idx, val, cap);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   uint64_t gs = (nsp + kExpandWaves - 1) / kExpandWaves;
   if (gs > g) gs = g;
+  trace_mark(s, "k_expand_sparse");
   hipLaunchKernelGGL(k_expand_sparse, dim3((uint32_t)gs, W), dim3(kExpandThreads), 0, s, grad, ld,
                      tiles, bitmaps, words, spans, nspan, idx, val, cap);
   return hipGetLastError();
@@ -848,6 +857,7 @@ hipError_t launch_scatter(const HashArgs& h, uint32_t W, uint64_t tiles, const u
                           const uint32_t* idx, const float* val, uint64_t cap, uint64_t chunks,
                           float* sketches, uint64_t w, hipStream_t s) {
   if (chunks == 0) return hipSuccess;
+  trace_mark(s, "k_scatter");
   S2R_DISPATCH_D(h.d, hipLaunchKernelGGL((k_scatter<D>), dim3((uint32_t)chunks, W),
                                          dim3(kScatterThreads), 0, s, h, tiles, offsets, idx, val,
                                          cap, sketches, w));
@@ -862,6 +872,7 @@ hipError_t launch_bin(const HashArgs& h, uint32_t W, uint64_t tiles, const uint3
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_bin),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
+  trace_mark(s, "k_bin");
   hipLaunchKernelGGL(k_bin, dim3((uint32_t)chunks, W), dim3(kBinThreads), lds, s, h, tiles,
                      offsets, idx, val, cap, chunks, (uint32_t)partitions, bins, prefix);
   return hipGetLastError();
@@ -880,10 +891,12 @@ hipError_t launch_accumulate(const HashArgs& h, uint32_t W, uint64_t tiles,
   S2R_DISPATCH_D(h.d, {
     e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_accumulate<D>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e == hipSuccess)
+    if (e == hipSuccess) {
+      trace_mark(s, "k_accumulate");
       hipLaunchKernelGGL((k_accumulate<D>), dim3((uint32_t)partitions, W), dim3(kAccThreads), lds,
                          s, h, tiles, offsets, cap, chunks, (uint32_t)partitions, bins, prefix,
                          sketches, w, vec4, nt);
+    }
   });
   if (e != hipSuccess) return e;
   return hipGetLastError();

@@ -27,6 +27,7 @@ hipError_t launch_hash(const HashArgs& h, const uint32_t* keys, uint64_t m, uint
   if (m == 0) return hipSuccess;
   uint64_t blocks = (m + 255) / 256;
   if (blocks > 8192) blocks = 8192;
+  trace_mark(s, "k_hash");
   S2R_DISPATCH_D(h.d, hipLaunchKernelGGL((k_hash<D>), dim3((uint32_t)blocks), dim3(256), 0, s, h,
                                          keys, m, buckets, signs));
   return hipGetLastError();

@@ -56,6 +56,7 @@ hipError_t launch_reduce(uint32_t W, uint64_t cells, uint64_t words, const uint6
   // cap of 16384, 7% faster than 4096)
   if (blocks > 65536) blocks = 65536;
   if (blocks == 0) return hipSuccess;
+  trace_mark(s, "k_reduce");
   if (vec)
     hipLaunchKernelGGL(k_reduce<true>, dim3((uint32_t)blocks), dim3(256), 0, s, W, cells, words,
                        bitmaps, sketches, bitmap_out, sketch_out);

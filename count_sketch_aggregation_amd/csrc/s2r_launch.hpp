@@ -51,6 +51,11 @@ bool use_partitioned(const s2r_params& p);
 
 HashArgs make_hash_args(const s2r_params& p);
 
+// Kernel trace (s2r_diag_trace_attach): with a trace attached to the calling host thread,
+// records its next event on `s` and names it `name`, the kernel about to be launched (or
+// "end" after a call's last launch); does nothing otherwise.
+void trace_mark(hipStream_t s, const char* name);
+
 hipError_t launch_stream(uint32_t W, const float* grad, uint64_t n, uint64_t ld,
                          uint64_t tiles, uint64_t* bitmaps, uint32_t* counts, hipStream_t s);
 // tiles are scanned in blocks of kScanPass; more than one block needs W * scan_blocks(tiles)
@@ -108,6 +113,9 @@ TopkLayout topk_layout(uint32_t W, uint64_t n, uint64_t block);
 hipError_t launch_topk(uint32_t W, const float* grad, float* residual, uint64_t n, uint64_t ld,
                        uint64_t block, uint64_t K, float* out, uint64_t* selected,
                        void* workspace, hipStream_t s);
+
+hipError_t launch_gather_sum(uint32_t W, const uint32_t* idx, const float* val, uint64_t cap,
+                             const uint64_t* nnz, uint64_t n, float* out, hipStream_t s);
 
 hipError_t launch_hash(const HashArgs& h, const uint32_t* keys, uint64_t m, uint32_t* buckets,
                        int8_t* signs, hipStream_t s);

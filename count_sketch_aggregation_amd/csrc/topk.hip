@@ -22,7 +22,6 @@
 //                kept blocks becomes 0 (the rest already holds g).
 // HBM traffic with error feedback: 12 B per element in the first pass (read gradient and
 // residual, write g) and 8 B in the last (read g, write out), plus 4 B per kept element.
-#include <atomic>
 
 #include "s2r_launch.hpp"
 
@@ -563,27 +562,16 @@ __global__ __launch_bounds__(kTkApplyThreads) void k_tk_apply(const float* __res
 // ---------------------------------------------------------------------------------------
 // host side
 
-// Dynamic LDS beyond the default per-launch limit is allowed once per device; where the
-// device refuses, the select kernel stages fewer candidates.
+// The select kernel stages up to kTkCandBig candidates in dynamic LDS; where the device
+// refuses that much, it stages fewer.  Asked on every call (the library caches nothing).
 static uint32_t select_cand_cap() {
-  constexpr int kMaxDevices = 64;
-  static std::atomic<uint32_t> cap[kMaxDevices];
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
-    (void)hipGetLastError();
-    return kTkCandSmall;
-  }
-  uint32_t c = cap[dev].load(std::memory_order_relaxed);
-  if (c != 0) return c;
-  c = kTkCandBig;
   if (hipFuncSetAttribute(reinterpret_cast<const void*>(&k_tk_select),
                           hipFuncAttributeMaxDynamicSharedMemorySize,
                           (int)(kTkCandBig * sizeof(uint64_t))) != hipSuccess) {
     (void)hipGetLastError();
-    c = kTkCandSmall;
+    return kTkCandSmall;
   }
-  cap[dev].store(c, std::memory_order_relaxed);
-  return c;
+  return kTkCandBig;
 }
 
 TopkLayout topk_layout(uint32_t W, uint64_t n, uint64_t block) {
@@ -620,6 +608,7 @@ hipError_t launch_topk(uint32_t W, const float* grad, float* residual, uint64_t 
   TkOutcome* outcome = reinterpret_cast<TkOutcome*>(ws + L.off_outcome);
   const int vec4 = (block % 4 == 0) && (ld % 4 == 0);
   const uint64_t ngroups = (L.nb + kTkNormThreads / kWave - 1) / (kTkNormThreads / kWave);
+  trace_mark(s, "k_tk_norm");
   hipLaunchKernelGGL(k_tk_norm, dim3((uint32_t)ngroups, W), dim3(kTkNormThreads), 0, s, grad,
                      residual, n, ld, block, L.nb, L.key_stride, keys, vec4, scratch,
                      L.scratch_words);
@@ -629,17 +618,20 @@ hipError_t launch_topk(uint32_t W, const float* grad, float* residual, uint64_t 
   if (K > 0 && K < L.nb) {  // else the select has nothing to histogram
     const uint32_t slices = (uint32_t)((L.nb + kTkSliceKeys - 1) / kTkSliceKeys);
     for (int p = 0; p < kTkGlobalPasses; ++p) {
+      trace_mark(s, "k_tk_hist");
       hipLaunchKernelGGL(k_tk_hist, dim3(slices, W), dim3(kTkHistThreads), 0, s, keys, L.nb,
                          L.key_stride, K, p, scratch, L.scratch_words, gcand, cap);
       e = hipGetLastError();
       if (e != hipSuccess) return e;
     }
   }
+  trace_mark(s, "k_tk_select");
   hipLaunchKernelGGL(k_tk_select, dim3(W), dim3(kTkSelThreads), cap * sizeof(uint64_t), s, keys,
                      L.nb, L.key_stride, K, sel, L.sel_words, cap, scratch, L.scratch_words,
                      gcand, outcome);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
+  trace_mark(s, "k_tk_bitmap");
   hipLaunchKernelGGL(k_tk_bitmap, dim3((uint32_t)((L.sel_words + 3) / 4), W), dim3(256), 0, s,
                      keys, L.nb, L.key_stride, outcome, sel, L.sel_words);
   e = hipGetLastError();
@@ -647,6 +639,7 @@ hipError_t launch_topk(uint32_t W, const float* grad, float* residual, uint64_t 
   const uint64_t per = 4ull * kTkApplyThreads * kTkApplyIters;
   // blocks beyond n hold the whole row: dividing by n gives the same block ids (all 0)
   const DivU32 dv = make_div_u32((uint32_t)(block < n ? block : n));
+  trace_mark(s, "k_tk_apply");
   hipLaunchKernelGGL(k_tk_apply, dim3((uint32_t)((n + per - 1) / per), W), dim3(kTkApplyThreads), 0,
                      s, grad, residual, n, ld, dv, sel, L.sel_words, out);
   return hipGetLastError();

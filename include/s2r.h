@@ -15,6 +15,8 @@
  *                  Algorithm 1: for every set bit i, g_hat(i) = median over rows j of
  *                  s_j(i) * S[j, h_j(i)]; every clear bit decodes to +0.0.
  *   s2r_hash    -- the bucket and sign hashes of Algorithm 1 on arbitrary keys (test hook).
+ *   s2r_gather_sum -- the lossless comparator of Section 1 and Section 2.2 (Fig. 1(b)):
+ *                  the exact sum of the workers' (index, value) lists.
  *   s2r_topk_ef -- Section 2.2 and Appendix A.2: block-wise Top-K sparsification with error
  *                  feedback, which produces the sparse gradients that s2r_encode compresses.
  *
@@ -97,6 +99,26 @@ s2r_status s2r_params_from_seed(uint64_t seed, uint32_t d, uint32_t log2_w, uint
  * budget of the partitioned path; pure host code. */
 uint32_t s2r_default_log2_part(uint32_t d, uint32_t log2_w);
 
+/* Sketch-size ratio lambda (Section 3.1 "Decompressing Sparse Gradient": the sketch
+ * compresses when lambda = m / (alpha d) < 1, alpha d being the number of non-zeros of a
+ * d-element gradient; Appendix B.3 calls lambda the ratio of the sketch's size to the
+ * number of non-zeros and finds 0.5 best for its models).  The pages size a single-row
+ * sketch of m buckets in Section 3.1 but a rows x columns table in Algorithm 1, so both
+ * readings are offered:
+ *   per_row == 0:  lambda = rows * 2^log2_w / nnz   (every cell of the table)
+ *   per_row != 0:  lambda = 2^log2_w / nnz          (one row, the pages' m)
+ * nnz is whichever non-zero count the caller sizes for (one worker's, or the merged
+ * union).  Returns 0.0 when nnz == 0 or rows is outside 1..S2R_MAX_ROWS or log2_w > 31.
+ * Pure host code. */
+double s2r_sketch_lambda(uint32_t rows, uint32_t log2_w, uint64_t nnz, int per_row);
+
+/* The smallest log2_w in 0..31 whose sketch reaches the target ratio under the same
+ * reading, s2r_sketch_lambda(rows, log2_w, nnz, per_row) >= lambda (widths are powers of
+ * two, so the ratio reached lies in [lambda, 2 lambda) unless log2_w = 0 already exceeds
+ * it).  Returns 0 for nnz == 0, and UINT32_MAX when rows is outside 1..S2R_MAX_ROWS, lambda
+ * is not a positive finite number, or no log2_w <= 31 reaches it.  Pure host code. */
+uint32_t s2r_log2_w_for_lambda(uint32_t rows, uint64_t nnz, double lambda, int per_row);
+
 /* ceil(n / 64): uint64 words of an element-granular bitmap. */
 uint64_t s2r_bitmap_words(uint64_t n);
 
@@ -169,6 +191,24 @@ size_t s2r_decode_workspace_bytes(const s2r_params* p, uint64_t n, uint64_t max_
 s2r_status s2r_decode(const s2r_params* p, uint64_t n, const uint64_t* bitmap,
                       const float* sketch, float* out, uint64_t max_set, void* workspace,
                       size_t ws_bytes, void* stream);
+
+/* Lossless comparator: the exact sum of the workers' sparse gradients, formed from their
+ * compacted lists -- the aggregate the sketch path estimates.  Section 1 and Section 2.2
+ * (Fig. 1(b)) describe it: without a mergeable structure, workers gather one another's
+ * indices and values and add them afterwards.  On one GPU the W lists are already resident
+ * (s2r_encode writes them), so this is the add.  For i < n:
+ *   out[i] = the fp32 sum, in worker order k = 0, 1, ..., W-1 starting from +0.0, of
+ *            val[k][t] over the entries t < min(nnz[k], cap) with idx[k][t] == i;
+ *   out[i] = +0.0 where no worker lists i.
+ * idx [W][cap] uint32, val [W][cap] fp32 and nnz [W] uint64 are device memory, read-only,
+ * in the layout s2r_encode writes; the indices of one worker must be distinct (s2r_encode's
+ * are strictly ascending; repeated indices give an unspecified sum at those elements).
+ * Entries with idx >= n are skipped.  out [n] fp32, 16-byte aligned, may not overlap the
+ * inputs.  Deterministic: the same inputs give the same bits on every run.
+ * Errors: S2R_ERR_NULL, S2R_ERR_DIM (W == 0 or W > 65535, n >= 2^32), S2R_ERR_ALIGN
+ * (out not 16-byte aligned, idx / val not 4-byte or nnz not 8-byte aligned), S2R_ERR_HIP. */
+s2r_status s2r_gather_sum(uint32_t W, const uint32_t* idx, const float* val, uint64_t cap,
+                          const uint64_t* nnz, uint64_t n, float* out, void* stream);
 
 /* Test hook: the same device hash the other calls use, on arbitrary keys.
  *   buckets[j * m + t] = h_j(keys[t]),  signs[j * m + t] = s_j(keys[t])  (int8, +1/-1)

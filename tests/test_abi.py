@@ -70,6 +70,33 @@ def test_small_helpers(s2r):
     assert s2r.status_string(s2r.S2R_ERR_WORKSPACE) == "workspace too small"
 
 
+def test_sketch_lambda(s2r):
+    """lambda = sketch size / non-zeros, both readings (whole table, one row)."""
+    assert s2r.s2r_sketch_lambda(5, 20, 2_097_152) == 5 * 2**20 / 2_097_152
+    assert s2r.s2r_sketch_lambda(5, 20, 2_097_152, per_row=True) == 0.5
+    assert s2r.s2r_sketch_lambda(3, 0, 3) == 1.0
+    for bad in [(0, 10, 5), (17, 10, 5), (3, 32, 5), (3, 10, 0)]:
+        assert s2r.s2r_sketch_lambda(*bad) == 0.0
+    # the smallest width reaching the target, checked against every width by brute force
+    for rows, nnz, lam, per_row in [(5, 2_097_152, 0.5, True), (5, 2_097_152, 0.5, False),
+                                    (3, 255_744, 1.0, False), (1, 1, 1.0, True),
+                                    (3, 1000, 0.05, False), (16, 7, 3.0, True),
+                                    (2, 10**9, 0.5, True)]:
+        L = s2r.s2r_log2_w_for_lambda(rows, nnz, lam, per_row)
+        cells = lambda k: (1 if per_row else rows) * 2**k
+        ok = [k for k in range(32) if cells(k) / nnz >= lam]
+        assert L == ok[0]
+        got = s2r.s2r_sketch_lambda(rows, L, nnz, per_row)
+        assert got >= lam and (L == 0 or got < 2 * lam)
+    assert s2r.s2r_log2_w_for_lambda(5, 2_097_152, 0.5, True) == 20  # the embedding workload
+    assert s2r.s2r_log2_w_for_lambda(3, 0, 0.5, False) == 0
+    none = 2**32 - 1
+    assert s2r.s2r_log2_w_for_lambda(1, 2**63, 1.0, True) == none  # needs more than 2^31
+    for bad in [(0, 10, 0.5), (17, 10, 0.5), (3, 10, 0.0), (3, 10, -1.0), (3, 10, float("nan")),
+                (3, 10, float("inf"))]:
+        assert s2r.s2r_log2_w_for_lambda(*bad) == none
+
+
 FAKE = 1 << 20  # a 256-byte aligned non-null address; never dereferenced on these paths
 
 

@@ -83,6 +83,22 @@ def test_encode(case):
     gp.assert_encode_matches(op, grads, n, res)
 
 
+@pytest.mark.parametrize("K", [None, 14])
+def test_encode_reduce_decode_empty_gradient(K):
+    """n == 0 (regression: the list scan once read the word before its tile counts when a
+    worker had no tiles): nnz = 0, all-zero sketches, and reduce and decode are no-ops."""
+    gp.say(f"encode n=0 K={K}")
+    W, d, L = 3, 3, 14  # K = 14: a 192 KiB table, the global-atomic path
+    p, op = gp.params_pair(606, d, L, K)
+    res = gp.run_encode(p, np.zeros((W, 4), np.float32), 0)
+    assert np.array_equal(res["nnz"], np.zeros(W, np.int64))
+    assert np.array_equal(res["sketches"], np.zeros((W, d, 1 << L), np.float32))
+    gp.assert_encode_matches(op, np.zeros((W, 4), np.float32), 0, res)
+    bm, S = gp.run_reduce(p, 0, res["bitmaps"], res["sketches"])
+    assert bm.size == 0 and np.array_equal(S, np.zeros((d, 1 << L), np.float32))
+    assert gp.run_decode(p, 0, bm, S).size == 0
+
+
 @pytest.mark.parametrize("K", [None, 15])
 def test_encode_integer_values_exact(K):
     """Integer values: every fp32 partial sum is exact, so the sketch must be bit-exact."""
