@@ -19,7 +19,9 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libs2r.so")
 MAX_ROWS = 16
 
-S2R_OK, S2R_ERR_NULL, S2R_ERR_DIM, S2R_ERR_ALIGN, S2R_ERR_WORKSPACE, S2R_ERR_HIP = range(6)
+(S2R_OK, S2R_ERR_NULL, S2R_ERR_DIM, S2R_ERR_ALIGN, S2R_ERR_WORKSPACE, S2R_ERR_HIP,
+ S2R_ERR_SCRATCH) = range(7)
+NOALLOC_SCRATCH_BYTES = 256 << 20
 
 
 class S2RError(RuntimeError):
@@ -90,6 +92,9 @@ def lib() -> ctypes.CDLL:
         L.s2r_encode.argtypes = [P(s2r_params), u32, vp, u64, u64, vp, vp, vp, vp, u64, vp, vp, sz,
                                  vp]
         L.s2r_encode.restype = st
+        L.s2r_encode_noalloc.argtypes = [P(s2r_params), u32, vp, u64, u64, vp, vp, vp, vp, u64,
+                                         vp, vp]
+        L.s2r_encode_noalloc.restype = st
         L.s2r_reduce.argtypes = [P(s2r_params), u32, u64, vp, vp, vp, vp, vp]
         L.s2r_reduce.restype = st
         L.s2r_decode_workspace_bytes.argtypes = [P(s2r_params), u64, u64]
@@ -192,6 +197,14 @@ def s2r_encode(p: s2r_params, W: int, grad, n: int, ld: int, bitmaps, sketches, 
     _check(lib().s2r_encode(ctypes.byref(p), W, _ptr(grad), n, ld, _ptr(bitmaps), _ptr(sketches),
                             _ptr(idx), _ptr(val), cap, _ptr(nnz), _ptr(workspace), ws_bytes,
                             _stream(stream)), "s2r_encode")
+
+
+def s2r_encode_noalloc(p: s2r_params, W: int, grad, n: int, ld: int, bitmaps, sketches, idx, val,
+                       cap: int, nnz, stream=None) -> None:
+    """s2r_encode with the library's static scratch as its workspace (allocates nothing)."""
+    _check(lib().s2r_encode_noalloc(ctypes.byref(p), W, _ptr(grad), n, ld, _ptr(bitmaps),
+                                    _ptr(sketches), _ptr(idx), _ptr(val), cap, _ptr(nnz),
+                                    _stream(stream)), "s2r_encode_noalloc")
 
 
 def s2r_reduce(p: s2r_params, W: int, n: int, bitmaps, sketches, bitmap_out, sketch_out,
@@ -298,7 +311,7 @@ __all__ = [
     "s2r_params", "S2RError", "s2r_params_from_seed", "s2r_default_log2_part", "s2r_bitmap_words",
     "s2r_sketch_lambda", "s2r_log2_w_for_lambda",
     "s2r_block_bitmap_words",
-    "s2r_encode_workspace_bytes", "s2r_encode", "s2r_reduce", "s2r_decode_workspace_bytes",
+    "s2r_encode_workspace_bytes", "s2r_encode", "s2r_encode_noalloc", "s2r_reduce", "s2r_decode_workspace_bytes",
     "s2r_decode", "s2r_hash", "s2r_gather_sum", "s2r_topk_workspace_bytes", "s2r_topk_ef",
     "s2r_trace", "s2r_diag_trace_attach",
     "alloc_encode_buffers", "status_string", "lib",

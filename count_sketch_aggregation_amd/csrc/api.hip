@@ -4,6 +4,8 @@
 // nothing.
 #include <string.h>
 
+#include <mutex>
+
 #include "s2r_diag.h"
 #include "s2r_launch.hpp"
 
@@ -165,22 +167,65 @@ static inline bool aligned(const void* ptr, size_t a) {
     if ((expr) != hipSuccess) return S2R_ERR_HIP; \
   } while (0)
 
-s2r_status s2r_encode(const s2r_params* p, uint32_t W, const float* grad, uint64_t n,
-                      uint64_t ld, uint64_t* bitmaps, float* sketches, uint32_t* idx,
-                      float* val, uint64_t cap, uint64_t* nnz, void* workspace,
-                      size_t ws_bytes, void* stream) {
-  if (!p || (!bitmaps && n > 0) || !sketches || !nnz || !workspace) return S2R_ERR_NULL;
+// Workspace of s2r_encode_noalloc: a file-scope device array, one copy per GPU, which the
+// GPU holds until the process ends.  In host code `scratch` names a host-side stand-in, so
+// it is never passed to a kernel or copy: its device address is taken once per device with
+// hipGetSymbolAddress (with that device current) and kept here.
+static __device__ __align__(256) unsigned char scratch[S2R_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+static std::mutex g_scratch_mu;
+static void* g_scratch_ptr[kMaxDevices];
+
+// The device address of `scratch` on the device `s` runs on, which must be the current
+// device; nullptr when the device cannot be determined or the lookup fails.
+static void* scratch_address(hipStream_t s) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    (void)hipGetLastError();
+    return nullptr;
+  }
+  if (s != nullptr) {
+    int sdev = -1;
+    if (hipStreamGetDevice(s, &sdev) != hipSuccess || sdev != dev) {
+      (void)hipGetLastError();
+      return nullptr;
+    }
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr) {
+      (void)hipGetLastError();
+      return nullptr;
+    }
+    g_scratch_ptr[dev] = ptr;
+  }
+  return g_scratch_ptr[dev];
+}
+
+// Argument checks of s2r_encode and s2r_encode_noalloc, workspace aside (a caller-given
+// workspace is checked for NULL and alignment with the other pointers).
+static s2r_status encode_check(const s2r_params* p, uint32_t W, const float* grad, uint64_t n,
+                               uint64_t ld, const uint64_t* bitmaps, const float* sketches,
+                               const uint32_t* idx, const float* val, uint64_t cap,
+                               const uint64_t* nnz, bool ws_arg, const void* workspace) {
+  if (!p || (!bitmaps && n > 0) || !sketches || !nnz || (ws_arg && !workspace)) return S2R_ERR_NULL;
   if (n > 0 && !grad) return S2R_ERR_NULL;
   if (cap > 0 && (!idx || !val)) return S2R_ERR_NULL;
   if (!params_ok(p) || W == 0 || W > 65535 || n >= (1ull << 32) || ld < n) return S2R_ERR_DIM;
   if (ld % 4 != 0 || !aligned(grad, 16) || !aligned(bitmaps, 8) || !aligned(sketches, 4) ||
-      !aligned(nnz, 8) || !aligned(workspace, 16) || (cap > 0 && (!aligned(idx, 4) || !aligned(val, 4))))
+      !aligned(nnz, 8) || (ws_arg && !aligned(workspace, 16)) ||
+      (cap > 0 && (!aligned(idx, 4) || !aligned(val, 4))))
     return S2R_ERR_ALIGN;
-  const EncodeLayout L = encode_layout(*p, W, n, cap);
-  if (ws_bytes < L.total) return S2R_ERR_WORKSPACE;
+  return S2R_OK;
+}
 
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  char* ws = static_cast<char*>(workspace);
+// The encode kernels, in launch order, with workspace `ws` laid out as L.
+static s2r_status encode_launch(const s2r_params* p, uint32_t W, const float* grad, uint64_t n,
+                                uint64_t ld, uint64_t* bitmaps, float* sketches, uint32_t* idx,
+                                float* val, uint64_t cap, uint64_t* nnz, const EncodeLayout& L,
+                                char* ws, hipStream_t s) {
   uint32_t* counts = reinterpret_cast<uint32_t*>(ws + L.off_counts);
   uint32_t* offsets = reinterpret_cast<uint32_t*>(ws + L.off_offsets);
   const uint64_t w = 1ull << p->log2_w;
@@ -210,8 +255,35 @@ s2r_status s2r_encode(const s2r_params* p, uint32_t W, const float* grad, uint64
   } else {
     S2R_TRY(launch_scatter(h, W, L.tiles, offsets, idx, val, cap, L.chunks, sketches, w, s));
   }
-  trace_mark(static_cast<hipStream_t>(stream), "end");
+  trace_mark(s, "end");
   return S2R_OK;
+}
+
+s2r_status s2r_encode(const s2r_params* p, uint32_t W, const float* grad, uint64_t n,
+                      uint64_t ld, uint64_t* bitmaps, float* sketches, uint32_t* idx,
+                      float* val, uint64_t cap, uint64_t* nnz, void* workspace,
+                      size_t ws_bytes, void* stream) {
+  const s2r_status st =
+      encode_check(p, W, grad, n, ld, bitmaps, sketches, idx, val, cap, nnz, true, workspace);
+  if (st != S2R_OK) return st;
+  const EncodeLayout L = encode_layout(*p, W, n, cap);
+  if (ws_bytes < L.total) return S2R_ERR_WORKSPACE;
+  return encode_launch(p, W, grad, n, ld, bitmaps, sketches, idx, val, cap, nnz, L,
+                       static_cast<char*>(workspace), static_cast<hipStream_t>(stream));
+}
+
+s2r_status s2r_encode_noalloc(const s2r_params* p, uint32_t W, const float* grad, uint64_t n,
+                              uint64_t ld, uint64_t* bitmaps, float* sketches, uint32_t* idx,
+                              float* val, uint64_t cap, uint64_t* nnz, void* stream) {
+  const s2r_status st =
+      encode_check(p, W, grad, n, ld, bitmaps, sketches, idx, val, cap, nnz, false, nullptr);
+  if (st != S2R_OK) return st;
+  const EncodeLayout L = encode_layout(*p, W, n, cap);
+  if (L.total > (size_t)S2R_NOALLOC_SCRATCH_BYTES) return S2R_ERR_SCRATCH;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(scratch_address(s));
+  if (ws == nullptr) return S2R_ERR_HIP;
+  return encode_launch(p, W, grad, n, ld, bitmaps, sketches, idx, val, cap, nnz, L, ws, s);
 }
 
 s2r_status s2r_reduce(const s2r_params* p, uint32_t W, uint64_t n, const uint64_t* bitmaps,
@@ -310,6 +382,7 @@ const char* s2r_status_string(s2r_status s) {
     case S2R_ERR_ALIGN: return "misaligned pointer or leading dimension";
     case S2R_ERR_WORKSPACE: return "workspace too small";
     case S2R_ERR_HIP: return "HIP launch failed";
+    case S2R_ERR_SCRATCH: return "workspace need exceeds the static scratch of the allocation-free call";
   }
   return "unknown status";
 }

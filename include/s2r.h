@@ -22,8 +22,11 @@
  *
  * Conventions shared by every call:
  *   - Device arrays are caller-owned device memory (hipMalloc / torch tensors).  The
- *     library never allocates, frees or synchronises; it keeps no global state, so calls
- *     from several host threads are safe as long as their buffers differ.
+ *     library never allocates, frees or synchronises.  Its only state is the static scratch
+ *     of s2r_encode_noalloc (one array per GPU, with its device address looked up once per
+ *     GPU under a lock) and the per-thread trace pointer of s2r_diag.h; calls from several
+ *     host threads are safe as long as their buffers differ (for s2r_encode_noalloc see
+ *     there).
  *   - Work is only enqueued on `stream` (a hipStream_t; NULL = the default stream).  Every
  *     argument check happens on the host before anything is enqueued, so a call that
  *     returns an error has enqueued nothing.  S2R_ERR_HIP means a launch failed.
@@ -55,7 +58,9 @@ typedef enum {
   S2R_ERR_DIM = 2,       /* a size or parameter is out of range                        */
   S2R_ERR_ALIGN = 3,     /* a pointer or leading dimension breaks an alignment rule     */
   S2R_ERR_WORKSPACE = 4, /* the workspace is smaller than the *_workspace_bytes query    */
-  S2R_ERR_HIP = 5        /* a HIP launch failed                                        */
+  S2R_ERR_HIP = 5,       /* a HIP launch failed                                        */
+  S2R_ERR_SCRATCH = 6    /* s2r_encode_noalloc: the call needs more workspace than the
+                            static scratch holds (S2R_NOALLOC_SCRATCH_BYTES)             */
 } s2r_status;
 
 /* Hash constants shared by every worker and by encode and decode (Algorithm 1 draws its
@@ -152,6 +157,28 @@ s2r_status s2r_encode(const s2r_params* p, uint32_t W, const float* grad, uint64
                       uint64_t ld, uint64_t* bitmaps, float* sketches, uint32_t* idx,
                       float* val, uint64_t cap, uint64_t* nnz, void* workspace,
                       size_t ws_bytes, void* stream);
+
+/* Bytes of the static scratch that s2r_encode_noalloc uses as its workspace. */
+#define S2R_NOALLOC_SCRATCH_BYTES ((size_t)256 << 20)
+
+/* s2r_encode without a workspace argument, for callers that cannot allocate device memory:
+ * code under HIP graph capture, serving loops that forbid allocation, harnesses that
+ * disallow hipMalloc.  Same arguments, kernels, results and errors as s2r_encode, except:
+ *   - the workspace is a static device array of S2R_NOALLOC_SCRATCH_BYTES inside the
+ *     library, one per GPU, held from the library's first use on that GPU until the process
+ *     ends; nothing is allocated or freed by the call (no hipMalloc, no hipFree);
+ *   - a call whose s2r_encode_workspace_bytes(p, W, n, cap) exceeds that size returns
+ *     S2R_ERR_SCRATCH and enqueues nothing (at the five built-in workloads' sizes, the
+ *     1e9-element, ResNet-50, embedding and tiny ones fit; the 160M-element one does not);
+ *   - `stream` must belong to the current device (else S2R_ERR_HIP, nothing enqueued); the
+ *     first call on a device looks up that device's scratch address;
+ *   - every call on one GPU shares that GPU's scratch, which keeps the last call's
+ *     contents (the kernels need nothing cleared): calls whose work overlaps on one GPU
+ *     (other streams, other host threads) race on it and give unspecified results, so they
+ *     must be ordered, e.g. on one stream. */
+s2r_status s2r_encode_noalloc(const s2r_params* p, uint32_t W, const float* grad, uint64_t n,
+                              uint64_t ld, uint64_t* bitmaps, float* sketches, uint32_t* idx,
+                              float* val, uint64_t cap, uint64_t* nnz, void* stream);
 
 /* Aggregation (Section 3.1; the AllReduce of Algorithm 1) of W workers on one GPU:
  *   sketch_out[c] = sum_{k=0..W-1} sketches[k][c]   (fp32, added in order k = 0, 1, ...)

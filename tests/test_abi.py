@@ -97,6 +97,27 @@ def test_sketch_lambda(s2r):
         assert s2r.s2r_log2_w_for_lambda(*bad) == none
 
 
+def test_encode_noalloc_host_checks(s2r):
+    """The allocation-free encode refuses, before touching any device, a request larger
+    than its static scratch, and checks its arguments like s2r_encode."""
+    p = s2r.s2r_params_from_seed(1, 5, 22, 11)
+    L = s2r.lib()
+    W, n, cap = 8, 160_000_000, 8_000_512
+    assert s2r.s2r_encode_workspace_bytes(p, W, n, cap) > s2r.NOALLOC_SCRATCH_BYTES
+    args = [ctypes.byref(p), W, FAKE, n, n, FAKE, FAKE, FAKE, FAKE, cap, FAKE, 0]
+    assert L.s2r_encode_noalloc(*args) == s2r.S2R_ERR_SCRATCH
+    bad = list(args)
+    bad[5] = None
+    assert L.s2r_encode_noalloc(*bad) == s2r.S2R_ERR_NULL
+    bad = list(args)
+    bad[1] = 0
+    assert L.s2r_encode_noalloc(*bad) == s2r.S2R_ERR_DIM
+    bad = list(args)
+    bad[2] = FAKE + 4
+    assert L.s2r_encode_noalloc(*bad) == s2r.S2R_ERR_ALIGN
+    assert "static scratch" in s2r.status_string(s2r.S2R_ERR_SCRATCH)
+
+
 FAKE = 1 << 20  # a 256-byte aligned non-null address; never dereferenced on these paths
 
 
