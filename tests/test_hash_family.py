@@ -66,3 +66,25 @@ def test_partitioned_pair_collision_rates():
         cond = c1[c0].mean()
         assert abs(cond - cond_rate) < 6 * np.sqrt(cond_rate / max(c0.sum(), 1)) + 1e-3, \
             (fam_K, cond, cond_rate)
+
+
+def test_partitioned_rows_at_the_workloads_partition_geometry():
+    """The benchmark's partition shape: d = 5 rows, 2^11 buckets per partition and row (the
+    default K for d = 5), about 10 items per bucket as in the embedding and Transformer
+    workloads (U / w = 10.1 and 10.4).  Here w = 2^13 (4 partitions) and U = 81,920 items in
+    runs of 64, so every partition holds about 20K items as the embedding workload's do; the
+    median's error matches that of independent rows within Monte-Carlo noise."""
+    n, d, L, K = 1 << 20, 5, 13, 11
+    g_sparse = WL.blocks_sparse(n, 64, 0.078125, seed=21, std=1.0)
+    assert abs(g_sparse[0].size / (1 << L) - 10.0) < 0.1
+    seeds = range(300, 324)
+    e_ind = _errors(L, seeds, g_sparse, n, d, L)
+    e_part = _errors(K, seeds, g_sparse, n, d, L)
+    m_ind, m_part = np.abs(e_ind).mean(), np.abs(e_part).mean()
+    assert 0.95 < m_part / m_ind < 1.05, (m_ind, m_part)
+    r_ind = np.sqrt((e_ind ** 2).mean())
+    r_part = np.sqrt((e_part ** 2).mean())
+    assert 0.95 < r_part / r_ind < 1.05, (r_ind, r_part)
+    for q in (0.5, 0.9, 0.99):
+        a, b = np.quantile(np.abs(e_ind), q), np.quantile(np.abs(e_part), q)
+        assert 0.9 < b / a < 1.1, (q, a, b)
