@@ -22,7 +22,8 @@ average launch time and its algorithmic bytes per launch, and `roofline` is the 
 kernel's algorithmic bytes per launch over its average launch time against the 8 TB/s
 peak.  The line also carries the median and minimum per-step event times, cold-cache steps
 (each timed alone after an untimed 512 MiB write that evicts L2 and the Infinity Cache), a
-plain streaming read of 2 GiB on the same GPU (the achievable read ceiling), the sketch
+plain streaming read and a plain streaming write of 2 GiB on the same GPU (the achievable
+read and write rates), the sketch
 ratio lambda both ways, the estimation error of the decoded aggregate against the exact sum
 formed on the GPU by the lossless comparator (s2r_gather_sum, which is timed too), and the
 CPU oracle's rate on a bounded sample of the same workload with the host's identity.
@@ -537,9 +538,9 @@ def main() -> int:
                     "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None}
 
-    # --- cold-cache repetitions and the measured read ceiling ----------------------------
+    # --- cold-cache repetitions and the measured read and write ceilings -----------------
     # Before each cold step an untimed 512 MiB write evicts L2 and the Infinity Cache; each
-    # step is timed alone with events.  Then a plain streaming read of 2 GiB.
+    # step is timed alone with events.  Then a plain streaming read and write of 2 GiB.
     flush = torch.empty(512 << 18, dtype=torch.float32, device=dev)
     cold = []
     for _ in range(args.cold_reps):
@@ -561,6 +562,13 @@ def main() -> int:
     r1.record(stream)
     torch.cuda.synchronize()
     read_GBs = 5 * nbytes / (r0.elapsed_time(r1) * 1e-3) / 1e9
+    s2r.s2r_diag_stream_write(big, nbytes, 0.0, stream=stream)
+    r0.record(stream)
+    for _ in range(5):
+        s2r.s2r_diag_stream_write(big, nbytes, 0.0, stream=stream)
+    r1.record(stream)
+    torch.cuda.synchronize()
+    write_GBs = 5 * nbytes / (r0.elapsed_time(r1) * 1e-3) / 1e9
     del big
     log(f"ms/step {ms_per_step:.3f}  phases {phases}  step alg GB/s {step_alg:.0f}  "
         f"roofline {roofline['kernel']} {roofline['achieved']} GB/s")
@@ -594,6 +602,7 @@ def main() -> int:
         "cold_cache_step_ms": ({"median": round(cold[len(cold) // 2], 4), "min": round(cold[0], 4),
                                 "reps": len(cold)} if cold else None),
         "measured_read_GBs": round(read_GBs, 1),
+        "measured_write_GBs": round(write_GBs, 1),
         "step_frac_of_measured_read": round(step_alg / read_GBs, 4),
         "phases": phases,
         "kernels": kernels,

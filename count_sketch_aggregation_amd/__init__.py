@@ -111,6 +111,8 @@ def lib() -> ctypes.CDLL:
         L.s2r_topk_workspace_bytes.restype = sz
         L.s2r_topk_ef.argtypes = [u32, vp, vp, u64, u64, u64, u64, vp, vp, vp, sz, vp]
         L.s2r_topk_ef.restype = st
+        L.s2r_diag_stream_write.argtypes = [vp, sz, ctypes.c_float, vp]
+        L.s2r_diag_stream_write.restype = st
         L.s2r_diag_stream_read.argtypes = [vp, sz, vp, vp]
         L.s2r_diag_stream_read.restype = st
         L.s2r_status_string.argtypes = [st]
@@ -271,6 +273,12 @@ def s2r_diag_trace_attach(trace) -> None:
     """Attach an s2r_trace (or None to detach) to the calling thread (include/s2r_diag.h)."""
     _check(lib().s2r_diag_trace_attach(None if trace is None else ctypes.addressof(trace)),
            "s2r_diag_trace_attach")
+
+
+def s2r_diag_stream_write(buf, nbytes: int, value: float = 0.0, stream=None) -> None:
+    """Measurement helper (include/s2r_diag.h): fill `nbytes` of `buf` with `value` once."""
+    _check(lib().s2r_diag_stream_write(_ptr(buf), nbytes, value, _stream(stream)),
+           "s2r_diag_stream_write")
 
 
 def s2r_diag_stream_read(buf, nbytes: int, sink, stream=None) -> None:

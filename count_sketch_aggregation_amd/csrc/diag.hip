@@ -29,7 +29,30 @@ __global__ __launch_bounds__(kDiagThreads) void k_diag_read(const f32x4* __restr
   if (acc == 1.0f) *sink = acc;
 }
 
+// Grid-stride 128-bit stores of `value` over n4 float4 groups.
+__global__ __launch_bounds__(kDiagThreads) void k_diag_write(f32x4* __restrict__ out, uint64_t n4,
+                                                             float value) {
+  const uint64_t stride = (uint64_t)gridDim.x * kDiagThreads;
+  const f32x4 v = {value, value, value, value};
+  for (uint64_t i = (uint64_t)blockIdx.x * kDiagThreads + threadIdx.x; i < n4; i += stride)
+    out[i] = v;
+}
+
 }  // namespace s2r
+
+extern "C" s2r_status s2r_diag_stream_write(void* buf, size_t bytes, float value, void* stream) {
+  if (!buf) return S2R_ERR_NULL;
+  if (reinterpret_cast<uintptr_t>(buf) % 16 != 0 || bytes % 16 != 0) return S2R_ERR_ALIGN;
+  const uint64_t n4 = bytes / 16;
+  if (n4 == 0) return S2R_OK;
+  uint64_t blocks = (n4 + s2r::kDiagThreads - 1) / s2r::kDiagThreads;
+  if (blocks > 8192) blocks = 8192;
+  s2r::trace_mark(static_cast<hipStream_t>(stream), "k_diag_write");
+  hipLaunchKernelGGL(s2r::k_diag_write, dim3((uint32_t)blocks), dim3(s2r::kDiagThreads), 0,
+                     static_cast<hipStream_t>(stream), reinterpret_cast<s2r::f32x4*>(buf), n4,
+                     value);
+  return hipGetLastError() == hipSuccess ? S2R_OK : S2R_ERR_HIP;
+}
 
 extern "C" s2r_status s2r_diag_stream_read(const void* buf, size_t bytes, float* sink,
                                            void* stream) {

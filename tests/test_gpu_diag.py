@@ -96,3 +96,11 @@ def test_trace_attach_rejects_bad_capacity():
     t.capacity, t.count = 4, 5
     with pytest.raises(s2r.S2RError):
         s2r.s2r_diag_trace_attach(t)
+
+
+@pytest.mark.parametrize("n", [4, 1024, (1 << 22) + 4])
+def test_stream_write_fills_everything(n):
+    buf = torch.full((n,), -1.0, dtype=torch.float32, device="cuda")
+    s2r.s2r_diag_stream_write(buf, n * 4, 2.5)
+    torch.cuda.synchronize()
+    assert bool((buf == 2.5).all())
