@@ -534,9 +534,13 @@ __global__ __launch_bounds__(kDecThreads) void k_dwrite(HashArgs h, uint64_t n, 
     }
   }
   if (base + kDecTile <= n) {
+    // non-temporal: the output is not read again by this path, and cached stores leave it
+    // dirty in L2 and the Infinity Cache, where the next encode's gradient stream has to
+    // evict it (measured on MI355X: whole steps 0.4-1.1% faster, though this kernel alone
+    // is up to 15% slower on the embedding workload)
     f32x4* o4 = reinterpret_cast<f32x4*>(out + base);
 #pragma unroll
-    for (int r = 0; r < RPT; ++r) o4[tid + kDecThreads * r] = o[r];
+    for (int r = 0; r < RPT; ++r) __builtin_nontemporal_store(o[r], &o4[tid + kDecThreads * r]);
   } else {
 #pragma unroll
     for (int r = 0; r < RPT; ++r) {

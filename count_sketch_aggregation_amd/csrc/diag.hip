@@ -29,13 +29,20 @@ __global__ __launch_bounds__(kDiagThreads) void k_diag_read(const f32x4* __restr
   if (acc == 1.0f) *sink = acc;
 }
 
-// Grid-stride 128-bit stores of `value` over n4 float4 groups.
+// 128-bit non-temporal stores of `value`, shaped like the decode's output pass: one
+// 256-thread workgroup per 32 KiB, each thread storing kDiagStores float4 groups
+// tid + 256 r (every store instruction of a wave covers 1 KiB).
+constexpr int kDiagStores = 8;
+
 __global__ __launch_bounds__(kDiagThreads) void k_diag_write(f32x4* __restrict__ out, uint64_t n4,
                                                              float value) {
-  const uint64_t stride = (uint64_t)gridDim.x * kDiagThreads;
   const f32x4 v = {value, value, value, value};
-  for (uint64_t i = (uint64_t)blockIdx.x * kDiagThreads + threadIdx.x; i < n4; i += stride)
-    out[i] = v;
+  const uint64_t base = (uint64_t)blockIdx.x * kDiagThreads * kDiagStores;
+#pragma unroll
+  for (int r = 0; r < kDiagStores; ++r) {
+    const uint64_t i = base + threadIdx.x + (uint64_t)kDiagThreads * r;
+    if (i < n4) __builtin_nontemporal_store(v, &out[i]);
+  }
 }
 
 }  // namespace s2r
@@ -45,8 +52,9 @@ extern "C" s2r_status s2r_diag_stream_write(void* buf, size_t bytes, float value
   if (reinterpret_cast<uintptr_t>(buf) % 16 != 0 || bytes % 16 != 0) return S2R_ERR_ALIGN;
   const uint64_t n4 = bytes / 16;
   if (n4 == 0) return S2R_OK;
-  uint64_t blocks = (n4 + s2r::kDiagThreads - 1) / s2r::kDiagThreads;
-  if (blocks > 8192) blocks = 8192;
+  const uint64_t per = (uint64_t)s2r::kDiagThreads * s2r::kDiagStores;
+  const uint64_t blocks = (n4 + per - 1) / per;
+  if (blocks > 0x7fffffffull) return S2R_ERR_DIM;
   s2r::trace_mark(static_cast<hipStream_t>(stream), "k_diag_write");
   hipLaunchKernelGGL(s2r::k_diag_write, dim3((uint32_t)blocks), dim3(s2r::kDiagThreads), 0,
                      static_cast<hipStream_t>(stream), reinterpret_cast<s2r::f32x4*>(buf), n4,

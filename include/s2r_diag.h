@@ -20,11 +20,12 @@ extern "C" {
  * Errors: S2R_ERR_NULL, S2R_ERR_ALIGN, S2R_ERR_HIP. */
 s2r_status s2r_diag_stream_read(const void* buf, size_t bytes, float* sink, void* stream);
 
-/* Fills `bytes` of device memory with `value` once -- 128-bit stores from a grid-stride loop
- * over at most 8192 workgroups, the store form of the decode's output pass -- on `stream`.
- * The duration of the call, taken with events on that stream, gives the achievable HBM write
+/* Fills `bytes` of device memory with `value` once -- 128-bit non-temporal stores, one
+ * workgroup per 32 KiB, the store form of the decode's output pass -- on `stream`.  The
+ * duration of the call, taken with events on that stream, gives the achievable HBM write
  * rate.  buf 16-byte aligned, bytes a multiple of 16.
- * Errors: S2R_ERR_NULL, S2R_ERR_ALIGN, S2R_ERR_HIP. */
+ * Errors: S2R_ERR_NULL, S2R_ERR_ALIGN, S2R_ERR_DIM (more than 2^31 - 1 workgroups),
+ * S2R_ERR_HIP. */
 s2r_status s2r_diag_stream_write(void* buf, size_t bytes, float value, void* stream);
 
 #define S2R_TRACE_MAX 64
