@@ -625,121 +625,193 @@ __device__ __forceinline__ void acc_add(const HashArgs& h, float* tile, uint32_t
   lds_add_f32_many<UN * D>(tile, cell, add, live);
 }
 
-// k_accumulate (partitioned path): grid (P, W), 512 threads, items XCD-grouped; the tile
-// leaves with non-temporal stores when nt is set.  The partition's d x 2^K
-// buckets live in LDS.  Its entries are spread over one short segment per list chunk; the
-// segments of up to kSegBatch chunks are flattened with a prefix sum so that consecutive
-// threads read consecutive entries, several per thread in flight.
-template <int D>
+// Item v of k_accumulate's sequence (v < items) -> (worker, partition) item: XCD x runs the
+// x-th eighth of the items in order, so that neighbouring partitions, whose chunk offsets
+// share cache lines, run on one XCD at about the same time.  Workgroup b runs on XCD b % 8
+// and walks v = b, b + G, b + 2G, ... with G (the grid) a multiple of 8, so v % 8 stays b's
+// XCD.  Identity when either count is not a multiple of 8.
+__device__ __forceinline__ uint32_t acc_item(uint32_t v, uint32_t items) {
+  if (items % kXcds != 0 || gridDim.x % kXcds != 0) return v;
+  return (v % kXcds) * (items / kXcds) + v / kXcds;
+}
+
+// Issues the loads of a chunk batch's segment bounds: chunk row (cb + c) of the partition's
+// column pf, for c = tid * PER + u below nb (clamped, unconditional loads: all in flight at
+// once; rows past nb re-read row cb + nb - 1 and are dropped by acc_flatten).
+template <int PER>
+__device__ __forceinline__ void acc_bounds(const uint32_t* pf, uint32_t partitions, uint64_t cb,
+                                           uint64_t nb, uint32_t* lo, uint32_t* hi) {
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int u = 0; u < PER; ++u) {
+    const uint64_t c = (uint64_t)tid * PER + u < nb ? (uint64_t)tid * PER + u : nb - 1;
+    const uint64_t row = (cb + c) * (partitions + 1);
+    lo[u] = pf[row];
+    hi[u] = pf[row + 1];
+  }
+}
+
+// Flattens the segments of chunks [cb, cb + nb) (bounds lo/hi from acc_bounds) into
+// seg_src / seg_off and returns their total entry count E.  Whole workgroup, two barriers;
+// seg_src, seg_off and wtot must be free on entry.
+template <int PER>
+__device__ __forceinline__ uint32_t acc_flatten(uint32_t cb, uint32_t nb, const uint32_t* lo,
+                                                const uint32_t* hi, uint32_t* seg_src,
+                                                uint32_t* seg_off, uint32_t* wtot) {
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  uint32_t len[PER], sum = 0;
+#pragma unroll
+  for (int u = 0; u < PER; ++u) {
+    const uint32_t c = tid * PER + u;
+    len[u] = 0;
+    if (c < nb) {
+      seg_src[c] = (cb + c) * (uint32_t)kChunk + lo[u];
+      len[u] = hi[u] - lo[u];
+    }
+    sum += len[u];
+  }
+  const uint32_t inc = wave_inclusive_sum(sum);
+  if (lane == kWave - 1) wtot[wave] = inc;
+  __syncthreads();
+  uint32_t run = inc - sum;
+  for (int v = 0; v < wave; ++v) run += wtot[v];
+#pragma unroll
+  for (int u = 0; u < PER; ++u) {
+    const uint32_t c = tid * PER + u;
+    if (c <= nb) seg_off[c] = run;  // seg_off[nb] = total entries of the batch
+    run += len[u];
+  }
+  if (tid == kAccThreads - 1 && nb == (uint32_t)kSegBatch) seg_off[kSegBatch] = run;
+  __syncthreads();
+  return seg_off[nb];
+}
+
+// Adds the E > 0 flattened entries of a batch into the tile; the thread's first group
+// (entries tid + u * kAccThreads) is already in pa.  Software pipeline: the segment search
+// and list loads of the next group issue before the current group's adds, so one group's
+// global round trip overlaps the previous group's LDS work.  The register sets a and b
+// alternate, so no loaded register is ever copied (a copy would wait for its load).
+template <int D, int UN>
+__device__ __forceinline__ void acc_batch(const HashArgs& h, float* tile, uint32_t pw,
+                                          const uint32_t* seg_off, const uint32_t* seg_src,
+                                          uint32_t nb, uint32_t E, const uint2* kb, uint2* pa) {
+  constexpr uint32_t kStep = kAccThreads * UN;
+  uint2 pb[UN];
+  for (uint32_t e0 = threadIdx.x; e0 < E; e0 += 2 * kStep) {
+    acc_fetch<UN>(seg_off, seg_src, nb, E, kb, e0 + kStep, pb);
+    acc_add<D, UN>(h, tile, pw, E, e0, pa);
+    if (e0 + kStep >= E) break;
+    acc_fetch<UN>(seg_off, seg_src, nb, E, kb, e0 + 2 * kStep, pa);
+    acc_add<D, UN>(h, tile, pw, E, e0 + kStep, pb);
+  }
+}
+
+// k_accumulate (partitioned path): a grid of G workgroups (a multiple of 8 where the item
+// count allows), 512 threads; workgroup b accumulates items v = b, b + G, ... of the P x W
+// (partition, worker) items in turn (acc_item): one item each when G = P W, else a resident
+// grid walking the items.  The partition's d x 2^K buckets live in LDS.  Its entries are
+// spread over one short segment per list chunk; the segments of up to kSegBatch chunks are
+// flattened with a prefix sum so that consecutive threads read consecutive entries, several
+// per thread in flight.  The next item's list length and first segment bounds load while
+// this item accumulates, and its first segments are flattened and its first entries loaded
+// before this item's tile is written, so its two dependent round trips overlap this item's
+// adds and tile write.  The tile leaves with dense coalesced stores (non-temporal when nt
+// is set) and, on a walking grid, is cleared in LDS as it is read.  WALK = false compiles
+// the one-item-per-workgroup form, without the next item's registers.
+template <int D, bool WALK>
 __global__ __launch_bounds__(kAccThreads) void k_accumulate(
     HashArgs h, uint64_t tiles, const uint32_t* __restrict__ offsets, uint64_t cap,
-    uint64_t chunks, uint32_t partitions, const uint2* __restrict__ bins,
+    uint64_t chunks, uint32_t partitions, uint32_t items, const uint2* __restrict__ bins,
     const uint32_t* __restrict__ prefix, float* __restrict__ sketches, uint64_t w, int vec4,
     int nt) {
   extern __shared__ __align__(16) float tile[];  // D * 2^K
   __shared__ uint32_t seg_src[kSegBatch];
   __shared__ uint32_t seg_off[kSegBatch + 1];
   __shared__ uint32_t wtot[kAccThreads / kWave];
-  const uint32_t item = xcd_grouped_item();
-  const uint32_t p = item % partitions, k = item / partitions;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  constexpr int UN = acc_unroll(D);
+  constexpr int PER = kSegBatch / kAccThreads;
+  const int tid = threadIdx.x;
   const uint32_t pw = 1u << h.K;
   const uint32_t cells = D * pw;
-  for (uint32_t c = tid; c < cells; c += kAccThreads) tile[c] = 0.f;
+  uint32_t v = blockIdx.x;
+  if (v >= items) return;  // uniform
+  uint32_t item = acc_item(v, items);
+  uint32_t p = item % partitions, k = item / partitions;
 
-  // column p of the worker's chunk-major offsets: strided, but the XCD grouping runs the
-  // partitions that share each cache line on one XCD at about the same time
-  const uint32_t* pf = prefix + (uint64_t)k * chunks * (partitions + 1) + p;
-  const uint64_t kbase = (uint64_t)k * chunks * kChunk;
-  constexpr int PER = kSegBatch / kAccThreads;
-  // The first batch's offsets are read in the same round trip as the list length, before
-  // the number of filled chunks is known: rows up to the workspace's last chunk are in
-  // bounds, and those past the filled ones are dropped below.
+  // The first item's list length and first batch of segment bounds: rows up to the
+  // workspace's last chunk are in bounds, and those past the filled ones are dropped.  With
+  // no list capacity (chunks == 0) nothing is listed and every tile is written as zeros.
   uint32_t lo[PER], hi[PER];
-  if (chunks > 0) {
-#pragma unroll
-    for (int u = 0; u < PER; ++u) {
-      const uint64_t c = tid * PER + u < chunks ? tid * PER + u : chunks - 1;
-      lo[u] = pf[c * (partitions + 1)];
-      hi[u] = pf[c * (partitions + 1) + 1];
-    }
-  }
+  if (chunks > 0)
+    acc_bounds<PER>(prefix + (uint64_t)k * chunks * (partitions + 1) + p, partitions, 0, chunks,
+                    lo, hi);
   const uint64_t total = offsets[(uint64_t)k * (tiles + 1) + tiles];
-  const uint64_t lim = total < cap ? total : cap;
-  const uint32_t nch = (uint32_t)((lim + kChunk - 1) / kChunk);
-  for (uint32_t cb = 0; cb < nch; cb += kSegBatch) {
-    const uint32_t nb = nch - cb < (uint32_t)kSegBatch ? nch - cb : (uint32_t)kSegBatch;
-    __syncthreads();  // the previous batch is consumed (and the tile is zeroed)
-    uint32_t len[PER], sum = 0;
-    if (cb > 0) {
-#pragma unroll
-      for (int u = 0; u < PER; ++u) {  // clamped, unconditional loads: all in flight at once
-        const uint32_t c = tid * PER + u < nb ? tid * PER + u : nb - 1;
-        const uint64_t row = (uint64_t)(cb + c) * (partitions + 1);
-        lo[u] = pf[row];
-        hi[u] = pf[row + 1];
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < PER; ++u) {
-      const uint32_t c = tid * PER + u;
-      len[u] = 0;
-      if (c < nb) {
-        seg_src[c] = (cb + c) * (uint32_t)kChunk + lo[u];
-        len[u] = hi[u] - lo[u];
-      }
-      sum += len[u];
-    }
-    const uint32_t inc = wave_inclusive_sum(sum);
-    if (lane == kWave - 1) wtot[wave] = inc;
-    __syncthreads();
-    uint32_t run = inc - sum;
-    for (int v = 0; v < wave; ++v) run += wtot[v];
-#pragma unroll
-    for (int u = 0; u < PER; ++u) {
-      const uint32_t c = tid * PER + u;
-      if (c <= nb) seg_off[c] = run;  // seg_off[nb] = total entries of the batch
-      run += len[u];
-    }
-    if (tid == kAccThreads - 1 && nb == (uint32_t)kSegBatch) seg_off[kSegBatch] = run;
-    __syncthreads();
-    const uint32_t E = seg_off[nb];
-    if (E == 0) continue;  // uniform
-    // This thread's entries come in groups of UN (e0 + u * kAccThreads, e0 = tid + m * kStep).
-    // Software pipeline: the segment search and list loads of the next group issue before the
-    // current group's adds, so one group's global round trip overlaps the previous group's LDS
-    // work.  The register sets a and b alternate, so no loaded register is ever copied (a copy
-    // would wait for its load).
-    constexpr int UN = acc_unroll(D);
-    constexpr uint32_t kStep = kAccThreads * UN;
-    const uint2* kb = bins + kbase;
-    uint2 pa[UN], pb[UN];
-    acc_fetch<UN>(seg_off, seg_src, nb, E, kb, tid, pa);
-    for (uint32_t e0 = tid; e0 < E; e0 += 2 * kStep) {
-      acc_fetch<UN>(seg_off, seg_src, nb, E, kb, e0 + kStep, pb);
-      acc_add<D, UN>(h, tile, pw, E, e0, pa);
-      if (e0 + kStep >= E) break;
-      acc_fetch<UN>(seg_off, seg_src, nb, E, kb, e0 + 2 * kStep, pa);
-      acc_add<D, UN>(h, tile, pw, E, e0 + kStep, pb);
-    }
-  }
-  __syncthreads();
+  for (uint32_t c = tid; c < cells; c += kAccThreads) tile[c] = 0.f;
+  uint32_t nch = (uint32_t)(((total < cap ? total : cap) + kChunk - 1) / kChunk);
+  uint32_t nb = nch < (uint32_t)kSegBatch ? nch : (uint32_t)kSegBatch;
+  uint32_t E = nb ? acc_flatten<PER>(0, nb, lo, hi, seg_src, seg_off, wtot) : 0u;
+  uint2 pa[UN];
+  if (E) acc_fetch<UN>(seg_off, seg_src, nb, E, bins + (uint64_t)k * chunks * kChunk, tid, pa);
 
-  float* sk = sketches + (uint64_t)k * D * w + (uint64_t)p * pw;
-  if (vec4) {
-    const uint32_t pw4 = pw / 4;
-    for (uint32_t c = tid; c < D * pw4; c += kAccThreads) {
-      const uint32_t j = c / pw4, q = c - j * pw4;
-      const f32x4 x = *reinterpret_cast<const f32x4*>(&tile[j * pw + 4 * q]);
-      f32x4* dst = reinterpret_cast<f32x4*>(sk + (uint64_t)j * w + 4 * q);
-      if (nt) __builtin_nontemporal_store(x, dst);
-      else *dst = x;
+  while (true) {
+    const uint32_t* pf = prefix + (uint64_t)k * chunks * (partitions + 1) + p;
+    const uint2* kb = bins + (uint64_t)k * chunks * kChunk;
+    // the next item's list length and first segment bounds, in flight during this item
+    const uint32_t nv = v + gridDim.x;
+    const bool more = WALK && nv < items;  // uniform
+    const uint32_t nitem = more ? acc_item(nv, items) : item;
+    const uint32_t np = nitem % partitions, nk = nitem / partitions;
+    uint32_t nlo[PER], nhi[PER];
+    uint64_t ntotal = 0;
+    if (more) {
+      if (chunks > 0)
+        acc_bounds<PER>(prefix + (uint64_t)nk * chunks * (partitions + 1) + np, partitions, 0,
+                        chunks, nlo, nhi);
+      ntotal = offsets[(uint64_t)nk * (tiles + 1) + tiles];
     }
-  } else {
-    for (uint32_t c = tid; c < cells; c += kAccThreads) {
-      const uint32_t j = c / pw, q = c - j * pw;
-      sk[(uint64_t)j * w + q] = tile[c];
+    // this item's batches; the first is flattened and its first group loaded already
+    for (uint32_t cb = 0; cb < nch; cb += kSegBatch) {
+      if (cb > 0) {
+        nb = nch - cb < (uint32_t)kSegBatch ? nch - cb : (uint32_t)kSegBatch;
+        acc_bounds<PER>(pf, partitions, cb, nb, lo, hi);
+        __syncthreads();  // the previous batch is consumed
+        E = acc_flatten<PER>(cb, nb, lo, hi, seg_src, seg_off, wtot);
+        if (E) acc_fetch<UN>(seg_off, seg_src, nb, E, kb, tid, pa);
+      }
+      if (E) acc_batch<D, UN>(h, tile, pw, seg_off, seg_src, nb, E, kb, pa);
     }
+    __syncthreads();  // the tile is complete; the segment arrays are free
+    if (more) {  // the next item's first batch, before this tile is written
+      nch = (uint32_t)(((ntotal < cap ? ntotal : cap) + kChunk - 1) / kChunk);
+      nb = nch < (uint32_t)kSegBatch ? nch : (uint32_t)kSegBatch;
+      E = nb ? acc_flatten<PER>(0, nb, nlo, nhi, seg_src, seg_off, wtot) : 0u;
+      if (E) acc_fetch<UN>(seg_off, seg_src, nb, E, bins + (uint64_t)nk * chunks * kChunk, tid, pa);
+    }
+    float* sk = sketches + (uint64_t)k * D * w + (uint64_t)p * pw;
+    if (vec4) {
+      const uint32_t pw4 = pw / 4;
+      f32x4* t4 = reinterpret_cast<f32x4*>(tile);
+      for (uint32_t c = tid; c < D * pw4; c += kAccThreads) {
+        const uint32_t j = c / pw4, q = c - j * pw4;
+        const f32x4 x = t4[c];  // = tile[j pw + 4 q]
+        if constexpr (WALK) t4[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+        f32x4* dst = reinterpret_cast<f32x4*>(sk + (uint64_t)j * w + 4 * q);
+        if (nt) __builtin_nontemporal_store(x, dst);
+        else *dst = x;
+      }
+    } else {
+      for (uint32_t c = tid; c < cells; c += kAccThreads) {
+        const uint32_t j = c / pw, q = c - j * pw;
+        sk[(uint64_t)j * w + q] = tile[c];
+        if constexpr (WALK) tile[c] = 0.f;
+      }
+    }
+    if (!more) break;
+    __syncthreads();  // the tile is clear before the next item's adds
+    v = nv;
+    item = nitem;
+    p = np;
+    k = nk;
   }
 }
 
@@ -887,15 +959,53 @@ hipError_t launch_accumulate(const HashArgs& h, uint32_t W, uint64_t tiles,
   // sketches larger than the Infinity Cache go out with non-temporal stores; smaller ones
   // stay cached for the reduce that reads them next (both measured faster on MI355X)
   const int nt = (uint64_t)W * ((uint64_t)h.d * w) * sizeof(float) > kCacheResidentBytes ? 1 : 0;
+  const uint64_t items = partitions * W;
+  if (items == 0) return hipSuccess;
+  if (items > 0xffffffffull) return hipErrorInvalidValue;
   hipError_t e = hipSuccess;
+  // Partitions with few entries (the list capacity over P, at most kAccWalkEntries) are
+  // bound by each item's two dependent round trips: a resident grid that walks the items
+  // overlaps them with the previous item's adds and tile write.  Partitions with many
+  // entries are bound by the LDS adds, and one workgroup per item, each slot refilled as
+  // its workgroup ends, is faster.  Measured on MI355X, one workgroup per item against the
+  // walking grid: 244 entries per partition 392 -> 355 us, about 2000 40 -> 37 us; about
+  // 4000 the walk loses, 116 -> 125 us and 486 -> 503 us.
+  const bool walk = cap / partitions <= kAccWalkEntries;
+  int cus = 0;
+  if (walk) {
+    int dev = 0;
+    e = hipGetDevice(&dev);
+    if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return e;
+  }
   S2R_DISPATCH_D(h.d, {
-    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_accumulate<D>),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    const void* kfn = walk ? reinterpret_cast<const void*>(&k_accumulate<D, true>)
+                           : reinterpret_cast<const void*>(&k_accumulate<D, false>);
+    e = hipFuncSetAttribute(kfn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    uint64_t grid = items;
+    if (e == hipSuccess && walk) {
+      int per_cu = 0;
+      e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kfn, kAccThreads, lds);
+      // as many workgroups as are resident at once, a multiple of 8 (acc_item), spread so
+      // that every workgroup gets the same number of items to within one
+      uint64_t most = (uint64_t)(per_cu > 0 ? per_cu : 1) * (uint64_t)(cus > 0 ? cus : 1);
+      if (most > kXcds) most -= most % kXcds;
+      const uint64_t rounds = (items + most - 1) / most;
+      grid = (items + rounds - 1) / rounds;
+      if (grid > kXcds) grid = (grid + kXcds - 1) / kXcds * kXcds;
+      if (grid > most) grid = most;
+      if (grid > items) grid = items;
+    }
     if (e == hipSuccess) {
       trace_mark(s, "k_accumulate");
-      hipLaunchKernelGGL((k_accumulate<D>), dim3((uint32_t)partitions, W), dim3(kAccThreads), lds,
-                         s, h, tiles, offsets, cap, chunks, (uint32_t)partitions, bins, prefix,
-                         sketches, w, vec4, nt);
+      if (walk)
+        hipLaunchKernelGGL((k_accumulate<D, true>), dim3((uint32_t)grid), dim3(kAccThreads), lds,
+                           s, h, tiles, offsets, cap, chunks, (uint32_t)partitions,
+                           (uint32_t)items, bins, prefix, sketches, w, vec4, nt);
+      else
+        hipLaunchKernelGGL((k_accumulate<D, false>), dim3((uint32_t)grid), dim3(kAccThreads), lds,
+                           s, h, tiles, offsets, cap, chunks, (uint32_t)partitions,
+                           (uint32_t)items, bins, prefix, sketches, w, vec4, nt);
     }
   });
   if (e != hipSuccess) return e;

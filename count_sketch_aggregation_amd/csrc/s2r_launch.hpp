@@ -25,10 +25,13 @@ constexpr int kChunk = 8192;                        // list entries per chunk
 constexpr int kBinThreads = 512;                    // 16 entries per thread
 constexpr int kMaxPartitions = 8192;                // LDS histogram limit of the binning pass
 constexpr int kAccThreads = 512;
-// entries in flight per thread of the encode accumulation (measured on MI355X: 2 beats 1
-// and 4, which costs occupancy at d = 5); one for many rows keeps it out of scratch
-constexpr int acc_unroll(int d) { return d <= 5 ? 2 : 1; }
+// entries in flight per thread of the encode accumulation (measured on MI355X at d = 5:
+// one is 1-5% faster than two, whose ten compare-and-swaps in flight cost registers; at
+// d = 3 two win); one for many rows keeps it out of scratch
+constexpr int acc_unroll(int d) { return d <= 3 ? 2 : 1; }
 constexpr int kSegBatch = 1024;                     // chunk segments flattened per batch
+constexpr uint64_t kAccWalkEntries = 2048;          // entries per partition up to which the
+                                                    // accumulation walks items on a resident grid
 constexpr size_t kAccLdsBytes = 64 * 1024;          // LDS of one partition tile
 constexpr uint64_t kCacheResidentBytes = 256ull << 20;  // MI355X Infinity Cache
 
