@@ -250,6 +250,27 @@ def test_decode_sparse_bitmap_tight_capacity(n, density):
     gp.assert_decode_matches(out, want, tol, gp.bits_of(bm, n), exact=True)
 
 
+@pytest.mark.parametrize("set_bits", [9_999, 10_000, 10_001, 96_000])
+def test_decode_unsort_threshold(set_bits):
+    """The partitioned decode on both sides of the density where the medians stop being put
+    in rank order by a separate pass (fewer than n / 32 set bits: k_dwrite reads each median
+    through its rank's slot instead), with exactly `set_bits` set bits out of n = 320,000."""
+    d, L, n = 5, 20, 320_000  # a 20 MiB table: the partitioned path; n / 32 = 10,000
+    p, op = gp.params_pair(91, d, L)
+    sketch = WL.random_sketch((d, 1 << L), 12)
+    rng = np.random.Generator(np.random.PCG64(set_bits))
+    pos = rng.choice(n, size=set_bits, replace=False)
+    bits = np.zeros(((n + 63) // 64) * 64, dtype=np.uint8)
+    bits[pos] = 1
+    bm = np.packbits(bits, bitorder="little").view(np.uint64).copy()
+    assert int(gp.bits_of(bm, n).sum()) == set_bits
+    gp.say(f"decode unsort threshold U={set_bits} n={n}")
+    want, tol = oracle.decode_dense(op, n, bm, sketch.astype(np.float64))
+    for ms in (n, set_bits):
+        out = gp.run_decode(p, n, bm, sketch, path="partitioned", max_set=ms)
+        gp.assert_decode_matches(out, want, tol, gp.bits_of(bm, n), exact=True)
+
+
 # ---------------------------------------------------------------------------------------
 # end to end
 
