@@ -69,6 +69,9 @@ ENCODE_CASES = [
     ("d2_w1", 2, 5_000, 5_000, 0.1, 2, 0, 0, {}),
     ("w2_K0", 2, 5_000, 5_000, 0.1, 3, 1, 0, {}),
     ("K0_many_partitions", 2, 200_000, 200_000, 0.05, 3, 13, 0, {}),
+    # 201 x 4 (worker, partition) items on a walking accumulation grid: two rounds, an item
+    # count that is not a multiple of 8, workgroups with one and with two items
+    ("walk_ragged_items", 201, 4096, 4096, 0.2, 5, 13, None, {}),
 ]
 
 
