@@ -120,7 +120,8 @@ __global__ __launch_bounds__(kDcountThreads) void k_dcount(const uint64_t* __res
                                                            uint64_t tiles, uint32_t lb,
                                                            uint32_t* __restrict__ tcount) {
   const int lane = threadIdx.x & 63;
-  const uint64_t t0 = ((uint64_t)blockIdx.x * (kDcountThreads / kWave) + (threadIdx.x >> 6)) * 2;
+  const uint64_t vb = xcd_run_item(blockIdx.x, gridDim.x, 256);  // 2 MiB of bitmap per XCD run
+  const uint64_t t0 = (vb * (kDcountThreads / kWave) + (threadIdx.x >> 6)) * 2;
   if (t0 >= tiles) return;  // wave-uniform
   const uint64_t q0 = t0 * kDecWords + 4 * lane;
   uint64_t r[4];
@@ -477,10 +478,11 @@ __global__ __launch_bounds__(kDecThreads) void k_dwrite(HashArgs h, uint64_t n, 
   __shared__ uint32_t lwo[kDecWords];
   __shared__ uint32_t wtot[2];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const uint64_t base = (uint64_t)blockIdx.x * kDecTile;
+  const uint64_t tile = xcd_run_item(blockIdx.x, gridDim.x, 64);  // 2 MiB of output per XCD run
+  const uint64_t base = tile * kDecTile;
   uint64_t wv = 0;
   if (tid < kDecWords)
-    wv = masked_word(bitmap, nwords, n, (uint64_t)blockIdx.x * kDecWords + tid, h.lb);
+    wv = masked_word(bitmap, nwords, n, tile * kDecWords + tid, h.lb);
   const uint32_t pc = (uint32_t)__popcll(wv);
   const uint32_t inc = wave_inclusive_sum(pc);
   if (tid < kDecWords) {
@@ -493,7 +495,7 @@ __global__ __launch_bounds__(kDecThreads) void k_dwrite(HashArgs h, uint64_t n, 
   const uint64_t U = ws.toff[tiles];
   const bool direct = U > ws.max_set;
   const bool via_slot = U < ws.sparse_below;  // k_dunsort did nothing
-  const uint64_t rank0 = ws.toff[blockIdx.x];
+  const uint64_t rank0 = ws.toff[tile];
   constexpr int RPT = kDecTile / 4 / kDecThreads;  // 8 groups per thread
   uint32_t nib[RPT], rk[RPT];
 #pragma unroll
@@ -597,19 +599,20 @@ __global__ __launch_bounds__(kDecThreads) void k_dwrite_direct(
     const float* __restrict__ sketch, uint64_t w, float* __restrict__ out) {
   __shared__ __align__(16) float lout[kDecTile];
   const int tid = threadIdx.x;
-  const uint64_t base = (uint64_t)blockIdx.x * kDecTile;
+  const uint64_t tile = xcd_run_item(blockIdx.x, gridDim.x, 64);  // 2 MiB of output per XCD run
+  const uint64_t base = tile * kDecTile;
   constexpr int RPT = kDecTile / 4 / kDecThreads;  // 8 groups per thread
   // group g = tid + 256 r lies in word g >> 4 = (tid >> 4) + 16 r at bit 4 (tid & 15)
   uint64_t raw[RPT];
 #pragma unroll
   for (int r = 0; r < RPT; ++r) {  // all eight loads first, then the (branchy) masking
-    const uint64_t q = (uint64_t)blockIdx.x * kDecWords + (tid >> 4) + 16 * r;
+    const uint64_t q = tile * kDecWords + (tid >> 4) + 16 * r;
     raw[r] = bitmap[masked_src(q < nwords ? q : nwords - 1, h.lb)];
   }
   uint32_t mask = 0;
 #pragma unroll
   for (int r = 0; r < RPT; ++r) {
-    const uint64_t q = (uint64_t)blockIdx.x * kDecWords + (tid >> 4) + 16 * r;
+    const uint64_t q = tile * kDecWords + (tid >> 4) + 16 * r;
     const uint64_t wv = masked_from(raw[r], nwords, n, q, h.lb);
     mask |= (uint32_t)((wv >> (4 * (tid & 15))) & 0xFu) << (4 * r);
   }

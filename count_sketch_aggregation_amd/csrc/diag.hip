@@ -31,13 +31,14 @@ __global__ __launch_bounds__(kDiagThreads) void k_diag_read(const f32x4* __restr
 
 // 128-bit non-temporal stores of `value`, shaped like the decode's output pass: one
 // 256-thread workgroup per 32 KiB, each thread storing kDiagStores float4 groups
-// tid + 256 r (every store instruction of a wave covers 1 KiB).
+// tid + 256 r (every store instruction of a wave covers 1 KiB), the workgroups in XCD runs
+// of 2 MiB (xcd_run_item; measured on MI355X: 6.2-6.3 TB/s against 5.6 in round-robin order).
 constexpr int kDiagStores = 8;
 
 __global__ __launch_bounds__(kDiagThreads) void k_diag_write(f32x4* __restrict__ out, uint64_t n4,
                                                              float value) {
   const f32x4 v = {value, value, value, value};
-  const uint64_t base = (uint64_t)blockIdx.x * kDiagThreads * kDiagStores;
+  const uint64_t base = xcd_run_item(blockIdx.x, gridDim.x, 64) * kDiagThreads * kDiagStores;
 #pragma unroll
   for (int r = 0; r < kDiagStores; ++r) {
     const uint64_t i = base + threadIdx.x + (uint64_t)kDiagThreads * r;

@@ -77,7 +77,11 @@ __global__ __launch_bounds__(kStreamThreads) void k_stream(
     uint64_t* __restrict__ bitmaps, uint32_t* __restrict__ counts) {
   __shared__ uint64_t lwords[kTileWords];
   __shared__ uint32_t wcount[kStreamThreads / kWave];
-  const uint32_t t = blockIdx.x, k = blockIdx.y;
+  // tiles in XCD runs of 2 MiB (xcd_run_item); the grid is x-fastest over (tile, worker)
+  const uint64_t item =
+      xcd_run_item(blockIdx.x + (uint64_t)blockIdx.y * gridDim.x, (uint64_t)gridDim.x * gridDim.y,
+                   (2u << 20) / (kTile * sizeof(float)));
+  const uint32_t t = (uint32_t)(item % gridDim.x), k = (uint32_t)(item / gridDim.x);
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const float* row = grad + (uint64_t)k * ld;
   const uint64_t tile_base = (uint64_t)t * kTile;

@@ -23,7 +23,8 @@ __global__ __launch_bounds__(256) void k_reduce(uint32_t W, uint64_t cells, uint
   // no __restrict__ on sketches / sketch_out: they may alias (in place into slot 0)
   if (blockIdx.x < sblocks) {
     const uint64_t stride = (uint64_t)sblocks * blockDim.x;
-    const uint64_t gid = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    // 4 KiB of each worker per workgroup and pass: XCD runs of 2 MiB (xcd_run_item)
+    const uint64_t gid = xcd_run_item(blockIdx.x, sblocks, 512) * blockDim.x + threadIdx.x;
     if constexpr (VS) {
       const uint64_t c4 = cells / 4;
       const f32x4* in = reinterpret_cast<const f32x4*>(sketches);
@@ -46,7 +47,7 @@ __global__ __launch_bounds__(256) void k_reduce(uint32_t W, uint64_t cells, uint
   }
   const uint32_t bblocks = gridDim.x - sblocks;
   const uint64_t stride = (uint64_t)bblocks * blockDim.x;
-  const uint64_t gid = (uint64_t)(blockIdx.x - sblocks) * blockDim.x + threadIdx.x;
+  const uint64_t gid = xcd_run_item(blockIdx.x - sblocks, bblocks, 512) * blockDim.x + threadIdx.x;
   if constexpr (VB) {  // pairs of words, 128-bit loads (words even, 16-byte aligned rows)
     const uint64_t w2 = words / 2;
     const uint4* in = reinterpret_cast<const uint4*>(bitmaps);
@@ -87,6 +88,8 @@ hipError_t launch_reduce(uint32_t W, uint64_t cells, uint64_t words, const uint6
   if (blocks > 65536) blocks = 65536;
   uint64_t sblocks = su ? (blocks * su + total - 1) / total : 0;
   if (su && sblocks == 0) sblocks = 1;
+  // a multiple of 8, so that the bitmap part's workgroups start on XCD 0 (xcd_run_item)
+  if (sblocks > kXcds) sblocks = (sblocks + kXcds - 1) / kXcds * kXcds;
   uint64_t bblocks = blocks > sblocks ? blocks - sblocks : 0;
   if (bu && bblocks == 0) bblocks = 1;
   const dim3 grid((uint32_t)(sblocks + bblocks));

@@ -198,6 +198,22 @@ __device__ __forceinline__ uint32_t xcd_grouped_item() {
   return (lin % kXcds) * (total / kXcds) + lin / kXcds;
 }
 
+// Streaming kernels: workgroups are dispatched to the 8 XCDs round-robin by linear id, and
+// each XCD translates addresses through its own L2 TLB.  With consecutive work items on
+// consecutive XCDs every XCD touches every page of the stream; this maps the linear id so
+// that each XCD takes runs of `run` consecutive work items (one 2 MiB page of the stream),
+// the 8 XCDs taking 8 adjacent runs at a time, so the stream still advances as one front.
+// Measured on MI355X for the gradient stream (16 KiB per item): runs of 2 MiB beat 0.5, 1
+// and 4 MiB, and the 32 GB stream of the 10^9-element workload ran 8% faster than
+// round-robin order (5.29 -> 4.81 ms), the 1.6-5 GB ones 4-7% faster.  Items past the last
+// whole group of 8 runs keep their own id.
+__device__ __forceinline__ uint64_t xcd_run_item(uint64_t lin, uint64_t total, uint32_t run) {
+  const uint64_t span = (uint64_t)kXcds * run;
+  if (lin >= total / span * span) return lin;
+  const uint64_t j = lin / kXcds;
+  return (j / run) * span + (lin % kXcds) * run + j % run;
+}
+
 // For each of U positions e[u]: the largest c in [0, nb) with off[c] <= e[u] (off
 // non-decreasing, off[0] = 0).  Branch-free search whose step count depends only on nb, so
 // the U searches advance together with U independent LDS reads per step.

@@ -43,12 +43,15 @@ __global__ __launch_bounds__(kTkNormThreads) void k_tk_norm(const float* __restr
                                                             int vec4,
                                                             uint32_t* __restrict__ zero,
                                                             uint32_t zero_words) {
-  const uint32_t k = blockIdx.y;
+  // (group, worker) items in XCD runs of 512 groups (xcd_run_item), the grid x-fastest
+  const uint64_t item =
+      xcd_run_item(blockIdx.x + (uint64_t)blockIdx.y * gridDim.x, (uint64_t)gridDim.x * gridDim.y, 512);
+  const uint32_t x = (uint32_t)(item % gridDim.x), k = (uint32_t)(item / gridDim.x);
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  if (blockIdx.x == 0)  // the worker's select histograms and candidate count start at zero
+  if (x == 0)  // the worker's select histograms and candidate count start at zero
     for (uint32_t i = threadIdx.x; i < zero_words; i += kTkNormThreads)
       zero[(uint64_t)k * zero_words + i] = 0u;
-  const uint64_t q = (uint64_t)blockIdx.x * (kTkNormThreads / kWave) + wave;
+  const uint64_t q = (uint64_t)x * (kTkNormThreads / kWave) + wave;
   if (q >= nb) return;  // whole wave
   const uint64_t first = q * block;
   const uint64_t len = first + block <= n ? block : n - first;
@@ -485,7 +488,10 @@ __global__ __launch_bounds__(kTkApplyThreads) void k_tk_apply(const float* __res
                                                               const uint64_t* __restrict__ sel,
                                                               uint64_t sel_words,
                                                               float* __restrict__ out) {
-  const uint32_t k = blockIdx.y;
+  // (group, worker) items in XCD runs of 128 groups of 16 KiB (xcd_run_item)
+  const uint64_t item =
+      xcd_run_item(blockIdx.x + (uint64_t)blockIdx.y * gridDim.x, (uint64_t)gridDim.x * gridDim.y, 128);
+  const uint32_t x = (uint32_t)(item % gridDim.x), k = (uint32_t)(item / gridDim.x);
   const uint64_t* sk = sel + (uint64_t)k * sel_words;
   // with error feedback the residual holds g (k_tk_norm), else g is the gradient itself
   const float* src = residual ? residual + (uint64_t)k * ld : grad + (uint64_t)k * ld;
@@ -493,7 +499,7 @@ __global__ __launch_bounds__(kTkApplyThreads) void k_tk_apply(const float* __res
   float* o = out + (uint64_t)k * ld;
   const uint32_t d = dv.d;  // the block size, or n when the block holds the whole row
   constexpr uint64_t kStep = 4ull * kTkApplyThreads;
-  const uint64_t e0 = 4 * ((uint64_t)blockIdx.x * kTkApplyThreads * kTkApplyIters + threadIdx.x);
+  const uint64_t e0 = 4 * ((uint64_t)x * kTkApplyThreads * kTkApplyIters + threadIdx.x);
   if (e0 + kStep * (kTkApplyIters - 1) + 4 <= n) {
     // every group whole and inside the row (ld % 4 == 0: aligned float4 groups)
     f32x4 g[kTkApplyIters];
