@@ -72,6 +72,9 @@ ENCODE_CASES = [
     # 201 x 4 (worker, partition) items on a walking accumulation grid: two rounds, an item
     # count that is not a multiple of 8, workgroups with one and with two items
     ("walk_ragged_items", 201, 4096, 4096, 0.2, 5, 13, None, {}),
+    # 402 tiles x 3 workers: one whole group of 8 XCD runs of 128 tiles, then a ragged tail
+    # of 182 tiles in launch order
+    ("xcd_runs_ragged", 3, 1_642_497, 1_642_500, 0.01, 3, 15, None, {}),
 ]
 
 
@@ -192,7 +195,10 @@ def test_reduce_integer_exact():
 DECODE_CASES = [(3, 14, 13, 1 << 20, 0.04), (5, 16, 12, 100_003, 0.3), (1, 10, 10, 4097, 0.5),
                 (2, 10, 4, 5000, 0.5), (4, 12, 12, 65, 1.0), (7, 9, 3, 9000, 0.2),
                 (16, 11, 11, 3000, 0.2), (5, 20, 12, 1, 1.0), (3, 18, 0, 300_000, 0.6),
-                (5, 22, 12, 200_000, 0.02), (3, 20, 20, 50_000, 0.1)]
+                (5, 22, 12, 200_000, 0.02), (3, 20, 20, 50_000, 0.1),
+                # 2076 output tiles of 8192: whole groups of 8 XCD runs (64 tiles of the
+                # output pass, 256 workgroups of the count pass) and ragged tails
+                (5, 20, None, 17_000_003, 0.01)]
 
 
 @pytest.mark.parametrize("path", ["direct", "partitioned", "overflow"])
