@@ -49,18 +49,15 @@ __global__ __launch_bounds__(256) void k_reduce(uint32_t W, uint64_t cells, uint
   const uint64_t stride = (uint64_t)bblocks * blockDim.x;
   const uint64_t gid = xcd_run_item(blockIdx.x - sblocks, bblocks, 512) * blockDim.x + threadIdx.x;
   if constexpr (VB) {  // pairs of words, 128-bit loads (words even, 16-byte aligned rows)
+    // non-temporal loads: the bitmaps are read once (measured on MI355X: 455 -> 437 us over
+    // the 1e9-element workload's 2.6 GB, no change on the smaller ones)
+    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
     const uint64_t w2 = words / 2;
-    const uint4* in = reinterpret_cast<const uint4*>(bitmaps);
-    uint4* out = reinterpret_cast<uint4*>(bitmap_out);
+    const u32x4* in = reinterpret_cast<const u32x4*>(bitmaps);
+    u32x4* out = reinterpret_cast<u32x4*>(bitmap_out);
     for (uint64_t q = gid; q < w2; q += stride) {
-      uint4 m = in[q];
-      for (uint32_t k = 1; k < W; ++k) {
-        const uint4 x = in[(uint64_t)k * w2 + q];
-        m.x |= x.x;
-        m.y |= x.y;
-        m.z |= x.z;
-        m.w |= x.w;
-      }
+      u32x4 m = __builtin_nontemporal_load(in + q);
+      for (uint32_t k = 1; k < W; ++k) m |= __builtin_nontemporal_load(in + (uint64_t)k * w2 + q);
       out[q] = m;
     }
   } else {
