@@ -150,64 +150,108 @@ struct DecodeWs {
   uint64_t sparse_below;      // U below this: no unsort pass; k_dwrite reads through slots
 };
 
-// Raw bitmap words q .. q + WPT - 1 of a k_dbin round (clamped below q_end, so every load
-// issues unconditionally; masked in dbin_round).
-template <int WPT>
-__device__ __forceinline__ void dbin_words(const uint64_t* __restrict__ bitmap, uint64_t q,
-                                           uint64_t q_end, uint32_t lb, uint64_t* wv) {
-#pragma unroll
-  for (int u = 0; u < WPT; ++u)
-    wv[u] = bitmap[masked_src(q + u < q_end ? q + u : q_end - 1, lb)];
+// Word u (< kDBinWordsPerThread) of thread tid in a k_dbin round starting at word q0.
+// Interleaved (IL): q0 + u * NT + tid, so a run of set bits shorter than the round spreads
+// over every wave (dense bitmaps, where a chunk's set bits fill a fraction of one round);
+// else blocked: q0 + kDBinWordsPerThread * tid + u (sparse bitmaps, where a chunk spans
+// several rounds and every wave already meets it).
+template <int NT, bool IL>
+__device__ __forceinline__ uint64_t dbin_word_index(uint64_t q0, int u, int tid) {
+  return IL ? q0 + (uint64_t)u * NT + tid : q0 + (uint64_t)kDBinWordsPerThread * tid + u;
 }
 
-// One round of k_dbin's rank expansion over words [q0, q0 + NT * kDBinWordsPerThread): masks the
-// thread's raw words, ranks them with a workgroup scan and expands the set bits whose rank
-// lies in [start, end) into litem; advances q0 and rank0.  Called by the whole workgroup
-// (two barriers).
-template <int NT>
-__device__ __forceinline__ void dbin_round(const uint64_t* raw, uint64_t n, uint64_t nwords,
+// Raw bitmap words of a k_dbin round (clamped below q_end, so every load issues
+// unconditionally; masked in dbin_round).
+template <int NT, bool IL>
+__device__ __forceinline__ void dbin_words(const uint64_t* __restrict__ bitmap, uint64_t q0,
+                                           uint64_t q_end, uint32_t lb, int tid, uint64_t* wv) {
+#pragma unroll
+  for (int u = 0; u < kDBinWordsPerThread; ++u) {
+    const uint64_t q = dbin_word_index<NT, IL>(q0, u, tid);
+    wv[u] = bitmap[masked_src(q < q_end ? q : q_end - 1, lb)];
+  }
+}
+
+// One round of k_dbin's rank expansion over words [q0, q0 + NT * kDBinWordsPerThread): masks
+// the thread's raw words (in place), ranks them in word order and expands the set bits whose rank lies
+// in [start, end) into litem; advances q0 and rank0.  Blocked: one workgroup scan of the
+// threads' popcount sums.  Interleaved: slice u (every thread's word u) precedes slice u + 1;
+// the four popcounts go through the wave scan as 16-bit fields of two words (a wave's field
+// sums stay below 2^13) and the per-wave sums are combined in full words.  Called by the
+// whole workgroup (two barriers).
+template <int NT, bool IL>
+__device__ __forceinline__ void dbin_round(uint64_t* wv, uint64_t n, uint64_t nwords,
                                            uint64_t q_end, uint32_t lb, uint64_t start,
                                            uint64_t end, uint64_t& q0, uint64_t& rank0,
-                                           uint32_t* litem, uint32_t* wtot, int tid) {
+                                           uint32_t* litem, uint4* wtot, int tid) {
+  static_assert(kDBinWordsPerThread == 4, "four slices packed in two scan words");
+  constexpr int NW = NT / kWave;
   const int wave = tid >> 6, lane = tid & 63;
-  uint64_t wv[kDBinWordsPerThread];
-  uint32_t sum = 0;
+  uint32_t pc[kDBinWordsPerThread];
 #pragma unroll
   for (int u = 0; u < kDBinWordsPerThread; ++u) {
-    const uint64_t q = q0 + (uint64_t)tid * kDBinWordsPerThread + u;
-    wv[u] = q < q_end ? masked_from(raw[u], nwords, n, q, lb) : 0ull;
-    sum += (uint32_t)__popcll(wv[u]);
-  }
-  const uint32_t inc = wave_inclusive_sum(sum);
-  if (lane == kWave - 1) wtot[wave] = inc;
-  __syncthreads();
-  uint32_t before = inc - sum, batch_total = 0;
-  for (int v = 0; v < NT / kWave; ++v) {
-    if (v < wave) before += wtot[v];
-    batch_total += wtot[v];
+    const uint64_t q = dbin_word_index<NT, IL>(q0, u, tid);
+    wv[u] = q < q_end ? masked_from(wv[u], nwords, n, q, lb) : 0ull;  // masked in place
+    pc[u] = (uint32_t)__popcll(wv[u]);
   }
   uint64_t rk0[kDBinWordsPerThread];
+  if constexpr (IL) {
+    const uint32_t a = pc[0] | (pc[1] << 16), b = pc[2] | (pc[3] << 16);
+    const uint32_t ia = wave_inclusive_sum(a), ib = wave_inclusive_sum(b);
+    if (lane == kWave - 1) wtot[wave] = make_uint4(ia & 0xFFFFu, ia >> 16, ib & 0xFFFFu, ib >> 16);
+    __syncthreads();
+    const uint32_t ea = ia - a, eb = ib - b;  // exclusive, within the wave
+    uint32_t before[kDBinWordsPerThread] = {ea & 0xFFFFu, ea >> 16, eb & 0xFFFFu, eb >> 16};
+    uint32_t total[kDBinWordsPerThread] = {0u, 0u, 0u, 0u};
+#pragma unroll 4
+    for (int v = 0; v < NW; ++v) {
+      const uint4 t = wtot[v];
+      if (v < wave) {
+        before[0] += t.x; before[1] += t.y; before[2] += t.z; before[3] += t.w;
+      }
+      total[0] += t.x; total[1] += t.y; total[2] += t.z; total[3] += t.w;
+    }
+    uint64_t base = rank0;
 #pragma unroll
-  for (int u = 0; u < kDBinWordsPerThread; ++u) {
-    rk0[u] = rank0 + before;
-    before += (uint32_t)__popcll(wv[u]);
+    for (int u = 0; u < kDBinWordsPerThread; ++u) {
+      rk0[u] = base + before[u];
+      base += total[u];
+    }
+    rank0 = base;
+  } else {
+    const uint32_t sum = pc[0] + pc[1] + pc[2] + pc[3];
+    const uint32_t inc = wave_inclusive_sum(sum);
+    if (lane == kWave - 1) wtot[wave].x = inc;
+    __syncthreads();
+    uint32_t before = inc - sum, total = 0;
+    for (int v = 0; v < NW; ++v) {
+      if (v < wave) before += wtot[v].x;
+      total += wtot[v].x;
+    }
+#pragma unroll
+    for (int u = 0; u < kDBinWordsPerThread; ++u) {
+      rk0[u] = rank0 + before;
+      before += pc[u];
+    }
+    rank0 += total;
   }
-  expand_owned_words<kDBinWordsPerThread>(wv, rk0, q0 + (uint64_t)tid * kDBinWordsPerThread,
-                                          start, end, litem, lane);
-  rank0 += batch_total;
+  expand_owned_words<kDBinWordsPerThread>(wv, rk0, q0, IL ? 1 : kDBinWordsPerThread,
+                                          IL ? (uint64_t)NT : 1, start, end, litem, tid);
   q0 += (uint64_t)NT * kDBinWordsPerThread;
   __syncthreads();  // wtot is reused next round
 }
 
-template <int NT>
-__global__ __launch_bounds__(NT) void k_dbin(HashArgs h, uint64_t n,
+template <int NT, bool IL>
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(NT <= 512 ? 6 : 4)))
+void k_dbin(HashArgs h, uint64_t n,
                                                        const uint64_t* __restrict__ bitmap,
                                                        uint64_t nwords, uint64_t tiles,
                                                        DecodeWs ws, uint32_t P) {
   extern __shared__ uint32_t hist[];  // P + 1
-  __shared__ uint32_t litem[kChunk];  // indices in rank order
-  __shared__ __align__(16) uint32_t sitem[kChunk];  // indices in partition order
-  __shared__ uint32_t wtot[NT / kWave];
+  // the chunk's indices in rank order, then (once every thread holds its own in registers)
+  // in partition order
+  __shared__ __align__(16) uint32_t litem[kChunk];
+  __shared__ uint4 wtot[NT / kWave];
   const uint32_t c = blockIdx.x;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const uint64_t U = ws.toff[tiles];
@@ -218,11 +262,11 @@ __global__ __launch_bounds__(NT) void k_dbin(HashArgs h, uint64_t n,
   const uint32_t cnt = (uint32_t)(U - start < kChunk ? U - start : kChunk);
   const uint64_t end = start + cnt;
 
-  // 1. expand ranks [start, end) into litem, NT * kDBinWordsPerThread bitmap words per round: each
-  //    thread holds kDBinWordsPerThread words and their ranks, and the waves expand only the
-  //    non-empty words that meet the chunk (expand_owned_words).  The chunk's last rank lies
-  //    at or before the tile where the next chunk starts, so words past that tile are not
-  //    read (a thread past it re-reads the last word in range and drops it).
+  // 1. expand ranks [start, end) into litem, NT * kDBinWordsPerThread bitmap words per round
+  //    (expand_owned_words visits only the non-empty words that meet the chunk).  The
+  //    chunk's last rank lies at or before the tile where the next chunk starts, so words
+  //    past that tile are not read (a thread past it re-reads the last word in range and
+  //    drops it).
   uint64_t q0 = (uint64_t)t0 * kDecWords;
   uint64_t rank0 = ws.toff[t0];
   const uint64_t t_last = end < U ? (uint64_t)ws.chunk_tile[c + 1] : tiles - 1;
@@ -232,28 +276,27 @@ __global__ __launch_bounds__(NT) void k_dbin(HashArgs h, uint64_t n,
   // word in range and are never used.
   constexpr uint64_t kRound = (uint64_t)NT * kDBinWordsPerThread;  // words per round
   uint64_t wa[kDBinWordsPerThread], wb[kDBinWordsPerThread];
-  dbin_words<kDBinWordsPerThread>(bitmap, q0 + (uint64_t)tid * kDBinWordsPerThread, q_end, h.lb, wa);
+  dbin_words<NT, IL>(bitmap, q0, q_end, h.lb, tid, wa);
   while (rank0 < end && q0 < q_end) {
-    dbin_words<kDBinWordsPerThread>(bitmap, q0 + kRound + (uint64_t)tid * kDBinWordsPerThread,
-                                    q_end, h.lb, wb);
-    dbin_round<NT>(wa, n, nwords, q_end, h.lb, start, end, q0, rank0, litem, wtot, tid);
+    dbin_words<NT, IL>(bitmap, q0 + kRound, q_end, h.lb, tid, wb);
+    dbin_round<NT, IL>(wa, n, nwords, q_end, h.lb, start, end, q0, rank0, litem, wtot, tid);
     if (!(rank0 < end && q0 < q_end)) break;
-    dbin_words<kDBinWordsPerThread>(bitmap, q0 + kRound + (uint64_t)tid * kDBinWordsPerThread,
-                                    q_end, h.lb, wa);
-    dbin_round<NT>(wb, n, nwords, q_end, h.lb, start, end, q0, rank0, litem, wtot, tid);
+    dbin_words<NT, IL>(bitmap, q0 + kRound, q_end, h.lb, tid, wa);
+    dbin_round<NT, IL>(wb, n, nwords, q_end, h.lb, start, end, q0, rank0, litem, wtot, tid);
   }
   for (uint32_t p = tid; p <= P; p += NT) hist[p] = 0;
   __syncthreads();
 
-  // 2. counting sort by partition
+  // 2. counting sort by partition; each thread keeps its items in registers, so litem can
+  //    take the sorted order
   constexpr int R = kChunk / NT;
-  uint32_t pp[R], rk[R];
+  uint32_t it[R], rk[R];
 #pragma unroll
   for (int r = 0; r < R; ++r) {
     const uint32_t s = tid + NT * r;
     if (s < cnt) {
-      pp[r] = partition_of(h, litem[s]);
-      rk[r] = atomicAdd(&hist[pp[r]], 1u);
+      it[r] = litem[s];
+      rk[r] = atomicAdd(&hist[partition_of(h, it[r])], 1u);
     }
   }
   __syncthreads();
@@ -264,10 +307,10 @@ __global__ __launch_bounds__(NT) void k_dbin(HashArgs h, uint64_t n,
     uint32_t sum = 0;
     for (uint32_t p = lo; p < hi; ++p) sum += hist[p];
     const uint32_t inc = wave_inclusive_sum(sum);
-    if (lane == kWave - 1) wtot[wave] = inc;
+    if (lane == kWave - 1) wtot[wave].x = inc;
     __syncthreads();
     uint32_t run = inc - sum;
-    for (int v = 0; v < wave; ++v) run += wtot[v];
+    for (int v = 0; v < wave; ++v) run += wtot[v].x;
     for (uint32_t p = lo; p < hi; ++p) {
       const uint32_t x = hist[p];
       hist[p] = run;
@@ -283,8 +326,8 @@ __global__ __launch_bounds__(NT) void k_dbin(HashArgs h, uint64_t n,
   for (int r = 0; r < R; ++r) {
     const uint32_t s = tid + NT * r;
     if (s < cnt) {
-      const uint32_t pos = hist[pp[r]] + rk[r];
-      sitem[pos] = litem[s];
+      const uint32_t pos = hist[partition_of(h, it[r])] + rk[r];
+      litem[pos] = it[r];
       sl[s] = (uint16_t)pos;
     }
   }
@@ -292,8 +335,8 @@ __global__ __launch_bounds__(NT) void k_dbin(HashArgs h, uint64_t n,
   uint32_t* bo = ws.bidx + start;
   const uint32_t cnt4 = cnt / 4;
   for (uint32_t q = tid; q < cnt4; q += NT)
-    *reinterpret_cast<uint4*>(bo + 4 * q) = *reinterpret_cast<const uint4*>(&sitem[4 * q]);
-  for (uint32_t s = 4 * cnt4 + tid; s < cnt; s += NT) bo[s] = sitem[s];
+    *reinterpret_cast<uint4*>(bo + 4 * q) = *reinterpret_cast<const uint4*>(&litem[4 * q]);
+  for (uint32_t s = 4 * cnt4 + tid; s < cnt; s += NT) bo[s] = litem[s];
 }
 
 // ---------------------------------------------------------------------------------------
@@ -750,17 +793,17 @@ hipError_t launch_decode(const HashArgs& h, const s2r_params& p, uint64_t n,
       // 1e9-element bitmap at 0.8% density; on denser ones the wide kernel is 40-65% slower)
       const bool wide = nwords * (uint64_t)kChunk >
                         4 * (uint64_t)kDBinThreads * kDBinWordsPerThread * ws.max_set;
-      const void* kfn = wide ? reinterpret_cast<const void*>(&k_dbin<kDBinThreadsWide>)
-                             : reinterpret_cast<const void*>(&k_dbin<kDBinThreads>);
+      const void* kfn = wide ? reinterpret_cast<const void*>(&k_dbin<kDBinThreadsWide, false>)
+                             : reinterpret_cast<const void*>(&k_dbin<kDBinThreads, true>);
       e = hipFuncSetAttribute(kfn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
       if (e != hipSuccess) return e;
       trace_mark(s, "k_dbin");
       if (wide)
-        hipLaunchKernelGGL(k_dbin<kDBinThreadsWide>, dim3((uint32_t)L.chunks),
+        hipLaunchKernelGGL((k_dbin<kDBinThreadsWide, false>), dim3((uint32_t)L.chunks),
                            dim3(kDBinThreadsWide), lds, s, h, n, bitmap, nwords, L.tiles, ws,
                            (uint32_t)L.partitions);
       else
-        hipLaunchKernelGGL(k_dbin<kDBinThreads>, dim3((uint32_t)L.chunks), dim3(kDBinThreads),
+        hipLaunchKernelGGL((k_dbin<kDBinThreads, true>), dim3((uint32_t)L.chunks), dim3(kDBinThreads),
                            lds, s, h, n, bitmap, nwords, L.tiles, ws, (uint32_t)L.partitions);
       e = hipGetLastError();
       if (e != hipSuccess) return e;

@@ -127,16 +127,19 @@ __device__ __forceinline__ uint64_t readlane64(uint64_t v, int l) {
   return ((uint64_t)hi << 32) | lo;
 }
 
-// List expansion of bitmap words held in registers: lane l of the wave owns words
-// qbase(l) + u (u < WPT) whose first set bit has list rank rank[u].  Writes
-// item[r - start] = 64 * word + bit for every set bit with rank r in [start, end).  The wave
-// visits only lanes whose word is non-empty and meets the range (a ballot), broadcasts that
-// word, and expands its 64 bits with one lane per bit (v_mbcnt gives each bit's rank), so the
-// cost follows the set bits in range, not the span of words.
+// List expansion of bitmap words held in registers: thread t owns words
+// qbase + t * tstride + u * ustride (u < WPT), whose first set bit has list rank rank[u].
+// Writes item[r - start] = 64 * word + bit for every set bit with rank r in [start, end).
+// The wave visits only lanes whose word is non-empty and meets the range (a ballot),
+// broadcasts that word, and expands its 64 bits with one lane per bit (v_mbcnt gives each
+// bit's rank), so the cost follows the set bits in range, not the span of words.
 template <int WPT>
 __device__ __forceinline__ void expand_owned_words(const uint64_t* wv, const uint64_t* rank,
-                                                   uint64_t qbase, uint64_t start, uint64_t end,
-                                                   uint32_t* item, int lane) {
+                                                   uint64_t qbase, uint64_t tstride,
+                                                   uint64_t ustride, uint64_t start,
+                                                   uint64_t end, uint32_t* item, int tid) {
+  const int lane = tid & (kWave - 1);
+  const uint64_t qwave = qbase + (uint64_t)(tid - lane) * tstride;
 #pragma unroll
   for (int u = 0; u < WPT; ++u) {
     const uint64_t pc = (uint64_t)__popcll(wv[u]);
@@ -146,7 +149,7 @@ __device__ __forceinline__ void expand_owned_words(const uint64_t* wv, const uin
       m &= m - 1;
       const uint64_t w = readlane64(wv[u], l);
       const uint64_t r = readlane64(rank[u], l) + bits_below_lane(w);
-      const uint64_t q = readlane64(qbase, l) + u;
+      const uint64_t q = qwave + (uint64_t)l * tstride + u * ustride;
       if (((w >> lane) & 1ull) && r >= start && r < end) item[r - start] = (uint32_t)(q * 64 + lane);
     }
   }
