@@ -56,6 +56,10 @@ constexpr int kDMedianUnroll = 4;  // items in flight per thread (stride kAccThr
 constexpr int kTileLoads = 8;      // 16-byte cell loads per thread in flight when a tile fills
 constexpr uint64_t kDMedianTargetGroups = 1536;
 constexpr uint32_t kDMedianMaxSplits = 8;
+// Set bits per k_dmedian workgroup above which a partition's chunks are split further
+// (measured on MI355X: about 21K per workgroup -> 11K took the Transformer workload's
+// k_dmedian 349 -> 317 us; below about 7K the extra cell loads cost more than they save)
+constexpr uint64_t kDMedianGroupItems = 16384;
 constexpr int kDBinWordsPerThread = 4;
 
 // Element word q (elements 64q .. 64q+63) of the query set, bits at or beyond n cleared.
@@ -809,9 +813,13 @@ hipError_t launch_decode(const HashArgs& h, const s2r_params& p, uint64_t n,
       if (e != hipSuccess) return e;
       const size_t tlds = ((size_t)p.d << p.log2_part) * sizeof(float);
       const int vec4 = (p.log2_part >= 2 && (reinterpret_cast<uintptr_t>(sketch) % 16) == 0);
-      // enough workgroups to fill the chip about twice at a few per CU; each split reloads
-      // the partition's cells, so never more splits than rank chunks
+      // enough workgroups to fill the chip about twice at a few per CU, and at most about
+      // kDMedianGroupItems set bits per workgroup (max_set stands in for U); each split
+      // reloads the partition's cells, so never more splits than rank chunks
       uint32_t splits = (uint32_t)((kDMedianTargetGroups + L.partitions - 1) / L.partitions);
+      const uint64_t by_items =
+          (ws.max_set + L.partitions * kDMedianGroupItems - 1) / (L.partitions * kDMedianGroupItems);
+      if (by_items > splits) splits = (uint32_t)(by_items < kDMedianMaxSplits ? by_items : kDMedianMaxSplits);
       if (splits > kDMedianMaxSplits) splits = kDMedianMaxSplits;
       if (splits > L.chunks) splits = (uint32_t)L.chunks;
       if (splits < 1) splits = 1;
