@@ -280,6 +280,36 @@ def test_decode_unsort_threshold(set_bits):
         gp.assert_decode_matches(out, want, tol, gp.bits_of(bm, n), exact=True)
 
 
+@pytest.mark.parametrize("pattern,density", [("uniform", 0.0152), ("uniform", 0.0160),
+                                             ("runs", 0.30), ("runs", 0.012)])
+def test_decode_binning_kernels(pattern, density):
+    """The partitioned decode with max_set = U on both sides of the density (one set bit in
+    64 elements) where the rank expansion changes from four consecutive bitmap words per
+    thread (1024 threads) to four words a round apart (512 threads), a chunk then spanning
+    about four rounds; and with the set bits in aligned runs of 1024 (all-ones words), dense
+    and sparse.  n = 2,000,003: a ragged last word and tile."""
+    d, L, n = 5, 20, 2_000_003
+    p, op = gp.params_pair(93, d, L)
+    sketch = WL.random_sketch((d, 1 << L), 14)
+    if pattern == "uniform":
+        bm = WL.random_bitmap(n, density, 15)
+    else:
+        rng = np.random.Generator(np.random.PCG64(16))
+        rows = (n + 1023) // 1024
+        pick = rng.random(rows) < density
+        bits = np.zeros(((n + 63) // 64) * 64, dtype=np.uint8)
+        run = np.repeat(pick, 1024).astype(np.uint8)
+        m = min(run.size, bits.size)
+        bits[:m] = run[:m]
+        bits[n:] = 0
+        bm = np.packbits(bits, bitorder="little").view(np.uint64).copy()
+    U = int(gp.bits_of(bm, n).sum())
+    gp.say(f"decode binning kernels {pattern} density={density} U={U} n={n}")
+    want, tol = oracle.decode_dense(op, n, bm, sketch.astype(np.float64))
+    out = gp.run_decode(p, n, bm, sketch, path="partitioned", max_set=U)
+    gp.assert_decode_matches(out, want, tol, gp.bits_of(bm, n), exact=True)
+
+
 # ---------------------------------------------------------------------------------------
 # end to end
 
