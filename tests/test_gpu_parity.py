@@ -141,6 +141,27 @@ def test_encode_capacity(cap):
     gp.assert_encode_matches(op, grads, n, res, cap=cap)
 
 
+def test_encode_reduce_max_workers():
+    """W = 65535, the most workers one encode call accepts (one grid row per worker): 100
+    elements each at 30% density, d = 3, w = 2^9 in 4 partitions (262,140 (worker,
+    partition) items on the walking accumulation grid); then the reduce over all 65535
+    sketches and bitmaps against the oracle's."""
+    W, n, d, L, K = 65535, 100, 3, 9, 7
+    gp.say(f"encode + reduce W={W} n={n} d={d} L={L} K={K}")
+    p, op = gp.params_pair(65535, d, L, K)
+    rng = np.random.Generator(np.random.PCG64(65535))
+    grads = np.zeros((W, n), np.float32)
+    mask = rng.random((W, n)) < 0.3
+    grads[mask] = rng.standard_normal(int(mask.sum())).astype(np.float32)
+    res = gp.run_encode(p, grads, n)
+    encs = gp.assert_encode_matches(op, grads, n, res)
+    bm, S = gp.run_reduce(p, n, res["bitmaps"], res["sketches"])
+    obm, oS, oA = oracle.reduce(np.stack([e["bitmap"] for e in encs]),
+                                np.stack([e["S"] for e in encs]), np.stack([e["A"] for e in encs]))
+    assert np.array_equal(bm, obm)
+    gp.assert_sketch_close(S, oS, oA, "reduced sketch")
+
+
 def test_encode_deterministic_integer_parts():
     """Two runs give identical bitmaps and lists (catches races in the compaction)."""
     gp.say("encode twice")
