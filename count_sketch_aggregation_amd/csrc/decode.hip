@@ -148,7 +148,7 @@ struct DecodeWs {
   uint16_t* slot;             // [chunks][kChunk] rank -> slot in that order
   float* gval;                // [chunks][kChunk] median of the item at each slot (k_dmedian),
                               // then of each rank (k_dunsort, dense set bits only)
-  uint32_t* prefix;           // [chunks][P + 1] partition starts per chunk
+  uint16_t* prefix;           // [chunks][P + 1] partition starts per chunk (<= kChunk)
   uint64_t chunks;            // capacity in chunks (max_set rounded up)
   uint64_t max_set;
   uint64_t sparse_below;      // U below this: no unsort pass; k_dwrite reads through slots
@@ -322,9 +322,9 @@ void k_dbin(HashArgs h, uint64_t n,
     }
     __syncthreads();
   }
-  uint32_t* pf = ws.prefix + (uint64_t)c * (P + 1);  // one contiguous row per chunk
-  for (uint32_t p = tid; p < P; p += NT) pf[p] = hist[p];
-  if (tid == 0) pf[P] = cnt;
+  uint16_t* pf = ws.prefix + (uint64_t)c * (P + 1);  // one contiguous row per chunk
+  for (uint32_t p = tid; p < P; p += NT) pf[p] = (uint16_t)hist[p];
+  if (tid == 0) pf[P] = (uint16_t)cnt;
   uint16_t* sl = ws.slot + start;
 #pragma unroll
   for (int r = 0; r < R; ++r) {
@@ -392,7 +392,7 @@ __global__ __launch_bounds__(kAccThreads) void k_dmedian(HashArgs h, uint64_t ti
   const uint32_t c_lo = (uint32_t)(nch * split / gridDim.y);
   const uint32_t c_hi = (uint32_t)(nch * (split + 1) / gridDim.y);
   if (c_lo >= c_hi) return;
-  const uint32_t* pf = ws.prefix + p;  // column p of the chunk-major offsets
+  const uint16_t* pf = ws.prefix + p;  // column p of the chunk-major offsets
   constexpr int PER = kSegBatch / kAccThreads;
   for (uint32_t cb = c_lo; cb < c_hi; cb += kSegBatch) {
     const uint32_t nb = c_hi - cb < (uint32_t)kSegBatch ? c_hi - cb : (uint32_t)kSegBatch;
@@ -744,7 +744,7 @@ DecodeLayout decode_layout(const s2r_params& p, uint64_t n, uint64_t max_set) {
   L.off_gval = off;
   off = align256(off + L.chunks * kChunk * 4);
   L.off_prefix = off;
-  off = align256(off + (L.partitions + 1) * L.chunks * 4);
+  off = align256(off + (L.partitions + 1) * L.chunks * 2);
   L.total = L.partitioned ? off : 0;
   return L;
 }
@@ -774,7 +774,7 @@ hipError_t launch_decode(const HashArgs& h, const s2r_params& p, uint64_t n,
     ws.bidx = reinterpret_cast<uint32_t*>(b + L.off_bidx);
     ws.slot = reinterpret_cast<uint16_t*>(b + L.off_slot);
     ws.gval = reinterpret_cast<float*>(b + L.off_gval);
-    ws.prefix = reinterpret_cast<uint32_t*>(b + L.off_prefix);
+    ws.prefix = reinterpret_cast<uint16_t*>(b + L.off_prefix);
     ws.chunks = L.chunks;
     ws.max_set = L.chunks * kChunk < max_set ? L.chunks * kChunk : max_set;
     if (ws.max_set > n) ws.max_set = n;
