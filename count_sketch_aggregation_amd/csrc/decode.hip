@@ -17,9 +17,10 @@
 //   k_dcount   popcount per 8192-element tile of the merged bitmap;
 //   k_scan     tile rank offsets, the number U of set bits, and the tile where every chunk
 //              of 8192 consecutive ranks starts;
-//   k_dbin     per rank chunk: expands its indices from the bitmap, counting-sorts them by
-//              partition in LDS, writes them partition-ordered with per-partition offsets,
-//              and records for every rank its slot in that order;
+//   k_dbin     per rank chunk: expands its indices from the bitmap (a round's words
+//              spread over every wave where a chunk fills less than a round), counting-sorts
+//              them by partition in LDS, writes them partition-ordered with 16-bit
+//              per-partition offsets, and records for every rank its slot in that order;
 //   k_dmedian  per partition (split over rank-chunk ranges): loads the partition's d x 2^K
 //              cells into LDS and takes every item's median from LDS, writing it at the
 //              item's slot;
@@ -140,7 +141,7 @@ __global__ __launch_bounds__(kDcountThreads) void k_dcount(const uint64_t* __res
 }
 
 // ---------------------------------------------------------------------------------------
-// k_dbin: grid = rank chunks, 512 threads.
+// The partitioned path's workspace, shared by k_dbin, k_dmedian, k_dunsort and k_dwrite.
 struct DecodeWs {
   const uint32_t* toff;       // [tiles + 1] rank offset of every tile
   const uint32_t* chunk_tile; // [chunks] tile holding rank c * kChunk
@@ -176,13 +177,13 @@ __device__ __forceinline__ void dbin_words(const uint64_t* __restrict__ bitmap, 
   }
 }
 
-// One round of k_dbin's rank expansion over words [q0, q0 + NT * kDBinWordsPerThread): masks
-// the thread's raw words (in place), ranks them in word order and expands the set bits whose rank lies
-// in [start, end) into litem; advances q0 and rank0.  Blocked: one workgroup scan of the
-// threads' popcount sums.  Interleaved: slice u (every thread's word u) precedes slice u + 1;
-// the four popcounts go through the wave scan as 16-bit fields of two words (a wave's field
-// sums stay below 2^13) and the per-wave sums are combined in full words.  Called by the
-// whole workgroup (two barriers).
+// One round of k_dbin's rank expansion over words [q0, q0 + NT * kDBinWordsPerThread):
+// masks the thread's raw words (in place), ranks them in word order and expands the set bits
+// whose rank lies in [start, end) into litem; advances q0 and rank0.  Blocked: one workgroup
+// scan of the threads' popcount sums.  Interleaved: slice u (every thread's word u) precedes
+// slice u + 1; the four popcounts go through the wave scan as 16-bit fields of two words (a
+// wave's field sums stay below 2^13) and the per-wave sums are combined in full words.
+// Called by the whole workgroup (two barriers).
 template <int NT, bool IL>
 __device__ __forceinline__ void dbin_round(uint64_t* wv, uint64_t n, uint64_t nwords,
                                            uint64_t q_end, uint32_t lb, uint64_t start,
@@ -245,12 +246,13 @@ __device__ __forceinline__ void dbin_round(uint64_t* wv, uint64_t n, uint64_t nw
   __syncthreads();  // wtot is reused next round
 }
 
+// k_dbin: grid = rank chunks, NT threads; IL selects the word layout of the rank expansion
+// (dbin_word_index).  The 512-thread kernel is held to six waves per SIMD, so three
+// workgroups (40 KiB of LDS each with P = 2048) share a CU.
 template <int NT, bool IL>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(NT <= 512 ? 6 : 4)))
-void k_dbin(HashArgs h, uint64_t n,
-                                                       const uint64_t* __restrict__ bitmap,
-                                                       uint64_t nwords, uint64_t tiles,
-                                                       DecodeWs ws, uint32_t P) {
+void k_dbin(HashArgs h, uint64_t n, const uint64_t* __restrict__ bitmap, uint64_t nwords,
+            uint64_t tiles, DecodeWs ws, uint32_t P) {
   extern __shared__ uint32_t hist[];  // P + 1
   // the chunk's indices in rank order, then (once every thread holds its own in registers)
   // in partition order
