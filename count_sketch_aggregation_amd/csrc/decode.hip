@@ -161,18 +161,18 @@ struct DecodeWs {
 // else blocked: q0 + kDBinWordsPerThread * tid + u (sparse bitmaps, where a chunk spans
 // several rounds and every wave already meets it).
 template <int NT, bool IL>
-__device__ __forceinline__ uint64_t dbin_word_index(uint64_t q0, int u, int tid) {
-  return IL ? q0 + (uint64_t)u * NT + tid : q0 + (uint64_t)kDBinWordsPerThread * tid + u;
+__device__ __forceinline__ uint32_t dbin_word_index(uint32_t q0, int u, int tid) {
+  return IL ? q0 + (uint32_t)(u * NT + tid) : q0 + (uint32_t)(kDBinWordsPerThread * tid + u);
 }
 
 // Raw bitmap words of a k_dbin round (clamped below q_end, so every load issues
 // unconditionally; masked in dbin_round).
 template <int NT, bool IL>
-__device__ __forceinline__ void dbin_words(const uint64_t* __restrict__ bitmap, uint64_t q0,
-                                           uint64_t q_end, uint32_t lb, int tid, uint64_t* wv) {
+__device__ __forceinline__ void dbin_words(const uint64_t* __restrict__ bitmap, uint32_t q0,
+                                           uint32_t q_end, uint32_t lb, int tid, uint64_t* wv) {
 #pragma unroll
   for (int u = 0; u < kDBinWordsPerThread; ++u) {
-    const uint64_t q = dbin_word_index<NT, IL>(q0, u, tid);
+    const uint32_t q = dbin_word_index<NT, IL>(q0, u, tid);
     wv[u] = bitmap[masked_src(q < q_end ? q : q_end - 1, lb)];
   }
 }
@@ -186,8 +186,8 @@ __device__ __forceinline__ void dbin_words(const uint64_t* __restrict__ bitmap, 
 // Called by the whole workgroup (two barriers).
 template <int NT, bool IL>
 __device__ __forceinline__ void dbin_round(uint64_t* wv, uint64_t n, uint64_t nwords,
-                                           uint64_t q_end, uint32_t lb, uint64_t start,
-                                           uint64_t end, uint64_t& q0, uint64_t& rank0,
+                                           uint32_t q_end, uint32_t lb, uint32_t start,
+                                           uint32_t end, uint32_t& q0, uint32_t& rank0,
                                            uint32_t* litem, uint4* wtot, int tid) {
   static_assert(kDBinWordsPerThread == 4, "four slices packed in two scan words");
   constexpr int NW = NT / kWave;
@@ -195,11 +195,11 @@ __device__ __forceinline__ void dbin_round(uint64_t* wv, uint64_t n, uint64_t nw
   uint32_t pc[kDBinWordsPerThread];
 #pragma unroll
   for (int u = 0; u < kDBinWordsPerThread; ++u) {
-    const uint64_t q = dbin_word_index<NT, IL>(q0, u, tid);
+    const uint32_t q = dbin_word_index<NT, IL>(q0, u, tid);
     wv[u] = q < q_end ? masked_from(wv[u], nwords, n, q, lb) : 0ull;  // masked in place
     pc[u] = (uint32_t)__popcll(wv[u]);
   }
-  uint64_t rk0[kDBinWordsPerThread];
+  uint32_t rk0[kDBinWordsPerThread];
   if constexpr (IL) {
     const uint32_t a = pc[0] | (pc[1] << 16), b = pc[2] | (pc[3] << 16);
     const uint32_t ia = wave_inclusive_sum(a), ib = wave_inclusive_sum(b);
@@ -216,7 +216,7 @@ __device__ __forceinline__ void dbin_round(uint64_t* wv, uint64_t n, uint64_t nw
       }
       total[0] += t.x; total[1] += t.y; total[2] += t.z; total[3] += t.w;
     }
-    uint64_t base = rank0;
+    uint32_t base = rank0;
 #pragma unroll
     for (int u = 0; u < kDBinWordsPerThread; ++u) {
       rk0[u] = base + before[u];
@@ -240,9 +240,9 @@ __device__ __forceinline__ void dbin_round(uint64_t* wv, uint64_t n, uint64_t nw
     }
     rank0 += total;
   }
-  expand_owned_words<kDBinWordsPerThread>(wv, rk0, q0, IL ? 1 : kDBinWordsPerThread,
-                                          IL ? (uint64_t)NT : 1, start, end, litem, tid);
-  q0 += (uint64_t)NT * kDBinWordsPerThread;
+  expand_owned_words<kDBinWordsPerThread>(wv, rk0, q0, IL ? 1u : (uint32_t)kDBinWordsPerThread,
+                                          IL ? (uint32_t)NT : 1u, start, end, litem, tid);
+  q0 += (uint32_t)(NT * kDBinWordsPerThread);
   __syncthreads();  // wtot is reused next round
 }
 
@@ -263,24 +263,26 @@ void k_dbin(HashArgs h, uint64_t n, const uint64_t* __restrict__ bitmap, uint64_
   const uint64_t U = ws.toff[tiles];
   const uint32_t t0 = ws.chunk_tile[c];  // loaded with U (c < chunks); meaningful if start < U
   if (U > ws.max_set) return;  // over capacity: k_dwrite decodes directly
-  const uint64_t start = (uint64_t)c * kChunk;
+  // ranks and bitmap word indices below fit 32 bits (U <= n < 2^32, nwords < 2^26)
+  const uint32_t start = c * (uint32_t)kChunk;
   if (start >= U) return;
   const uint32_t cnt = (uint32_t)(U - start < kChunk ? U - start : kChunk);
-  const uint64_t end = start + cnt;
+  const uint32_t end = start + cnt;
 
   // 1. expand ranks [start, end) into litem, NT * kDBinWordsPerThread bitmap words per round
   //    (expand_owned_words visits only the non-empty words that meet the chunk).  The
   //    chunk's last rank lies at or before the tile where the next chunk starts, so words
   //    past that tile are not read (a thread past it re-reads the last word in range and
   //    drops it).
-  uint64_t q0 = (uint64_t)t0 * kDecWords;
-  uint64_t rank0 = ws.toff[t0];
+  uint32_t q0 = t0 * (uint32_t)kDecWords;
+  uint32_t rank0 = ws.toff[t0];
   const uint64_t t_last = end < U ? (uint64_t)ws.chunk_tile[c + 1] : tiles - 1;
-  const uint64_t q_end = (t_last + 1) * kDecWords < nwords ? (t_last + 1) * kDecWords : nwords;
+  const uint32_t q_end =
+      (uint32_t)((t_last + 1) * kDecWords < nwords ? (t_last + 1) * kDecWords : nwords);
   // The next round's words are loaded before the current round is expanded (register sets
   // a and b alternate, so no loaded register is copied); past q_end they re-read the last
   // word in range and are never used.
-  constexpr uint64_t kRound = (uint64_t)NT * kDBinWordsPerThread;  // words per round
+  constexpr uint32_t kRound = (uint32_t)(NT * kDBinWordsPerThread);  // words per round
   uint64_t wa[kDBinWordsPerThread], wb[kDBinWordsPerThread];
   dbin_words<NT, IL>(bitmap, q0, q_end, h.lb, tid, wa);
   while (rank0 < end && q0 < q_end) {
