@@ -127,35 +127,6 @@ __device__ __forceinline__ uint64_t readlane64(uint64_t v, int l) {
   return ((uint64_t)hi << 32) | lo;
 }
 
-// List expansion of bitmap words held in registers: thread t owns words
-// qbase + t * tstride + u * ustride (u < WPT), whose first set bit has list rank rank[u].
-// Writes item[r - start] = 64 * word + bit for every set bit with rank r in [start, end).
-// The wave visits only lanes whose word is non-empty and meets the range (a ballot),
-// broadcasts that word, and expands its 64 bits with one lane per bit (v_mbcnt gives each
-// bit's rank), so the cost follows the set bits in range, not the span of words.  Word
-// indices and ranks fit 32 bits: n < 2^32 elements have fewer than 2^26 words and set bits.
-template <int WPT>
-__device__ __forceinline__ void expand_owned_words(const uint64_t* wv, const uint32_t* rank,
-                                                   uint32_t qbase, uint32_t tstride,
-                                                   uint32_t ustride, uint32_t start,
-                                                   uint32_t end, uint32_t* item, int tid) {
-  const int lane = tid & (kWave - 1);
-  const uint32_t qwave = qbase + (uint32_t)(tid - lane) * tstride;
-#pragma unroll
-  for (int u = 0; u < WPT; ++u) {
-    const uint32_t pc = (uint32_t)__popcll(wv[u]);
-    uint64_t m = __ballot(pc != 0 && rank[u] < end && rank[u] + pc > start);
-    while (m) {
-      const int l = __builtin_ctzll(m);
-      m &= m - 1;
-      const uint64_t w = readlane64(wv[u], l);
-      const uint32_t r = (uint32_t)__builtin_amdgcn_readlane((int)rank[u], l) + bits_below_lane(w);
-      const uint32_t q = qwave + (uint32_t)l * tstride + (uint32_t)u * ustride;
-      if (((w >> lane) & 1ull) && r >= start && r < end) item[r - start] = q * 64u + (uint32_t)lane;
-    }
-  }
-}
-
 // Adds v[r] into tile[cell[r]] (an LDS array) for R independent cells: all reads and the
 // first compare-and-swap of every cell are issued back to back (R LDS round trips in
 // flight instead of R in sequence), then only cells that lost a race retry.  Same fp32
