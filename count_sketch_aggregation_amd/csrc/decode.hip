@@ -587,7 +587,7 @@ __global__ __launch_bounds__(kDecThreads) void k_dwrite(HashArgs h, uint64_t n, 
   const uint64_t U = ws.toff[tiles];
   const bool direct = U > ws.max_set;
   const bool via_slot = U < ws.sparse_below;  // k_dunsort did nothing
-  const uint64_t rank0 = ws.toff[tile];
+  const uint32_t rank0 = ws.toff[tile];  // ranks fit 32 bits (U <= n < 2^32)
   constexpr int RPT = kDecTile / 4 / kDecThreads;  // 8 groups per thread
   uint32_t nib[RPT], rk[RPT];
 #pragma unroll
@@ -621,8 +621,8 @@ __global__ __launch_bounds__(kDecThreads) void k_dwrite(HashArgs h, uint64_t n, 
       for (int b = 0; b < 4; ++b) {
         v[b] = 0.f;
         if ((nib[r] >> b) & 1u) {
-          const uint64_t R = rank0 + k++;  // median at its chunk's slot
-          v[b] = ws.gval[(R & ~(uint64_t)(kChunk - 1)) + ws.slot[R]];
+          const uint32_t R = rank0 + k++;  // median at its chunk's slot
+          v[b] = ws.gval[(R & ~(uint32_t)(kChunk - 1)) + ws.slot[R]];
         }
       }
       o[r] = f32x4{v[0], v[1], v[2], v[3]};
