@@ -402,10 +402,12 @@ __device__ __forceinline__ void dmedian_cells(const float* __restrict__ sk, uint
 }
 
 // ---------------------------------------------------------------------------------------
-// k_dmedian: grid (partitions, splits), kAccThreads threads, items XCD-grouped.  LDS holds the partition's
-// d x 2^K cells; workgroup (p, s) takes the partition-p items of the s-th of `splits` equal
-// ranges of rank chunks (their segments flattened as in the encode accumulation, kDMedianUnroll
-// items per thread in flight) and writes each median at its item's slot.
+// k_dmedian: grid (partitions, splits), kAccThreads threads, items XCD-grouped.  LDS holds
+// the partition's d x 2^K cells (non-temporal loads when nt: with one split no other
+// workgroup reads them); workgroup (p, s) takes the partition-p items of the s-th of
+// `splits` equal ranges of rank chunks (their segments flattened as in the encode
+// accumulation, kDMedianUnroll items per thread in flight) and writes each median at its
+// item's slot.
 template <int D>
 __global__ __launch_bounds__(kAccThreads) void k_dmedian(HashArgs h, uint64_t tiles,
                                                          const float* __restrict__ sketch,
