@@ -219,7 +219,10 @@ DECODE_CASES = [(3, 14, 13, 1 << 20, 0.04), (5, 16, 12, 100_003, 0.3), (1, 10, 1
                 (5, 22, 12, 200_000, 0.02), (3, 20, 20, 50_000, 0.1),
                 # 2076 output tiles of 8192: whole groups of 8 XCD runs (64 tiles of the
                 # output pass, 256 workgroups of the count pass) and ragged tails
-                (5, 20, None, 17_000_003, 0.01)]
+                (5, 20, None, 17_000_003, 0.01),
+                # the most partitions the binning allows (2^13) with even d: odd-length
+                # rows of 16-bit partition offsets, 8192 median workgroups
+                (2, 21, 8, 2_000_003, 0.05)]
 
 
 @pytest.mark.parametrize("path", ["direct", "partitioned", "overflow"])
