@@ -52,7 +52,9 @@ def test_block_encode(case):
 @pytest.mark.parametrize("path", ["direct", "partitioned", "overflow"])
 @pytest.mark.parametrize("lb,d,L,K,n,density", [(1, 3, 14, 13, 100_003, 0.1), (2, 5, 16, 12, 65_537, 0.2),
                                                 (5, 4, 12, 12, 9000, 0.3), (6, 3, 20, 12, 300_000, 0.05),
-                                                (9, 5, 22, 12, 1 << 20, 0.03), (12, 1, 10, 10, 40_000, 0.5)])
+                                                (9, 5, 22, 12, 1 << 20, 0.03), (12, 1, 10, 10, 40_000, 0.5),
+                                                # the largest block (2^16), a ragged last block
+                                                (16, 3, 20, 12, 1_000_003, 0.4)])
 def test_block_decode(lb, d, L, K, n, density, path):
     gp.say(f"block decode B=2^{lb} d={d} L={L} K={K} n={n} path={path}")
     p, op = gp.params_pair(60 + lb, d, L, K, log2_block=lb)
