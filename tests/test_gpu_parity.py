@@ -222,7 +222,10 @@ DECODE_CASES = [(3, 14, 13, 1 << 20, 0.04), (5, 16, 12, 100_003, 0.3), (1, 10, 1
                 (5, 20, None, 17_000_003, 0.01),
                 # the most partitions the binning allows (2^13) with even d: odd-length
                 # rows of 16-bit partition offsets, 8192 median workgroups
-                (2, 21, 8, 2_000_003, 0.05)]
+                (2, 21, 8, 2_000_003, 0.05),
+                # the most rows (16, even: mean of the middle two) and an odd count past the
+                # median-of-five network (7) on the partitioned path (tables over 4 MiB)
+                (16, 17, 10, 500_003, 0.1), (7, 19, 11, 400_001, 0.1)]
 
 
 @pytest.mark.parametrize("path", ["direct", "partitioned", "overflow"])
