@@ -75,6 +75,9 @@ ENCODE_CASES = [
     # 402 tiles x 3 workers: one whole group of 8 XCD runs of 128 tiles, then a ragged tail
     # of 182 tiles in launch order
     ("xcd_runs_ragged", 3, 1_642_497, 1_642_500, 0.01, 3, 15, None, {}),
+    # the walking accumulation with 16 and with 7 rows (list capacity / partitions <= 2048)
+    ("d16_walk", 3, 20_000, 20_000, 0.1, 16, 14, None, {}),
+    ("d7_walk", 3, 30_000, 30_000, 0.1, 7, 15, None, {}),
 ]
 
 
