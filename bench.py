@@ -25,7 +25,8 @@ kernel's algorithmic bytes per launch over its average launch time against the 8
 peak.  The line also carries the median and minimum per-step event times, cold-cache steps
 (each timed alone after an untimed 512 MiB write that evicts L2 and the Infinity Cache), a
 plain streaming read and a plain streaming write of 2 GiB on the same GPU (the achievable
-read and write rates), the sketch
+read and write rates), the same plain read over the gradient rows themselves (the read rate
+at the size the encode streams, which falls with size), the sketch
 ratio lambda both ways, the estimation error of the decoded aggregate against the exact sum
 formed on the GPU by the lossless comparator (s2r_gather_sum, which is timed too), and the
 CPU oracle's rate on a bounded sample of the same workload with the host's identity.
@@ -606,6 +607,15 @@ def main() -> int:
     torch.cuda.synchronize()
     write_GBs = 5 * nbytes / (r0.elapsed_time(r1) * 1e-3) / 1e9
     del big
+    # the same plain read over the W gradient rows themselves: the read rate at the size the
+    # encode streams (it falls with the size read)
+    gbytes = grad.numel() * grad.element_size()
+    r0.record(stream)
+    for _ in range(3):
+        s2r.s2r_diag_stream_read(grad, gbytes, sink, stream=stream)
+    r1.record(stream)
+    torch.cuda.synchronize()
+    grad_read_GBs = 3 * gbytes / (r0.elapsed_time(r1) * 1e-3) / 1e9
     log(f"ms/step {ms_per_step:.3f}  phases {phases}  step alg GB/s {step_alg:.0f}  "
         f"roofline {roofline['kernel']} {roofline['achieved']} GB/s")
 
@@ -639,6 +649,11 @@ def main() -> int:
                                 "reps": len(cold)} if cold else None),
         "measured_read_GBs": round(read_GBs, 1),
         "measured_write_GBs": round(write_GBs, 1),
+        "measured_read_GBs_gradient_size": {
+            "GBs": round(grad_read_GBs, 1), "bytes": gbytes,
+            "k_stream_ratio": (round(kernels["k_stream"]["alg_GBs"] / grad_read_GBs, 4)
+                               if "k_stream" in kernels and kernels["k_stream"]["alg_GBs"]
+                               else None)},
         "step_frac_of_measured_read": round(step_alg / read_GBs, 4),
         "phases": phases,
         "kernels": kernels,
