@@ -226,15 +226,15 @@ def topk_stage(args) -> int:
     (W=16, N=25,557,032, blocks of 256, K = 1% of the blocks), residual carried across steps.
     Algorithmic bytes of the step: 16 per element (read gradient and residual, write output
     and residual); the roofline names the dominant kernel with the bytes of its own pass."""
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus})", file=sys.stderr)
+        return 2
     import numpy as np
     import torch
 
     import count_sketch_aggregation_amd as s2r
     import workloads as WL
 
-    if args.gpus != 1:
-        print("bench.py runs on one GPU only", file=sys.stderr)
-        return 2
     cid, block = 2, 256
     wl = WL.workload(cid)
     nb = -(-wl.N // block)
