@@ -61,6 +61,8 @@ ENCODE_CASES = [
     ("tile_edge_4097", 3, 4097, 4100, 0.6, 3, 12, None, {}),
     ("ragged_many_tiles", 3, 100_003, 100_008, 0.05, 3, 15, None, {"pad": float("nan")}),
     ("dense_all", 2, 20_000, 20_000, 1.0, 3, 12, None, {}),
+    # every element non-zero over 37 list chunks per worker: only dense spans, full segments
+    ("dense_all_chunks", 2, 300_007, 300_008, 1.0, 5, 20, None, {}),
     ("all_zero", 2, 30_000, 30_000, 0.0, 3, 12, None, {}),
     ("blocks_partitioned", 4, 300_000, 300_000, 0.05, 5, 18, None, {"block": 256}),
     ("blocks_atomic", 2, 300_000, 300_000, 0.05, 5, 18, 18, {"block": 256}),
@@ -228,7 +230,10 @@ DECODE_CASES = [(3, 14, 13, 1 << 20, 0.04), (5, 16, 12, 100_003, 0.3), (1, 10, 1
                 (2, 21, 8, 2_000_003, 0.05),
                 # the most rows (16, even: mean of the middle two) and an odd count past the
                 # median-of-five network (7) on the partitioned path (tables over 4 MiB)
-                (16, 17, 10, 500_003, 0.1), (7, 19, 11, 400_001, 0.1)]
+                (16, 17, 10, 500_003, 0.1), (7, 19, 11, 400_001, 0.1),
+                # every bit set: all-ones words in every round of the rank expansion, 37
+                # chunks of 8192 set bits and a ragged last chunk, word and tile
+                (5, 20, 11, 300_007, 1.0)]
 
 
 @pytest.mark.parametrize("path", ["direct", "partitioned", "overflow"])
