@@ -374,7 +374,8 @@ def gpu_estimation_error(s2r, wl, cap, buf, out, stream) -> dict:
     gradients, ||g_hat - sum_k g_k|| / ||sum_k g_k||, with the exact sum formed on the GPU by
     the lossless comparator (s2r_gather_sum over the encode's own lists, an fp32 sum in worker
     order, within (W - 1) 2^-24 relative of the exact real sum) and both norms accumulated
-    in fp64 on the device.  Also times the comparator."""
+    in fp64 on the device.  Also times the comparator: HIP events around 20 calls (ms), and
+    its kernels alone from the library's per-launch events over 5 more (kernel_ms)."""
     import torch
 
     exact = torch.empty(wl.N, dtype=torch.float32, device=out.device)
@@ -385,13 +386,17 @@ def gpu_estimation_error(s2r, wl, cap, buf, out, stream) -> dict:
     gather()
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    reps = 5
+    reps = 20
     e0.record(stream)
     for _ in range(reps):
         gather()
     e1.record(stream)
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / reps
+    # the comparator's kernels alone: the library's per-launch events over 5 more calls
+    traced = 5
+    per, _ = traced_steps(gather, traced, stream)
+    kernel_ms = sum(t for _, t in per.values()) / traced
     err2 = ref2 = err2_listed = 0.0
     listed = 0
     chunk = 1 << 27
@@ -412,6 +417,8 @@ def gpu_estimation_error(s2r, wl, cap, buf, out, stream) -> dict:
         "exact_sum": "s2r_gather_sum (lossless comparator) on the device",
         "lossless_comparator": {
             "ms": round(ms, 4),
+            "kernel_ms": round(kernel_ms, 4),
+            "kernels_avg_us": {k: round(t / n * 1e3, 2) for k, (n, t) in per.items()},
             "G_elem_s": round(wl.W * wl.N / (ms * 1e-3) / 1e9, 3),
             # zero-fill of the dense output, then W list reads and scattered adds
             "alg_bytes": 4 * wl.N + 8 * nnz_total,
