@@ -290,7 +290,8 @@ def topk_stage(args) -> int:
         roofline = {"bound": "hbm", "kernel": dom, "achieved": kd["alg_GBs"],
                     "peak": HBM_PEAK_GBS, "unit": "GB/s",
                     "frac": round(kd["alg_GBs"] / HBM_PEAK_GBS, 4) if kd["alg_GBs"] else None,
-                    "traffic": None, "alg_bytes_per_launch": kd["alg_bytes_per_launch"],
+                    "traffic": measured_traffic("resnet50_topk", dom),
+                    "alg_bytes_per_launch": kd["alg_bytes_per_launch"],
                     "avg_launch_us": kd["avg_us"],
                     "timing": "HIP events recorded by the library on its stream around each "
                               f"launch of {dom} over {args.steps} traced steps"}
