@@ -135,6 +135,46 @@ def test_encode_special_values():
     gp.assert_encode_matches(op, g, n, res)
 
 
+@pytest.mark.parametrize("K", [None, 12])
+def test_encode_reduce_non_finite_values(K):
+    """+Inf, -Inf and NaN have non-zero magnitude bits, so the bitmap and the lists keep them
+    with their exact bits like any other value.  A sketch cell they reach is non-finite, and
+    of the same kind as the oracle's (NaN where contributions of both infinite signs or a NaN
+    meet, else the infinity's signed direction), whatever the order of the adds; every other
+    cell is within the tolerance.  The reduce keeps each cell's kind (K = L: the global-atomic
+    scatter; default K: the LDS tiles)."""
+    gp.say(f"encode/reduce non-finite values K={K}")
+    W, n, d, L = 3, 60_000, 3, 12
+    p, op = gp.params_pair(808, d, L, K)
+    grads = _grads(W, n, n, 0.1, 31)
+    rng = np.random.Generator(np.random.PCG64(32))
+    special = np.array([np.inf, -np.inf, np.nan, np.inf, -np.inf, np.nan, np.inf], np.float32)
+    for k in range(W):
+        grads[k, rng.choice(n, special.size, replace=False)] = special
+    res = gp.run_encode(p, grads, n)
+    for k in range(W):
+        e = oracle.encode_dense(op, grads[k, :n], cap=n)
+        assert np.array_equal(res["bitmaps"][k], e["bitmap"]), f"worker {k}: bitmap differs"
+        assert res["nnz"][k] == e["nnz"]
+        m = e["nnz"]
+        assert np.array_equal(res["idx"][k, :m], e["idx"])
+        assert np.array_equal(res["val"][k, :m].view(np.uint32), e["val"].view(np.uint32))
+        S, g = e["S"], res["sketches"][k].astype(np.float64)
+        for kind in (np.isnan, np.isposinf, np.isneginf):
+            assert np.array_equal(kind(g), kind(S)), f"worker {k}: {kind.__name__} cells differ"
+        assert np.isnan(S).any() and np.isinf(S).any()  # the case is exercised
+        fin = np.isfinite(S)
+        gp.assert_sketch_close(res["sketches"][k][fin], S[fin], e["A"][fin], f"worker {k} sketch")
+    _, red = gp.run_reduce(p, n, res["bitmaps"], res["sketches"])
+    want = res["sketches"][0].copy()
+    for k in range(1, W):
+        want = want + res["sketches"][k]  # fp32, worker order
+    for kind in (np.isnan, np.isposinf, np.isneginf):
+        assert np.array_equal(kind(red), kind(want)), f"reduce: {kind.__name__} cells differ"
+    fin = np.isfinite(want)
+    assert np.array_equal(red[fin].view(np.uint32), want[fin].view(np.uint32))
+
+
 @pytest.mark.parametrize("cap", [0, 1, 1000, 8192, 8193])
 def test_encode_capacity(cap):
     """nnz beyond cap: bitmap and nnz exact, the first cap list entries exact."""
