@@ -37,7 +37,10 @@
  *     significant bit first; bits of blocks at or beyond ceil(n/B) are 0 on output.
  *   - Sketch layout: fp32 [d][w] row-major per worker, w = 2^log2_w.
  *   - "Non-zero" means (bits(x) & 0x7fffffff) != 0: +0 and -0 are zero, subnormals are
- *     not.  Non-finite gradient values are outside the contract.
+ *     not.  By the same test +-Inf and NaN are non-zero: they are listed with their bits,
+ *     and the sketch cells and sums they reach are non-finite as IEEE arithmetic gives them
+ *     (NaN where both infinite signs or a NaN meet).  Decoding a non-finite cell is outside
+ *     the contract.
  */
 #ifndef S2R_H
 #define S2R_H
