@@ -55,7 +55,11 @@ constexpr int kDUnsortThreads = 512;
 constexpr uint64_t kDecSparseRatio = 32;
 constexpr int kDMedianUnroll = 4;  // items in flight per thread (stride kAccThreads)
 constexpr int kTileLoads = 8;      // 16-byte cell loads per thread in flight when a tile fills
-constexpr uint64_t kDMedianTargetGroups = 1536;
+// Workgroups k_dmedian aims for when partitions are few: each split reloads its partition's
+// cells, so fewer splits trade parallelism for cell traffic (measured on MI355X with 128
+// partitions of 48 KiB, the ResNet-50 workload: 8 splits 25.5 us, 4 splits 21 us, 3 or
+// 2 splits 23-24 us)
+constexpr uint64_t kDMedianTargetGroups = 512;
 constexpr uint32_t kDMedianMaxSplits = 8;
 // Set bits per k_dmedian workgroup above which a partition's chunks are split further
 // (measured on MI355X: about 21K per workgroup -> 11K took the Transformer workload's
@@ -860,9 +864,9 @@ hipError_t launch_decode(const HashArgs& h, const s2r_params& p, uint64_t n,
       if (e != hipSuccess) return e;
       const size_t tlds = ((size_t)p.d << p.log2_part) * sizeof(float);
       const int vec4 = (p.log2_part >= 2 && (reinterpret_cast<uintptr_t>(sketch) % 16) == 0);
-      // enough workgroups to fill the chip about twice at a few per CU, and at most about
-      // kDMedianGroupItems set bits per workgroup (max_set stands in for U); each split
-      // reloads the partition's cells, so never more splits than rank chunks
+      // about kDMedianTargetGroups workgroups, and at most about kDMedianGroupItems set bits
+      // per workgroup (max_set stands in for U); each split reloads the partition's cells,
+      // so never more splits than rank chunks
       uint32_t splits = (uint32_t)((kDMedianTargetGroups + L.partitions - 1) / L.partitions);
       const uint64_t by_items =
           (ws.max_set + L.partitions * kDMedianGroupItems - 1) / (L.partitions * kDMedianGroupItems);
